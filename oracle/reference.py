@@ -1,0 +1,339 @@
+"""Plain fp64 CPU oracle for single-token GQA decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP path (no kernels, headers, helpers or tables) and imports nothing
+from it; the only thing both sides share is the seeded input generator in
+``workloads``.
+
+Every function computes the plain definition, slowly and in float64, one
+(batch, head) at a time.  bf16 inputs are widened exactly to float64; the
+only rounding the oracle performs on purpose is the bf16 store of the
+appended K row (and of a bf16 output, when a caller asks for it).
+
+Sources (titles of the pages this follows):
+  * fusedtok 1.0.1 README, "Operators" table (rows RMSNorm, RoPE, Softmax,
+    attention_decode) and "Usage" (the attention_decode call with a GQA cache
+    [B,Hkv,T,D] and per-sequence int32 lens; RoPE with pos_offset, NeoX
+    layout; the dtype rule "compute in float32, convert at load/store").
+  * fusedtok 1.0.1 README, "Benchmarks" (attention references use heads
+    pre-expanded with repeat_interleave, i.e. query head h reads KV head
+    h // (Hq/Hkv)).
+  * cutileGPT README, "Why tiles" (the RMSNorm kernel figure:
+    rstd = 1/sqrt(sum(x*x)/N + eps), y = x*rstd*w) and its feature list
+    (RoPE, MHA/GQA, sliding-window attention, fused QK-Norm + RoPE +
+    KV-cache writes).
+Readings where the pages are silent are listed per function.
+
+Every function here is pinned by tests against closed forms, invariants,
+brute force and independent library routines, except where a docstring says
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "f64_to_bf16", "rmsnorm", "rope_inv_freq", "rope_neox",
+    "qkv_prologue", "attend_rows", "attend", "num_partitions",
+    "partition_ranges", "attend_partials", "lse_merge", "decode_step",
+]
+
+
+# ---------------------------------------------------------------------------
+# bf16 <-> float64
+# ---------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns: the upper half of an IEEE float32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (nearest, ties to even), one rounding.
+
+    The dtype rule of the fusedtok README ("Usage": float32 compute, convert at
+    the store) leaves the rounding mode open; nearest-even is the reading.
+    bf16 keeps 8 significant bits and float32's exponent range, so a finite
+    x = m * 2**e (0.5 <= |m| < 1) rounds to rint(m * 2**8) * 2**(e-8) for
+    normal results and to a multiple of 2**-133 for subnormal ones.  Values
+    whose rounded magnitude reaches 2**128 become infinity; NaN becomes the
+    quiet NaN 0x7FC0.  Returns uint16 bit patterns.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_x = x.reshape(-1)
+    flat_o = out.reshape(-1)
+    nan = np.isnan(flat_x)
+    m, e = np.frexp(flat_x)                     # x = m * 2**e
+    normal = e - 1 >= -126                      # |x| >= 2**-126
+    r = np.where(normal, np.ldexp(np.rint(np.ldexp(m, 8)), e - 8),
+                 np.ldexp(np.rint(np.ldexp(flat_x, 133)), -133))
+    with np.errstate(over="ignore"):
+        r32 = r.astype(np.float32)              # exact: r has <= 8 sig. bits
+    # r32 is now exactly a bf16 value (or +-inf); keep its upper 16 bits.
+    flat_o[:] = (r32.view(np.uint32) >> 16).astype(np.uint16)
+    flat_o[nan] = 0x7FC0
+    return out
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm (cutileGPT "Why tiles" figure; fusedtok Operators row RMSNorm)
+# ---------------------------------------------------------------------------
+def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """y = x * rstd * w with rstd = 1 / sqrt(mean(x*x) + eps), over the last axis.
+
+    The weight multiplies directly (not 1 + w), and eps is added to the mean
+    of squares inside the square root, as the cutileGPT RMSNorm figure shows.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    n = x.shape[-1]
+    rstd = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) / n + eps)
+    return x * rstd * w
+
+
+# ---------------------------------------------------------------------------
+# RoPE, NeoX layout (fusedtok Operators row RoPE; Usage: neox=True, pos_offset)
+# ---------------------------------------------------------------------------
+def rope_inv_freq(D: int, theta: float) -> np.ndarray:
+    """f_i = theta ** (-2i/D) for i < D/2 (the standard rotary schedule).
+
+    Parity unpinned by the pages: they name the NeoX layout and a position
+    offset but print no frequency formula.  theta comes with each workload.
+    """
+    i = np.arange(D // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * i / D)
+
+
+def rope_neox(x: np.ndarray, pos, theta: float) -> np.ndarray:
+    """Rotate pairs (i, i + D/2) of the last axis by angle pos * f_i.
+
+    y_i       = x_i cos a - x_{i+D/2} sin a
+    y_{i+D/2} = x_{i+D/2} cos a + x_i sin a
+    NeoX ("rotate half") pairing is the reading of the README's NeoX
+    (LLaMA-HF) layout; the whole head dimension is rotated (cutileGPT lists
+    partial RoPE as unsupported).  ``pos`` broadcasts against x[..., 0].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    h = D // 2
+    a = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(D, theta)
+    c, s = np.cos(a), np.sin(a)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# ---------------------------------------------------------------------------
+# Fused prologue (cutileGPT feature list: fused QK-Norm + RoPE + KV-cache writes)
+# ---------------------------------------------------------------------------
+def qkv_prologue(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache):
+    """QK-RMSNorm, then NeoX RoPE at pos[b], then append K and V at row pos[b].
+
+    q: [B,Hq,D] float64; k_new, v_new: [B,Hkv,D] float64 (exact widenings of
+    the bf16 inputs); w_q, w_k: [D] or None (None = no QK-norm; one weight
+    vector per projection shared by all heads); theta <= 0 = no RoPE;
+    pos: int [B]; caches: uint16 [B,Hkv,T,D].
+
+    Returns (q_hat float64 [B,Hq,D], k_cache', v_cache') with new arrays for
+    the caches.  Order norm -> RoPE -> write follows the feature's name.  V is
+    written unrotated and un-normalised.  A pos outside [0, T) rotates q but
+    writes nothing (the safe-behaviour reading for out-of-contract values).
+    The appended K row is rounded to bf16 once; q_hat stays float64.
+    """
+    q = np.array(q, dtype=np.float64)
+    k = np.array(k_new, dtype=np.float64)
+    v = np.array(v_new, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    T = k_cache.shape[2]
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    q_hat = np.empty_like(q)
+    for b in range(B):
+        p = int(pos[b])
+        for h in range(Hq):
+            x = q[b, h]
+            if w_q is not None:
+                x = rmsnorm(x, w_q, eps)
+            if theta > 0:
+                x = rope_neox(x, p, theta)
+            q_hat[b, h] = x
+        for g in range(Hkv):
+            x = k[b, g]
+            if w_k is not None:
+                x = rmsnorm(x, w_k, eps)
+            if theta > 0:
+                x = rope_neox(x, p, theta)
+            if 0 <= p < T:
+                kc[b, g, p] = f64_to_bf16(x)
+                vc[b, g, p] = f64_to_bf16(v[b, g])
+    return q_hat, kc, vc
+
+
+# ---------------------------------------------------------------------------
+# Attention (fusedtok Operators row attention_decode; Usage; Benchmarks)
+# ---------------------------------------------------------------------------
+def attend_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """Softmax attention of one query vector over rows of K, V (float64).
+
+    s_j = scale * <q, K_j>;  m = max_j s_j;  p_j = exp(s_j - m);
+    out = sum_j p_j V_j / sum_j p_j;  lse = m + ln(sum_j p_j).
+    No rows: out = 0 and lse = -inf (the empty-set convention used for empty
+    split-K partitions and lens = 0).
+    """
+    D = V.shape[-1]
+    if K.shape[0] == 0:
+        return np.zeros(D), -math.inf
+    s = scale * (K @ q)
+    m = np.max(s)
+    p = np.exp(s - m)
+    l = np.sum(p)
+    return (p @ V) / l, m + math.log(l)
+
+
+def _window(n_raw: int, T: int, window: int):
+    n = min(max(int(n_raw), 0), T)
+    lo = max(0, n - window) if window > 0 else 0
+    return lo, n
+
+
+def attend(q, k_cache, v_cache, lens, window: int = 0, scale: float = 0.0):
+    """Single-token GQA decode attention over a [B,Hkv,T,D] bf16 cache.
+
+    q: [B,Hq,D] float64.  Query head h reads KV head h // (Hq/Hkv) (the
+    repeat_interleave expansion of the fusedtok benchmarks).  Sequence b
+    attends cache rows [lo, n) with n = lens[b] clamped to [0, T] and
+    lo = max(0, n - window) for window > 0 (the last ``window`` rows,
+    including the newest), else 0.  scale <= 0 means 1/sqrt(D) (the
+    default of the SDPA the README compares against).
+    Returns (out float64 [B,Hq,D], lse float64 [B,Hq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    if scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((B, Hq, v_cache.shape[3]))
+    lse = np.full((B, Hq), -math.inf)
+    for b in range(B):
+        lo, n = _window(lens[b], T, window)
+        for g in range(Hkv):
+            K = bf16_to_f64(k_cache[b, g, lo:n])
+            V = bf16_to_f64(v_cache[b, g, lo:n])
+            for h in range(g * G, (g + 1) * G):
+                out[b, h], lse[b, h] = attend_rows(q[b, h], K, V, scale)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Flash-decoding split (fusedtok attention_decode row: "flash-decoding split
+# over long caches") and the log-sum-exp merge
+# ---------------------------------------------------------------------------
+def num_partitions(T: int, window: int, part_tokens: int) -> int:
+    """Partitions per (sequence, KV head): ceil(min(T, window or T) / P).
+
+    Depends on host-known sizes only, so it bounds every sequence's count.
+    """
+    span = min(T, window) if window > 0 else T
+    return -(-span // part_tokens)
+
+
+def partition_ranges(lo: int, n: int, part_tokens: int, count: int):
+    """J_k = [lo + k P, min(lo + (k+1) P, n)) for k < count; may be empty.
+
+    Partitions start at the window's first row (reading: the split is
+    window-relative; any cut gives the same merged result).
+    """
+    out = []
+    for k in range(count):
+        a = lo + k * part_tokens
+        out.append((min(a, n), min(a + part_tokens, n)))
+    return out
+
+
+def attend_partials(q, k_cache, v_cache, lens, window, scale, part_tokens):
+    """Attention restricted to each partition: (o_k, lse_k) per (b, h, k).
+
+    o_k is the normalised partition output and lse_k its log-sum-exp; an
+    empty partition gives o_k = 0, lse_k = -inf.
+    Returns (o float64 [B,Hq,P,D], lse float64 [B,Hq,P]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    G = Hq // Hkv
+    if scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    P = num_partitions(T, window, part_tokens)
+    o = np.zeros((B, Hq, P, v_cache.shape[3]))
+    lse = np.full((B, Hq, P), -math.inf)
+    for b in range(B):
+        lo, n = _window(lens[b], T, window)
+        for k, (a, e) in enumerate(partition_ranges(lo, n, part_tokens, P)):
+            for g in range(Hkv):
+                K = bf16_to_f64(k_cache[b, g, a:e])
+                V = bf16_to_f64(v_cache[b, g, a:e])
+                for h in range(g * G, (g + 1) * G):
+                    o[b, h, k], lse[b, h, k] = attend_rows(q[b, h], K, V, scale)
+    return o, lse
+
+
+def lse_merge(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Combine partition results: M = max_k lse_k, w_k = exp(lse_k - M),
+    out = sum_k w_k o_k / sum_k w_k, lse = M + ln sum_k w_k.
+
+    Partitions with lse_k = -inf weigh nothing; if all are -inf the result is
+    out = 0, lse = -inf.  Works over the second-to-last axis of o_parts.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    lead = lse_parts.shape[:-1]
+    D = o_parts.shape[-1]
+    out = np.zeros(lead + (D,))
+    lse = np.full(lead, -math.inf)
+    for idx in np.ndindex(*lead):
+        L = lse_parts[idx]
+        M = np.max(L) if L.size else -math.inf
+        if M == -math.inf:
+            continue
+        w = np.exp(L - M)
+        W = np.sum(w)
+        out[idx] = (w @ o_parts[idx]) / W
+        lse[idx] = M + math.log(W)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# One whole decode step on a workload
+# ---------------------------------------------------------------------------
+def decode_step(w, split: bool = False, scale: float = 0.0):
+    """Prologue (if the workload has one) followed by attention.
+
+    ``w`` carries the workload's arrays (see workloads.Workload).  Returns a
+    dict with q_hat, k_cache, v_cache (after the append), out, lse and, when
+    ``split`` is true, the partitions o_parts / lse_parts and the merged
+    result in out / lse.
+    """
+    q = bf16_to_f64(w.q)
+    if w.pos is not None:
+        q_hat, kc, vc = qkv_prologue(
+            q, bf16_to_f64(w.k_new), bf16_to_f64(w.v_new), w.w_q, w.w_k,
+            w.eps, w.theta, w.pos, w.k_cache, w.v_cache)
+    else:
+        q_hat, kc, vc = q, w.k_cache, w.v_cache
+    res = dict(q_hat=q_hat, k_cache=kc, v_cache=vc)
+    if split:
+        o, l = attend_partials(q_hat, kc, vc, w.lens, w.window, scale,
+                               w.part_tokens)
+        res["o_parts"], res["lse_parts"] = o, l
+        res["out"], res["lse"] = lse_merge(o, l)
+    else:
+        res["out"], res["lse"] = attend(q_hat, kc, vc, w.lens, w.window, scale)
+    return res

@@ -1,0 +1,468 @@
+"""Pins for the fp64 oracle: checks against what the pages and mathematics fix.
+
+Each pin takes a namespace ``O`` exposing the oracle's functions and raises
+AssertionError when the oracle disagrees with a closed form, an invariant,
+brute force, or an independent library routine.  ``test_oracle_pins``
+runs every pin on the real oracle; ``test_oracle_mutants`` runs them on
+copies of the oracle with planted mistakes and requires at least one pin to
+fail for each mistake.
+
+Sources: fusedtok 1.0.1 README ("Operators", "Usage", "Benchmarks");
+cutileGPT README ("Why tiles" RMSNorm figure; feature list).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import bruteforce as BF
+
+RNG_SEED = 1234
+
+
+def _rng(k=0):
+    return np.random.default_rng(RNG_SEED + k)
+
+
+def _bits(rng, shape):
+    """Random finite bf16 bit patterns of N(0,1) draws (no dependence on oracle)."""
+    x = rng.standard_normal(shape).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _torch_bf16_to_f64(bits):
+    t = torch.from_numpy(np.asarray(bits, np.uint16).astype(np.int16)).view(torch.bfloat16)
+    return t.double().numpy()
+
+
+def _close(a, b, tol, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err} > {tol}"
+
+
+# ---------------------------------------------------------------------------
+# bf16 conversion
+# ---------------------------------------------------------------------------
+def pin_bf16_decode_matches_torch(O):
+    """Every non-NaN bf16 pattern widens exactly as torch's bfloat16 does."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = _torch_bf16_to_f64(allb)
+    ok = ~np.isnan(ref)
+    got = O.bf16_to_f64(allb)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.all(np.isnan(got[~ok]))
+
+
+def pin_bf16_roundtrip_all_patterns(O):
+    """Rounding an exact bf16 value returns its own bit pattern (all 65536)."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = _torch_bf16_to_f64(allb)
+    ok = ~np.isnan(x)
+    got = O.f64_to_bf16(x[ok])
+    assert np.array_equal(got, allb[ok])
+
+
+def pin_bf16_rne_matches_torch_on_fp32(O):
+    """For float32-representable inputs one RNE rounding equals torch's
+    float32 -> bfloat16 conversion (round to nearest even)."""
+    rng = _rng(1)
+    x = rng.standard_normal(200000).astype(np.float32) * 3
+    # add exact ties: bf16 value + half an ulp
+    base = x[:5000].view(np.uint32) & np.uint32(0xFFFF0000)
+    x[:5000] = (base | np.uint32(0x8000)).view(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    got = O.f64_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def pin_bf16_single_rounding_cases(O):
+    """Hand-worked cases: ties go to even; a value just above a tie rounds up
+    (which a float32 intermediate would lose); specials."""
+    cases = [
+        (1.0 + 2.0 ** -8, 0x3F80),                 # tie -> even (1.0)
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),             # tie -> even (1 + 2^-6)
+        (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),    # above tie -> up
+        (1.0 + 2.0 ** -8 - 2.0 ** -40, 0x3F80),    # below tie -> down
+        (-(1.0 + 2.0 ** -8 + 2.0 ** -40), 0xBF81),
+        (0.0, 0x0000), (-0.0, 0x8000),
+        (math.inf, 0x7F80), (-math.inf, 0xFF80),
+        (3.3895313892515355e38, 0x7F7F),          # largest finite bf16
+        (3.4e38, 0x7F80),                          # rounds past the max -> inf
+        (2.0 ** -133, 0x0001),                     # smallest subnormal
+        (2.0 ** -134, 0x0000),                     # tie -> even (0)
+        (3 * 2.0 ** -135, 0x0001),                 # 0.75 ulp -> 1 ulp
+        (2.0 ** -126, 0x0080),                     # smallest normal
+    ]
+    xs = np.array([c[0] for c in cases])
+    want = np.array([c[1] for c in cases], np.uint16)
+    got = O.f64_to_bf16(xs)
+    assert np.array_equal(got, want), (got, want)
+    assert O.f64_to_bf16(np.array([math.nan]))[0] & 0x7FFF > 0x7F80
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+def pin_rmsnorm_matches_torch(O):
+    rng = _rng(2)
+    x = rng.standard_normal((7, 128))
+    w = 1 + 0.1 * rng.standard_normal(128)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,),
+                                       torch.from_numpy(w), eps=1e-6).numpy()
+    _close(O.rmsnorm(x, w, 1e-6), ref, 1e-12, "rmsnorm vs torch")
+
+
+def pin_rmsnorm_closed_forms(O):
+    # x = c * 1: y = c / sqrt(c^2 + eps) * w
+    w = np.array([0.5, 2.0, -1.0, 3.0])
+    for c, eps in [(2.0, 0.0), (0.5, 1e-2), (-3.0, 1.0)]:
+        _close(O.rmsnorm(np.full(4, c), w, eps), c / math.sqrt(c * c + eps) * w,
+               1e-14, "rmsnorm const")
+    # hand example: x=[3,4], w=[1,2], eps=0 -> mean square 12.5
+    _close(O.rmsnorm(np.array([3.0, 4.0]), np.array([1.0, 2.0]), 0.0),
+           [3 / math.sqrt(12.5), 8 / math.sqrt(12.5)], 1e-15, "rmsnorm hand")
+    # scale invariance with eps = 0
+    rng = _rng(3)
+    x = rng.standard_normal(64)
+    w = rng.standard_normal(64)
+    _close(O.rmsnorm(7.5 * x, w, 0.0), O.rmsnorm(x, w, 0.0), 1e-13, "rmsnorm scale")
+
+
+# ---------------------------------------------------------------------------
+# RoPE (NeoX)
+# ---------------------------------------------------------------------------
+def pin_rope_identity_and_norm(O):
+    rng = _rng(4)
+    x = rng.standard_normal((3, 128))
+    assert np.array_equal(O.rope_neox(x, 0, 1e4), x)
+    for pos in (1, 17, 4095, 32767, 131071):
+        y = O.rope_neox(x, pos, 5e5)
+        _close(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), 1e-12, "rope norm")
+
+
+def pin_rope_relative_and_composition(O):
+    rng = _rng(5)
+    q = rng.standard_normal(64)
+    k = rng.standard_normal(64)
+    for p, r in [(3, 10), (100, 37), (4096, 5000)]:
+        a = np.dot(O.rope_neox(q, p, 1e4), O.rope_neox(k, r, 1e4))
+        b = np.dot(q, O.rope_neox(k, r - p, 1e4))
+        assert abs(a - b) <= 1e-10 * (1 + abs(a)), (p, r, a, b)
+        _close(O.rope_neox(O.rope_neox(q, p, 1e4), r, 1e4),
+               O.rope_neox(q, p + r, 1e4), 1e-11, "rope composition")
+
+
+def pin_rope_small_closed_forms(O):
+    # D = 2: f_0 = 1, rotation by pos radians.
+    x = np.array([0.3, -1.7])
+    for p in (1, 2, 5):
+        c, s = math.cos(p), math.sin(p)
+        _close(O.rope_neox(x, p, 1e4), [x[0] * c - x[1] * s, x[1] * c + x[0] * s],
+               1e-15, "rope D=2")
+    # D = 4, theta = 4: f = [1, 4**-0.5 = 0.5]; pairs (0,2) and (1,3).
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    p = 3
+    a0, a1 = p * 1.0, p * 0.5
+    want = [1 * math.cos(a0) - 3 * math.sin(a0), 2 * math.cos(a1) - 4 * math.sin(a1),
+            3 * math.cos(a0) + 1 * math.sin(a0), 4 * math.cos(a1) + 2 * math.sin(a1)]
+    _close(O.rope_neox(x, p, 4.0), want, 1e-15, "rope D=4")
+
+
+def pin_rope_complex_form(O):
+    """NeoX rotation = multiplying z_i = x_i + j x_{i+D/2} by exp(j pos f_i)."""
+    rng = _rng(6)
+    x = rng.standard_normal(128)
+    pos, theta = 777, 1e6
+    f = theta ** (-np.arange(64) * 2.0 / 128)
+    z = (x[:64] + 1j * x[64:]) * np.exp(1j * pos * f)
+    _close(O.rope_neox(x, pos, theta), np.concatenate([z.real, z.imag]), 1e-12, "rope complex")
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+def _rand_case(k, B=2, Hq=8, Hkv=2, D=16, T=40, lens=None):
+    rng = _rng(100 + k)
+    q = rng.standard_normal((B, Hq, D))
+    kc = _bits(rng, (B, Hkv, T, D))
+    vc = _bits(rng, (B, Hkv, T, D))
+    if lens is None:
+        lens = rng.integers(1, T + 1, size=B).astype(np.int32)
+    return q, kc, vc, np.asarray(lens, np.int32)
+
+
+def _sdpa(q, kc, vc, lens, window, scale):
+    """torch CPU fp64 SDPA over repeat_interleave-expanded KV heads, plus lse."""
+    B, Hq, D = q.shape
+    Hkv, T = kc.shape[1], kc.shape[2]
+    G = Hq // Hkv
+    K = torch.from_numpy(_torch_bf16_to_f64(kc)).repeat_interleave(G, dim=1)
+    V = torch.from_numpy(_torch_bf16_to_f64(vc)).repeat_interleave(G, dim=1)
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -math.inf)
+    for b in range(B):
+        n = min(max(int(lens[b]), 0), T)
+        lo = max(0, n - window) if window > 0 else 0
+        if n - lo == 0:
+            continue
+        mask = torch.zeros(1, T, dtype=torch.bool)
+        mask[0, lo:n] = True
+        qb = torch.from_numpy(q[b]).unsqueeze(1)           # [Hq,1,D]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qb, K[b], V[b], attn_mask=mask, scale=scale)
+        out[b] = o[:, 0].numpy()
+        s = (qb @ K[b].transpose(-1, -2))[:, 0, lo:n] * scale
+        lse[b] = torch.logsumexp(s, dim=-1).numpy()
+    return out, lse
+
+
+def pin_attend_matches_sdpa(O):
+    for k, (Hq, Hkv, D, window) in enumerate([(8, 2, 16, 0), (8, 8, 8, 0), (6, 3, 32, 0),
+                                              (8, 2, 16, 5), (4, 1, 8, 13)]):
+        q, kc, vc, lens = _rand_case(k, Hq=Hq, Hkv=Hkv, D=D)
+        scale = 1 / math.sqrt(D)
+        out, lse = O.attend(q, kc, vc, lens, window, 0.0)
+        ro, rl = _sdpa(q, kc, vc, lens, window, scale)
+        _close(out, ro, 1e-12, "attend vs sdpa")
+        _close(lse, rl, 1e-12, "lse vs logsumexp")
+
+
+def pin_attend_matches_bruteforce(O):
+    for k, (B, Hq, Hkv, D, T, window) in enumerate(
+            [(2, 4, 2, 8, 9, 0), (1, 4, 1, 4, 7, 3), (2, 2, 2, 6, 5, 0), (2, 4, 2, 8, 9, 1)]):
+        q, kc, vc, lens = _rand_case(10 + k, B=B, Hq=Hq, Hkv=Hkv, D=D, T=T)
+        K = _torch_bf16_to_f64(kc).tolist()
+        V = _torch_bf16_to_f64(vc).tolist()
+        bo, bl = BF.attend(q.tolist(), K, V, lens.tolist(), window, 0.0)
+        out, lse = O.attend(q, kc, vc, lens, window, 0.0)
+        _close(out, bo, 1e-12, "attend vs brute force")
+        _close(lse, bl, 1e-12, "lse vs brute force")
+
+
+def pin_attend_special_cases(O):
+    rng = _rng(20)
+    B, Hq, Hkv, D, T = 1, 4, 2, 16, 12
+    q = rng.standard_normal((B, Hq, D))
+    kc = _bits(rng, (B, Hkv, T, D))
+    vc = _bits(rng, (B, Hkv, T, D))
+    Kf, Vf = _torch_bf16_to_f64(kc), _torch_bf16_to_f64(vc)
+    scale = 1 / math.sqrt(D)
+    # n = 1 -> V[0] exactly, lse = s_0
+    out, lse = O.attend(q, kc, vc, np.array([1], np.int32), 0, 0.0)
+    for h in range(Hq):
+        g = h // 2
+        assert np.array_equal(out[0, h], Vf[0, g, 0])
+        assert abs(lse[0, h] - scale * np.dot(q[0, h], Kf[0, g, 0])) <= 1e-14
+    # V = all ones -> weights sum to one
+    ones = np.full_like(vc, 0x3F80)
+    out, _ = O.attend(q, kc, ones, np.array([T], np.int32), 0, 0.0)
+    _close(out, np.ones_like(out), 1e-14, "weights sum")
+    # identical keys -> mean(V), lse = s + ln n
+    kc_same = np.broadcast_to(kc[:, :, :1], kc.shape).copy()
+    out, lse = O.attend(q, kc_same, vc, np.array([T], np.int32), 0, 0.0)
+    for h in range(Hq):
+        g = h // 2
+        _close(out[0, h], Vf[0, g].mean(0), 1e-14, "mean V")
+        s = scale * np.dot(q[0, h], Kf[0, g, 0])
+        assert abs(lse[0, h] - (s + math.log(T))) <= 1e-13
+    # window = 1 -> V[n-1]
+    out, _ = O.attend(q, kc, vc, np.array([9], np.int32), 1, 0.0)
+    for h in range(Hq):
+        assert np.array_equal(out[0, h], Vf[0, h // 2, 8])
+    # window >= n -> full attention
+    full, fl = O.attend(q, kc, vc, np.array([9], np.int32), 0, 0.0)
+    for W in (9, 10, 1000):
+        o2, l2 = O.attend(q, kc, vc, np.array([9], np.int32), W, 0.0)
+        _close(o2, full, 0.0, "window>=n")
+        _close(l2, fl, 0.0, "window>=n lse")
+    # lens clamped to [0, T]; lens = 0 -> out 0, lse -inf
+    for W in (0, 5):
+        o_big, _ = O.attend(q, kc, vc, np.array([T + 50], np.int32), W, 0.0)
+        o_T, _ = O.attend(q, kc, vc, np.array([T], np.int32), W, 0.0)
+        _close(o_big, o_T, 0.0, "lens clamp")
+    for n0 in (0, -3):
+        o0, l0 = O.attend(q, kc, vc, np.array([n0], np.int32), 0, 0.0)
+        assert np.all(o0 == 0) and np.all(l0 == -math.inf)
+
+
+def pin_attend_two_key_closed_form(O):
+    """q = e_0, scale = 1, keys (a,0..), (b,0..): weights e^a, e^b."""
+    D = 4
+    a_, b_ = 1.5, -0.25                       # exact in bf16
+    q = np.zeros((1, 1, D)); q[0, 0, 0] = 1.0
+    K = np.zeros((2, D)); K[0, 0] = a_; K[1, 0] = b_
+    V = np.array([[1.0, 2.0, -1.0, 0.5], [3.0, -2.0, 0.25, 4.0]])
+    kc = O.f64_to_bf16(K)[None, None]
+    vc = O.f64_to_bf16(V)[None, None]
+    out, lse = O.attend(q, kc, vc, np.array([2], np.int32), 0, 1.0)
+    ea, eb = math.exp(a_), math.exp(b_)
+    _close(out[0, 0], (ea * V[0] + eb * V[1]) / (ea + eb), 1e-15, "two keys")
+    assert abs(lse[0, 0] - math.log(ea + eb)) <= 1e-15
+
+
+def pin_attend_affine_and_shift(O):
+    """V -> aV + c maps out -> a out + c; a constant added to every score
+    (through an extra key component) leaves out unchanged even at scores of
+    several hundred, where exp without max-subtraction overflows."""
+    rng = _rng(30)
+    B, Hq, Hkv, D, T = 1, 4, 2, 8, 20
+    q = rng.standard_normal((B, Hq, D))
+    kc = _bits(rng, (B, Hkv, T, D))
+    lens = np.array([T], np.int32)
+    # V on a grid k/8 so that 2V + 0.5 is exact in bf16 as well
+    grid = rng.integers(-16, 17, size=(B, Hkv, T, D)) / 8.0
+    to_bits = lambda a: torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    vc = to_bits(grid)
+    vc2 = to_bits(2.0 * grid + 0.5)
+    out, lse = O.attend(q, kc, vc, lens, 0, 0.0)
+    o2, l2 = O.attend(q, kc, vc2, lens, 0, 0.0)
+    _close(o2, 2.0 * out + 0.5, 1e-13, "affine V")
+    _close(l2, lse, 0.0, "affine V lse")
+    # shift: append a key component equal to 1 and a query component c.
+    K1 = np.concatenate([_torch_bf16_to_f64(kc), np.ones((B, Hkv, T, 1))], axis=-1)
+    kc1 = to_bits(K1)
+    for c in (0.0, 400.0, 2000.0):
+        q1 = np.concatenate([q, np.full((B, Hq, 1), c)], axis=-1)
+        o1, l1 = O.attend(q1, kc1, vc, lens, 0, 1 / math.sqrt(D))
+        _close(o1, out, 1e-12, f"shift {c}")
+        _close(l1 - c / math.sqrt(D), lse, 1e-9, f"shift lse {c}")
+
+
+# ---------------------------------------------------------------------------
+# Split-K partitions and the log-sum-exp merge
+# ---------------------------------------------------------------------------
+def pin_split_equals_unsplit(O):
+    for k, (T, window) in enumerate([(40, 0), (40, 11), (33, 0), (64, 64)]):
+        q, kc, vc, lens = _rand_case(40 + k, B=3, Hq=4, Hkv=2, D=8, T=T,
+                                     lens=[T, 1, max(2, T // 2 + 1)])
+        full, fl = O.attend(q, kc, vc, lens, window, 0.0)
+        for P in (1, 3, 8, T, T + 5):
+            o, l = O.attend_partials(q, kc, vc, lens, window, 0.0, P)
+            assert o.shape[2] == O.num_partitions(T, window, P)
+            mo, ml = O.lse_merge(o, l)
+            _close(mo, full, 1e-12, f"split P={P}")
+            _close(ml, fl, 1e-12, f"split lse P={P}")
+
+
+def pin_merge_random_cuts(O):
+    """Uneven cuts, including empty pieces, merge back to the whole."""
+    rng = _rng(50)
+    D, n = 8, 37
+    q = rng.standard_normal(D)
+    K = _torch_bf16_to_f64(_bits(rng, (n, D)))
+    V = _torch_bf16_to_f64(_bits(rng, (n, D)))
+    whole, wl = O.attend_rows(q, K, V, 0.3)
+    for trial in range(5):
+        cuts = np.sort(rng.integers(0, n + 1, size=6))
+        edges = [0] + list(cuts) + [n]
+        os_, ls_ = [], []
+        for a, e in zip(edges[:-1], edges[1:]):
+            o, l = O.attend_rows(q, K[a:e], V[a:e], 0.3)
+            os_.append(o)
+            ls_.append(l)
+        mo, ml = O.lse_merge(np.array(os_)[None], np.array(ls_)[None])
+        _close(mo[0], whole, 1e-12, "random cuts")
+        assert abs(ml[0] - wl) <= 1e-12
+    # all-empty -> zeros and -inf
+    mo, ml = O.lse_merge(np.zeros((1, 3, D)), np.full((1, 3), -math.inf))
+    assert np.all(mo == 0) and ml[0] == -math.inf
+
+
+def pin_merge_peaky_partials(O):
+    """Partials whose lse differ by hundreds: max-subtraction keeps it finite
+    and the dominant partition wins."""
+    D = 4
+    o = np.array([[[1.0, 2, 3, 4], [5.0, 6, 7, 8], [9.0, 1, 1, 1]]])
+    lse = np.array([[800.0, 0.0, -math.inf]])
+    mo, ml = O.lse_merge(o, lse)
+    w1 = math.exp(-800.0)
+    _close(mo[0], (o[0, 0] + w1 * o[0, 1]) / (1 + w1), 1e-15, "peaky merge")
+    assert abs(ml[0] - (800.0 + math.log1p(w1))) <= 1e-12
+    # equal lse -> plain mean
+    mo, ml = O.lse_merge(o[:, :2], np.array([[2.0, 2.0]]))
+    _close(mo[0], (o[0, 0] + o[0, 1]) / 2, 1e-15, "equal merge")
+    assert abs(ml[0] - (2.0 + math.log(2))) <= 1e-15
+
+
+def pin_num_partitions(O):
+    assert O.num_partitions(131072, 0, 2048) == 64
+    assert O.num_partitions(32768, 4096, 512) == 8
+    assert O.num_partitions(100, 0, 7) == 15
+    assert O.num_partitions(100, 30, 7) == 5
+    assert O.num_partitions(10, 30, 7) == 2
+
+
+# ---------------------------------------------------------------------------
+# Fused prologue
+# ---------------------------------------------------------------------------
+def _prologue_case(k, norm=True, theta=1e4, B=2, Hq=4, Hkv=2, D=8, T=6, pos=(2, 5)):
+    rng = _rng(60 + k)
+    q = _torch_bf16_to_f64(_bits(rng, (B, Hq, D)))
+    kn = _torch_bf16_to_f64(_bits(rng, (B, Hkv, D)))
+    vn = _torch_bf16_to_f64(_bits(rng, (B, Hkv, D)))
+    kc = _bits(rng, (B, Hkv, T, D))
+    vc = _bits(rng, (B, Hkv, T, D))
+    wq = 1 + 0.1 * rng.standard_normal(D) if norm else None
+    wk = 1 + 0.1 * rng.standard_normal(D) if norm else None
+    return q, kn, vn, wq, wk, np.array(pos, np.int32), kc, vc
+
+
+def pin_prologue_matches_bruteforce(O):
+    for k, (norm, theta) in enumerate([(True, 1e4), (False, 5e5), (True, 0.0), (False, 0.0)]):
+        q, kn, vn, wq, wk, pos, kc, vc = _prologue_case(k, norm, theta)
+        eps = 1e-6
+        qh, kc2, vc2 = O.qkv_prologue(q, kn, vn, wq, wk, eps, theta, pos, kc, vc)
+        B, Hq, D = q.shape
+        for b in range(B):
+            for h in range(Hq):
+                x = list(q[b, h])
+                if norm:
+                    x = BF.rmsnorm(x, list(wq), eps)
+                if theta > 0:
+                    x = BF.rope_neox(x, int(pos[b]), theta)
+                _close(qh[b, h], x, 1e-12, "q_hat")
+            for g in range(kn.shape[1]):
+                x = list(kn[b, g])
+                if norm:
+                    x = BF.rmsnorm(x, list(wk), eps)
+                if theta > 0:
+                    x = BF.rope_neox(x, int(pos[b]), theta)
+                row = _torch_bf16_to_f64(kc2[b, g, pos[b]])
+                x = np.array(x)
+                # within half a bf16 ulp (2^-9 relative) of the exact value
+                half_ulp = np.ldexp(1.0, np.frexp(x)[1] - 9)
+                assert np.all(np.abs(row - x) <= half_ulp + 1e-300), (row, x)
+                if not norm and theta <= 0:
+                    assert np.array_equal(row, kn[b, g])
+
+
+def pin_prologue_writes_only_pos_rows(O):
+    q, kn, vn, wq, wk, pos, kc, vc = _prologue_case(9)
+    _, kc2, vc2 = O.qkv_prologue(q, kn, vn, wq, wk, 1e-6, 1e4, pos, kc, vc)
+    B, Hkv, T, D = kc.shape
+    for b in range(B):
+        for g in range(Hkv):
+            for t in range(T):
+                same_k = np.array_equal(kc2[b, g, t], kc[b, g, t])
+                same_v = np.array_equal(vc2[b, g, t], vc[b, g, t])
+                if t == pos[b]:
+                    # V row is the new value, bit for bit (bf16 in, bf16 out)
+                    assert np.array_equal(_torch_bf16_to_f64(vc2[b, g, t]), vn[b, g])
+                else:
+                    assert same_k and same_v, (b, g, t)
+    # out-of-range positions write nothing but still rotate q
+    for bad in ((-1, 6), (6, 100)):
+        qh, kc3, vc3 = O.qkv_prologue(q, kn, vn, wq, wk, 1e-6, 1e4,
+                                      np.array(bad, np.int32), kc, vc)
+        assert np.array_equal(kc3, kc) and np.array_equal(vc3, vc)
+        x = BF.rope_neox(BF.rmsnorm(list(q[1, 0]), list(wq), 1e-6), bad[1], 1e4)
+        _close(qh[1, 0], x, 1e-12, "q_hat out of range pos")
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

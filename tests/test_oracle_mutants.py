@@ -1,0 +1,287 @@
+"""Mutation tests for the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in the oracle -- a dropped term, a
+wrong sign or index, a transposed operand, a wrong rounding -- by replacing
+one of its module-level functions, then runs every pin.  The pins are good
+enough only if at least one of them fails for every planted mistake.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle_pins
+from oracle import reference as R
+
+_orig = {k: getattr(R, k) for k in dir(R) if not k.startswith("__")}
+
+
+# --- bf16 --------------------------------------------------------------------
+def _bf16_truncate(x):
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    return (x32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_double_round(x):
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _bf16_ties_away(x):
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)
+    r = np.sign(m) * np.floor(np.abs(np.ldexp(m, 8)) + 0.5)
+    r = np.ldexp(r, e - 8)
+    with np.errstate(over="ignore"):
+        return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _bf16_decode_abs(bits):
+    return np.abs(_orig["bf16_to_f64"](bits))
+
+
+# --- rmsnorm -----------------------------------------------------------------
+def _rms_no_eps(x, w, eps):
+    return _orig["rmsnorm"](x, w, 0.0)
+
+
+def _rms_one_plus_w(x, w, eps):
+    return _orig["rmsnorm"](x, 1.0 + np.asarray(w, np.float64), eps)
+
+
+def _rms_sum_not_mean(x, w, eps):
+    n = np.asarray(x).shape[-1]
+    return _orig["rmsnorm"](x, np.asarray(w, np.float64) / math.sqrt(n), eps / n)
+
+
+def _rms_no_sqrt(x, w, eps):
+    x = np.asarray(x, np.float64)
+    return x / (np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+
+
+# --- rope --------------------------------------------------------------------
+def _rope_neg(x, pos, theta):
+    return _orig["rope_neox"](x, -np.asarray(pos), theta)
+
+
+def _rope_interleaved(x, pos, theta):
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])
+    y = _orig["rope_neox"](x[..., perm], pos, theta)
+    out = np.empty_like(y)
+    out[..., perm] = y
+    return out
+
+
+def _rope_pos_plus_one(x, pos, theta):
+    return _orig["rope_neox"](x, np.asarray(pos) + 1, theta)
+
+
+def _inv_freq_half_exponent(D, theta):
+    return np.power(float(theta), -1.0 * np.arange(D // 2) / D)
+
+
+def _rope_cos_sin_swapped(x, pos, theta):
+    x = np.asarray(x, np.float64)
+    D = x.shape[-1]
+    h = D // 2
+    a = np.asarray(pos, np.float64)[..., None] * _orig["rope_inv_freq"](D, theta)
+    c, s = np.sin(a), np.cos(a)
+    return np.concatenate([x[..., :h] * c - x[..., h:] * s, x[..., h:] * c + x[..., :h] * s], -1)
+
+
+# --- attention -----------------------------------------------------------------
+def _rows_no_max(q, K, V, scale):
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[-1]), -math.inf
+    with np.errstate(over="ignore", invalid="ignore"):
+        p = np.exp(scale * (K @ q))
+        l = np.sum(p)
+        return (p @ V) / l, math.log(l) if np.isfinite(l) and l > 0 else math.inf
+
+
+def _rows_lse_no_m(q, K, V, scale):
+    o, l = _orig["attend_rows"](q, K, V, scale)
+    if K.shape[0] == 0:
+        return o, l
+    return o, l - np.max(scale * (K @ q))
+
+
+def _rows_swapped(q, K, V, scale):
+    return _orig["attend_rows"](q, V, K, scale)
+
+
+def _rows_unnormalised(q, K, V, scale):
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[-1]), -math.inf
+    s = scale * (K @ q)
+    m = np.max(s)
+    p = np.exp(s - m)
+    return p @ V, m + math.log(np.sum(p))
+
+
+def _rows_scale_ignored(q, K, V, scale):
+    return _orig["attend_rows"](q, K, V, 1.0)
+
+
+def _window_off_by_one(n_raw, T, window):
+    n = min(max(int(n_raw), 0), T)
+    lo = max(0, n - window + 1) if window > 0 else 0
+    return lo, n
+
+
+def _window_no_clamp(n_raw, T, window):
+    n = max(int(n_raw), 0)
+    lo = max(0, n - window) if window > 0 else 0
+    return min(lo, T), n
+
+
+def _attend_head_mod(q, k_cache, v_cache, lens, window=0, scale=0.0):
+    q = np.asarray(q, np.float64)
+    B, Hq, D = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    if scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    out = np.zeros((B, Hq, v_cache.shape[3]))
+    lse = np.full((B, Hq), -math.inf)
+    for b in range(B):
+        lo, n = R._window(lens[b], T, window)
+        for h in range(Hq):
+            g = h % Hkv
+            K = R.bf16_to_f64(k_cache[b, g, lo:n])
+            V = R.bf16_to_f64(v_cache[b, g, lo:n])
+            out[b, h], lse[b, h] = R.attend_rows(q[b, h], K, V, scale)
+    return out, lse
+
+
+# --- split / merge ---------------------------------------------------------------
+def _ranges_from_zero(lo, n, P, count):
+    return _orig["partition_ranges"](0, n, P, count)
+
+
+def _num_parts_floor(T, window, P):
+    span = min(T, window) if window > 0 else T
+    return max(1, span // P)
+
+
+def _merge_no_max(o_parts, lse_parts):
+    o_parts = np.asarray(o_parts, np.float64)
+    lse_parts = np.asarray(lse_parts, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        w = np.exp(lse_parts)
+        W = np.sum(w, -1)
+        return np.einsum("...k,...kd->...d", w, o_parts) / W[..., None], np.log(W)
+
+
+def _merge_unweighted(o_parts, lse_parts):
+    o, l = _orig["lse_merge"](o_parts, lse_parts)
+    o_parts = np.asarray(o_parts, np.float64)
+    fin = np.isfinite(np.asarray(lse_parts))
+    cnt = np.maximum(fin.sum(-1), 1)
+    return (o_parts * fin[..., None]).sum(-2) / cnt[..., None], l
+
+
+def _merge_log2(o_parts, lse_parts):
+    o, l = _orig["lse_merge"](o_parts, lse_parts)
+    return o, l / math.log(2)
+
+
+def _merge_no_empty_guard(o_parts, lse_parts):
+    o_parts = np.asarray(o_parts, np.float64)
+    lse_parts = np.asarray(lse_parts, np.float64)
+    with np.errstate(invalid="ignore"):
+        M = np.max(lse_parts, -1, keepdims=True)
+        w = np.exp(lse_parts - M)
+        W = np.sum(w, -1)
+        return np.einsum("...k,...kd->...d", w, o_parts) / W[..., None], M[..., 0] + np.log(W)
+
+
+# --- prologue ----------------------------------------------------------------------
+def _prologue_variant(kind):
+    def f(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache):
+        q = np.array(q, np.float64)
+        k = np.array(k_new, np.float64)
+        v = np.array(v_new, np.float64)
+        B, Hq, D = q.shape
+        Hkv, T = k.shape[1], k_cache.shape[2]
+        kc, vc = k_cache.copy(), v_cache.copy()
+        qh = np.empty_like(q)
+
+        def proc(x, w, p):
+            if kind == "rope_first":
+                if theta > 0:
+                    x = R.rope_neox(x, p, theta)
+                if w is not None:
+                    x = R.rmsnorm(x, w, eps)
+                return x
+            if w is not None:
+                x = R.rmsnorm(x, w, eps)
+            if theta > 0:
+                x = R.rope_neox(x, p, theta)
+            return x
+        for b in range(B):
+            p = int(pos[b])
+            for h in range(Hq):
+                qh[b, h] = proc(q[b, h], w_k if kind == "wk_for_q" else w_q, p)
+            for g in range(Hkv):
+                x = proc(k[b, g], w_k, p)
+                vv = v[b, g]
+                if kind == "rotate_v" and theta > 0:
+                    vv = R.rope_neox(vv, p, theta)
+                row = p + 1 if kind == "pos_plus_one" else p
+                if 0 <= row < T:
+                    kc[b, g, row] = R.f64_to_bf16(x)
+                    vc[b, g, row] = R.f64_to_bf16(vv)
+        return qh, kc, vc
+    return f
+
+
+MUTANTS = {
+    "bf16_truncate": {"f64_to_bf16": _bf16_truncate},
+    "bf16_double_round": {"f64_to_bf16": _bf16_double_round},
+    "bf16_ties_away": {"f64_to_bf16": _bf16_ties_away},
+    "bf16_decode_abs": {"bf16_to_f64": _bf16_decode_abs},
+    "rms_no_eps": {"rmsnorm": _rms_no_eps},
+    "rms_one_plus_w": {"rmsnorm": _rms_one_plus_w},
+    "rms_sum_not_mean": {"rmsnorm": _rms_sum_not_mean},
+    "rms_no_sqrt": {"rmsnorm": _rms_no_sqrt},
+    "rope_negative_angle": {"rope_neox": _rope_neg},
+    "rope_interleaved_pairs": {"rope_neox": _rope_interleaved},
+    "rope_pos_plus_one": {"rope_neox": _rope_pos_plus_one},
+    "rope_half_exponent": {"rope_inv_freq": _inv_freq_half_exponent},
+    "rope_cos_sin_swapped": {"rope_neox": _rope_cos_sin_swapped},
+    "attn_no_max_subtraction": {"attend_rows": _rows_no_max},
+    "attn_lse_without_max": {"attend_rows": _rows_lse_no_m},
+    "attn_k_v_swapped": {"attend_rows": _rows_swapped},
+    "attn_unnormalised": {"attend_rows": _rows_unnormalised},
+    "attn_scale_ignored": {"attend_rows": _rows_scale_ignored},
+    "attn_window_off_by_one": {"_window": _window_off_by_one},
+    "attn_lens_not_clamped": {"_window": _window_no_clamp},
+    "attn_head_map_modulo": {"attend": _attend_head_mod},
+    "split_ignores_window_start": {"partition_ranges": _ranges_from_zero},
+    "split_count_floor": {"num_partitions": _num_parts_floor},
+    "merge_no_max_subtraction": {"lse_merge": _merge_no_max},
+    "merge_unweighted": {"lse_merge": _merge_unweighted},
+    "merge_lse_base2": {"lse_merge": _merge_log2},
+    "merge_no_empty_guard": {"lse_merge": _merge_no_empty_guard},
+    "prologue_rope_before_norm": {"qkv_prologue": _prologue_variant("rope_first")},
+    "prologue_wk_for_q": {"qkv_prologue": _prologue_variant("wk_for_q")},
+    "prologue_rotates_v": {"qkv_prologue": _prologue_variant("rotate_v")},
+    "prologue_writes_pos_plus_one": {"qkv_prologue": _prologue_variant("pos_plus_one")},
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    for attr, fn in MUTANTS[name].items():
+        monkeypatch.setattr(R, attr, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(R)
+        except Exception as e:  # noqa: BLE001 - any failure counts as a catch
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin detects the planted mistake {name}"

@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for single-token GQA decode attention.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests
+and benchmark.  It only draws random numbers and lays them out; it performs
+none of the attention method's arithmetic (no normalisation, rotation,
+softmax, or rounding of computed values).  The one numeric conversion here
+is fp32 -> bf16 of freshly drawn N(0,1) samples, which is how bf16 inputs
+are produced in the first place.
+
+Workload shapes follow the five decode configurations the build targets:
+a tiny step, a Qwen3-0.6B-shaped layer, a Llama-3-8B-shaped batch with
+ragged lengths, a 128K-token long-context split-K case with a peaky
+softmax, and a 70B-shaped sliding-window case.  Every array is produced
+from ``numpy.random.default_rng(seed)`` (PCG64) in a fixed draw order:
+
+    lens (ragged configs only), q, k_new, v_new, K cache, V cache,
+    w_q, w_k (QK-norm configs only), peaky row indices (peaky configs only)
+
+Normal draws are float32 ``standard_normal`` rounded to bf16 with
+round-to-nearest-even; caches are generated in chunks so that the host
+never holds a float32 copy of a whole cache.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = ["Workload", "make", "CONFIGS", "kv_bytes", "fp32_to_bf16_bits"]
+
+# Chunk (in elements) for drawing cache contents: 16M float32 = 64 MiB.
+_CHUNK = 1 << 24
+
+
+def fp32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 samples to bf16 (nearest, ties to even); return uint16 bits.
+
+    Used only to turn freshly drawn finite float32 samples into bf16 inputs.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = fp32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+@dataclasses.dataclass
+class Workload:
+    """One decode step's inputs (host arrays) plus its launch configuration.
+
+    Shapes: q [B,Hq,D], k_new/v_new [B,Hkv,D], k_cache/v_cache [B,Hkv,T,D],
+    all bf16 stored as uint16 bit patterns.  ``pos`` is the RoPE position of
+    the new token, which is also the cache row it is written to; ``lens`` is
+    the number of cache rows [0, lens[b]) attended after the append.
+    ``prologue`` False means q is given directly to attention (no norm, RoPE
+    or append).  ``theta`` <= 0 disables RoPE; ``w_q``/``w_k`` None disables
+    QK-RMSNorm.  ``window`` <= 0 is full attention.
+    """
+
+    name: str
+    seed: int
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    T: int
+    lens: np.ndarray                 # int32 [B]
+    pos: Optional[np.ndarray]        # int32 [B] (None without a prologue)
+    window: int
+    theta: float
+    eps: float
+    out_dtype: str                   # "f32" | "bf16"
+    part_tokens: int                 # split-K partition size used by the bench
+    q: np.ndarray                    # uint16 [B,Hq,D]
+    k_new: Optional[np.ndarray]      # uint16 [B,Hkv,D]
+    v_new: Optional[np.ndarray]
+    k_cache: np.ndarray              # uint16 [B,Hkv,T,D]
+    v_cache: np.ndarray
+    w_q: Optional[np.ndarray]        # float32 [D]
+    w_k: Optional[np.ndarray]
+    peaky_rows: Optional[np.ndarray] = None  # int64 [B,Hkv,m] rows of K scaled by 4
+
+    @property
+    def prologue(self) -> bool:
+        return self.pos is not None
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def attended(self) -> np.ndarray:
+        """Rows attended per sequence, n_b - lo_b (after clamping lens to [0,T])."""
+        n = np.clip(self.lens.astype(np.int64), 0, self.T)
+        if self.window > 0:
+            return n - np.maximum(0, n - self.window)
+        return n
+
+
+def kv_bytes(w: Workload) -> int:
+    """Algorithmic KV-cache bytes one decode step reads: K and V rows of the
+    attended window, bf16, every KV head of every sequence."""
+    return int(w.attended().sum()) * w.Hkv * w.D * 2 * 2
+
+
+# name -> (base parameters).  Sizes may be overridden for reduced test cases.
+CONFIGS: Dict[str, dict] = {
+    # tiny step: B1 Hq8 Hkv2 D64 L128, RoPE 1e4 at pos L-1, no QK-norm
+    "1": dict(seed=1, B=1, Hq=8, Hkv=2, D=64, L=128, layout="last",
+              window=0, theta=1e4, norm=False, out_dtype="f32", part_tokens=64),
+    # Qwen3-0.6B-shaped layer, L in {512, 2048}; new token at pos=L
+    "2a": dict(seed=2, B=1, Hq=16, Hkv=8, D=128, L=512, layout="append",
+               window=0, theta=1e6, norm=True, out_dtype="f32", part_tokens=128),
+    "2b": dict(seed=2, B=1, Hq=16, Hkv=8, D=128, L=2048, layout="append",
+               window=0, theta=1e6, norm=True, out_dtype="f32", part_tokens=256),
+    # Llama-3-8B-shaped batch, ragged lens ~ U{128..4096}, bf16 output
+    "3": dict(seed=3, B=32, Hq=32, Hkv=8, D=128, L=4096, layout="ragged",
+              lmin=128, window=0, theta=5e5, norm=False, out_dtype="bf16",
+              part_tokens=512),
+    # long context, no prologue, q given in bf16, 1% of K rows x4, P=2048
+    "4": dict(seed=4, B=1, Hq=32, Hkv=8, D=128, L=131072, layout="noprologue",
+              window=0, theta=0.0, norm=False, out_dtype="f32", part_tokens=2048,
+              peaky=0.01),
+    # 70B-shaped sliding window: B8 Hq64 Hkv8 L32768, W=4096
+    "5": dict(seed=5, B=8, Hq=64, Hkv=8, D=128, L=32768, layout="last",
+              window=4096, theta=5e5, norm=True, out_dtype="f32", part_tokens=512),
+}
+
+
+def make(name: str, seed: Optional[int] = None, **over) -> Workload:
+    """Build workload ``name`` (a key of CONFIGS) with optional overrides.
+
+    Overrides accept any base key (B, Hq, Hkv, D, L, window, theta, norm,
+    out_dtype, part_tokens, peaky, lmin) plus ``T`` for ragged layouts.
+    Layouts:
+      last       T = L, new token at pos = L-1, lens = L
+      append     T = L + 64, new token at pos = L, lens = L + 1
+      ragged     T = L, lens ~ U{lmin..L}, pos = lens - 1
+      noprologue T = L, lens = L, q given directly
+    """
+    p = dict(CONFIGS[name])
+    p.update(over)
+    seed = p["seed"] if seed is None else seed
+    B, Hq, Hkv, D, L = p["B"], p["Hq"], p["Hkv"], p["D"], p["L"]
+    layout = p["layout"]
+    rng = np.random.default_rng(seed)
+
+    if layout == "last":
+        T = L
+        lens = np.full(B, L, np.int32)
+        pos = np.full(B, L - 1, np.int32)
+    elif layout == "append":
+        T = p.get("T", L + 64)
+        lens = np.full(B, L + 1, np.int32)
+        pos = np.full(B, L, np.int32)
+    elif layout == "ragged":
+        T = p.get("T", L)
+        lens = rng.integers(p["lmin"], L, size=B, endpoint=True).astype(np.int32)
+        pos = (lens - 1).astype(np.int32)
+    elif layout == "noprologue":
+        T = L
+        lens = np.full(B, L, np.int32)
+        pos = None
+    else:
+        raise ValueError(layout)
+
+    q = _normal_bf16(rng, (B, Hq, D))
+    if pos is not None:
+        k_new = _normal_bf16(rng, (B, Hkv, D))
+        v_new = _normal_bf16(rng, (B, Hkv, D))
+    else:
+        k_new = v_new = None
+    k_cache = _normal_bf16(rng, (B, Hkv, T, D))
+    v_cache = _normal_bf16(rng, (B, Hkv, T, D))
+    if p["norm"]:
+        w_q = (1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)).astype(np.float32)
+        w_k = (1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)).astype(np.float32)
+    else:
+        w_q = w_k = None
+
+    peaky_rows = None
+    frac = p.get("peaky", 0.0)
+    if frac:
+        # Scale round(frac * n) distinct rows of K by 4 in every (b, kv head).
+        # Multiplying a bf16 value by 4 adds 2 to its exponent: exact.
+        n = int(lens[0])
+        m = int(round(frac * n))
+        peaky_rows = np.empty((B, Hkv, m), np.int64)
+        for b in range(B):
+            for g in range(Hkv):
+                rows = rng.choice(n, size=m, replace=False)
+                peaky_rows[b, g] = rows
+                blk = k_cache[b, g, rows].astype(np.uint32) << 16
+                blk = (blk.view(np.float32) * np.float32(4.0)).view(np.uint32)
+                k_cache[b, g, rows] = (blk >> 16).astype(np.uint16)
+
+    return Workload(
+        name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, D=D, T=T, lens=lens, pos=pos,
+        window=int(p["window"]), theta=float(p["theta"]), eps=1e-6,
+        out_dtype=p["out_dtype"], part_tokens=int(p["part_tokens"]),
+        q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+        w_q=w_q, w_k=w_k, peaky_rows=peaky_rows)
