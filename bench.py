@@ -1,0 +1,245 @@
+"""Decode-attention benchmark on one MI355X.
+
+One step = one pass of the whole decode hot path over one batch: the fused
+prologue (QK-RMSNorm + NeoX RoPE + K/V append), the split-K attention pass,
+and the log-sum-exp merge, each one C-ABI call on torch's current stream,
+with every input already resident in HBM.  Before each timed step, a 1 GiB
+read-modify-write sweeps the L2s and the Infinity Cache so the KV window is
+read from HBM (outside the timed region).
+
+Prints ONE JSON line.  ``value`` is the step's KV-read throughput: KV-cache
+bytes the step must read (K and V rows of every attended window, bf16) per
+second of whole-step time, in GB/s.  ``roofline`` rates the dominant kernel
+(the split-K attention pass) against MI355X's 8 TB/s HBM peak, with its
+duration from HIP events on the launch stream.  ``cpu_baseline`` times the
+fp64 CPU oracle on the same workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("decode-attention µs/step and achieved KV-read HBM GB/s "
+          "(% of MI355X peak)")
+HBM_PEAK_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "gqa_attention_kv_amd", "csrc", "attn_decode.hip")
+
+WORKLOAD_NAMES = {
+    "1": "tiny GQA decode step",
+    "2a": "Qwen3-0.6B-shaped decode layer, L=512",
+    "2b": "Qwen3-0.6B-shaped decode layer, L=2048",
+    "3": "Llama-3-8B-shaped batched decode, ragged lengths",
+    "4": "long-context flash-decoding, L=131072",
+    "5": "70B-shaped sliding-window GQA decode (8:1)",
+}
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="5", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the cache sweep between steps (warm-cache figure)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time spent timing the oracle")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also time a plain device copy of this many MiB")
+    return ap.parse_args()
+
+
+def _src_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per attention launch from committed rocprofv3 counters, if
+    they were taken on the current attention kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attn_traffic_workload{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("attn_src_sha") != _src_sha(ATTN_SRC):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _cpu_baseline(w, min_seconds: float):
+    """Time the fp64 oracle's decode step on this host (a baseline, not a target)."""
+    import threadpoolctl
+    import workloads
+    from oracle import reference as oracle
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_step(w, split=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= 20:
+            break
+    kvb = workloads.kv_bytes(w)
+    return {
+        "value": round(kvb * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{reps} full decode step(s) of the same workload (prologue + unsplit "
+                   f"attention, float64 numpy), {el:.1f} s wall, "
+                   f"{1e6 * el / reps:.0f} us/step"),
+    }
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from gqa_attention_kv_amd.runner import DeviceStep
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = workloads.make(args.workload)
+    kvb = workloads.kv_bytes(w)
+    step = DeviceStep(w, device=dev, split=True)
+    flush = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+
+    def one_step(evs=None):
+        if flush is not None:
+            flush.add_(1)
+        if evs is not None:
+            evs[0].record()
+        step.prologue()
+        if evs is not None:
+            evs[1].record()
+        step.attention()
+        if evs is not None:
+            evs[2].record()
+        step.merge()
+        if evs is not None:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    pro_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    mean_step = statistics.fmean(step_ms)
+    mean_attn = statistics.fmean(attn_ms)
+    value = kvb / (mean_step * 1e-3) / 1e9
+    achieved = kvb / (mean_attn * 1e-3) / 1e9
+
+    res = step.results()
+    finite = bool(all(math.isfinite(x) for x in res["out"].reshape(-1)[:4096]))
+
+    copy_probe = None
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 18
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        ts = []
+        for _ in range(5):
+            if flush is not None:
+                flush.add_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst.copy_(src)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        t = statistics.median(ts)
+        copy_probe = {"bytes": 2 * n * 4, "ms": round(t, 4),
+                      "GBps": round(2 * n * 4 / (t * 1e-3) / 1e9, 1)}
+
+    cpu = None if args.no_cpu_baseline else _cpu_baseline(w, args.cpu_seconds)
+
+    traffic = _traffic(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_step, 5),
+        "us_per_step": round(1e3 * mean_step, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.workload],
+            "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D, "T": w.T,
+            "window": w.window, "part_tokens": w.part_tokens, "out_dtype": w.out_dtype,
+            "prologue": ("qk_rmsnorm+rope+append" if w.w_q is not None else
+                         "rope+append") if w.pos is not None else "none",
+            "kv_bytes_per_step": kvb,
+            "cache_flush_between_steps": flush is not None,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_decode_kernel (split-K partition pass)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "kernels_us": {
+            "prologue": round(1e3 * statistics.fmean(pro_ms), 2),
+            "attn_splitk": round(1e3 * mean_attn, 2),
+            "merge": round(1e3 * statistics.fmean(merge_ms), 2),
+            "step_p10": round(1e3 * sorted(step_ms)[len(step_ms) // 10], 2),
+            "step_p90": round(1e3 * sorted(step_ms)[(9 * len(step_ms)) // 10], 2),
+        },
+        "wall_s_timed_loop": round(wall, 4),
+        "output_finite": finite,
+        "cpu_baseline": cpu,
+    }
+    if copy_probe:
+        line["copy_probe"] = copy_probe
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

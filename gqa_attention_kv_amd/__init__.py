@@ -1,0 +1,247 @@
+"""Python binding of the gfx950 GQA decode-attention library.
+
+Argument marshalling only: each function checks torch tensors (dtype,
+device, layout), passes their device pointers and torch's current HIP
+stream to the C ABI in ``include/gqa_decode.h``, and raises on a non-zero
+status.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback.  Importing fails loudly when the library is missing.
+
+Functions follow the C entry points' names without the ``gqa_`` prefix:
+``qkv_prologue``, ``attn_decode``, ``attn_decode_splitk``,
+``attn_decode_merge``, ``splitk_workspace_bytes``, ``num_partitions``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from ._build import LIB_PATH
+
+__all__ = [
+    "GQAError", "lib", "qkv_prologue", "attn_decode", "attn_decode_splitk",
+    "attn_decode_merge", "splitk_workspace_bytes", "num_partitions",
+    "F32", "BF16", "SYMBOLS",
+]
+
+F32, BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -c 'import __graft_entry__ as g; g.build()')")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+_f = ctypes.c_float
+_d = ctypes.c_double
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); every symbol the header declares.
+SYMBOLS = {
+    "gqa_qkv_prologue": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _d, _p, _p, _p, _p,
+                              _i, _i, _i, _i, _i, _p]),
+    "gqa_attn_decode": (_i, [_p, _i, _p, _p, _p, _i, _f, _p, _i, _p, _i, _i, _i, _i, _i, _p]),
+    "gqa_num_partitions": (_i, [_i, _i, _i]),
+    "gqa_splitk_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "gqa_attn_decode_splitk": (_i, [_p, _i, _p, _p, _p, _i, _f, _i, _p, _sz,
+                                    _i, _i, _i, _i, _i, _p]),
+    "gqa_attn_decode_merge": (_i, [_p, _sz, _i, _i, _p, _i, _p, _i, _i, _i, _i, _p]),
+    "gqa_status_string": (ctypes.c_char_p, [_i]),
+}
+for _name, (_res, _args) in SYMBOLS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class GQAError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"gqa status {status}: {lib.gqa_status_string(status).decode()}")
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise GQAError(rc)
+
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _dtype_code(t: torch.Tensor, what: str) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"{what}: dtype {t.dtype} not supported (float32 or bfloat16)")
+    return _DT[t.dtype]
+
+
+def _dev(t: torch.Tensor, what: str, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+
+
+def _contig(t: torch.Tensor, what: str):
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def num_partitions(T: int, window: int, part_tokens: int) -> int:
+    return int(lib.gqa_num_partitions(T, window, part_tokens))
+
+
+def splitk_workspace_bytes(B: int, Hq: int, D: int, T: int, window: int,
+                           part_tokens: int) -> int:
+    return int(lib.gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens))
+
+
+def qkv_prologue(q, k_new, v_new, pos, k_cache, v_cache, q_norm_w=None, k_norm_w=None,
+                 eps: float = 1e-6, rope_theta: float = 0.0, q_out=None):
+    """QK-RMSNorm + NeoX RoPE at pos[b] + append of k/v at row pos[b].
+
+    q [B,Hq,D], k_new/v_new [B,Hkv,D] (float32 or bfloat16, heads contiguous,
+    any batch stride, k_new and v_new with the same batch stride);
+    pos int32 [B]; caches bfloat16 [B,Hkv,T,D] (written in place);
+    norm weights float32 [D] or None.  Returns q_out float32 [B,Hq,D].
+    """
+    dev = k_cache.device
+    for t, w in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (pos, "pos"),
+                 (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, w, dev)
+    B, Hq, D = q.shape
+    _, Hkv, T, _ = k_cache.shape
+    if q.dtype != k_new.dtype or q.dtype != v_new.dtype:
+        raise TypeError("q, k_new and v_new must share a dtype")
+    code = _dtype_code(q, "q")
+    for t, w, h in ((q, "q", Hq), (k_new, "k_new", Hkv), (v_new, "v_new", Hkv)):
+        if tuple(t.shape) != (B, h, D) or t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{w}: expected [B,{h},D] with contiguous heads")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must share a batch stride")
+    for t, w in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, Hkv, T, D):
+            raise ValueError(f"{w}: expected bfloat16 [B,Hkv,T,D]")
+        _contig(t, w)
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (B,):
+        raise ValueError("pos must be int32 [B]")
+    _contig(pos, "pos")
+    for w, nm in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _dev(w, nm, dev)
+            if w.dtype != torch.float32 or tuple(w.shape) != (D,):
+                raise ValueError(f"{nm} must be float32 [D]")
+            _contig(w, nm)
+    if q_out is None:
+        q_out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _check(lib.gqa_qkv_prologue(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0), k_new.stride(0),
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), float(rope_theta), _ptr(pos),
+        _ptr(q_out), _ptr(k_cache), _ptr(v_cache), B, Hq, Hkv, D, T, _stream(dev)))
+    return q_out
+
+
+def _attn_common(q, k_cache, v_cache, lens):
+    dev = k_cache.device
+    for t, w in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (lens, "lens")):
+        _dev(t, w, dev)
+        _contig(t, w)
+    B, Hq, D = q.shape
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must be [B,Hkv,T,D] of equal shape")
+    _, Hkv, T, Dk = k_cache.shape
+    if k_cache.shape[0] != B or Dk != D:
+        raise ValueError("cache shape does not match q")
+    if k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("caches must be bfloat16")
+    if lens.dtype != torch.int32 or tuple(lens.shape) != (B,):
+        raise ValueError("lens must be int32 [B]")
+    return dev, B, Hq, Hkv, D, T
+
+
+def _lse_check(lse_out, B, Hq, dev):
+    if lse_out is not None:
+        _dev(lse_out, "lse_out", dev)
+        _contig(lse_out, "lse_out")
+        if lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (B, Hq):
+            raise ValueError("lse_out must be float32 [B,Hq]")
+
+
+def attn_decode(q, k_cache, v_cache, lens, window: int = 0, scale: float = 0.0,
+                out=None, out_dtype=torch.float32, lse_out=None):
+    """Unsplit decode attention: one workgroup per (sequence, KV head).
+
+    Returns ``out`` [B,Hq,D]; writes the natural-log LSE into ``lse_out``
+    (float32 [B,Hq]) when given."""
+    dev, B, Hq, Hkv, D, T = _attn_common(q, k_cache, v_cache, lens)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+    _dev(out, "out", dev)
+    _contig(out, "out")
+    _lse_check(lse_out, B, Hq, dev)
+    _check(lib.gqa_attn_decode(
+        _ptr(q), _dtype_code(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(window),
+        float(scale), _ptr(out), _dtype_code(out, "out"), _ptr(lse_out), B, Hq, Hkv, D, T,
+        _stream(dev)))
+    return out
+
+
+def attn_decode_splitk(q, k_cache, v_cache, lens, part_tokens: int, window: int = 0,
+                       scale: float = 0.0, workspace=None):
+    """Partition pass of the split-K decode; returns the workspace tensor."""
+    dev, B, Hq, Hkv, D, T = _attn_common(q, k_cache, v_cache, lens)
+    need = splitk_workspace_bytes(B, Hq, D, T, window, part_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", dev)
+    _contig(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gqa_attn_decode_splitk(
+        _ptr(q), _dtype_code(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(window),
+        float(scale), int(part_tokens), _ptr(workspace), nbytes, B, Hq, Hkv, D, T,
+        _stream(dev)))
+    return workspace
+
+
+def attn_decode_merge(workspace, B: int, Hq: int, D: int, T: int, part_tokens: int,
+                      window: int = 0, out=None, out_dtype=torch.float32, lse_out=None):
+    """Log-sum-exp merge of the partitions in ``workspace``; returns ``out``."""
+    dev = workspace.device
+    _dev(workspace, "workspace")
+    _contig(workspace, "workspace")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+    _dev(out, "out", dev)
+    _contig(out, "out")
+    _lse_check(lse_out, B, Hq, dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gqa_attn_decode_merge(
+        _ptr(workspace), nbytes, int(window), int(part_tokens), _ptr(out),
+        _dtype_code(out, "out"), _ptr(lse_out), B, Hq, D, T, _stream(dev)))
+    return out
+
+
+def workspace_views(workspace, B: int, Hq: int, D: int, T: int, window: int,
+                    part_tokens: int):
+    """(lse [B,Hq,NP], o [B,Hq,NP,D]) float32 views of a split-K workspace,
+    following the layout documented in the header."""
+    npart = num_partitions(T, window, part_tokens)
+    n_lse = B * Hq * npart
+    off = (n_lse * 4 + 255) // 256 * 256
+    flat = workspace.view(torch.uint8)
+    lse = flat[: n_lse * 4].view(torch.float32).view(B, Hq, npart)
+    o = flat[off: off + n_lse * D * 4].view(torch.float32).view(B, Hq, npart, D)
+    return lse, o

@@ -1,0 +1,179 @@
+// extern "C" entry points declared in include/gqa_decode.h: host-side
+// argument checks, then one launcher call.  Nothing is enqueued when a check
+// fails, and no entry point allocates, frees, synchronises or reads device
+// memory.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/gqa_decode.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxIndex = INT64_C(1) << 62;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool dtype_ok(gqa_dtype_t t) { return t == GQA_F32 || t == GQA_BF16; }
+
+bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+
+// Shared shape checks for [B,Hq,D] queries against a [B,Hkv,T,D] cache.
+int check_shapes(int B, int Hq, int Hkv, int D, int T) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || T < 1) return GQA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return GQA_ERR_SHAPE;
+  if ((int64_t)B * Hkv * T > kMaxIndex / D) return GQA_ERR_SHAPE;
+  if ((int64_t)B * Hq > INT32_MAX / 2) return GQA_ERR_SHAPE;
+  if (B > 65535 || Hkv > 65535) return GQA_ERR_SHAPE;   // grid y/z limits
+  if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+  if (!group_ok(Hq / Hkv)) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+int check_split(int T, int window, int part_tokens) {
+  if (part_tokens < 1) return GQA_ERR_VALUE;
+  if ((int64_t)T + part_tokens >= INT32_MAX) return GQA_ERR_SHAPE;
+  return GQA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+float softmax_qscale(float scale, int D) {
+  const double s = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)D);
+  return (float)(s * 1.4426950408889634);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_NULL: return "a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "a size is < 1, inconsistent, or too large";
+    case GQA_ERR_UNSUPPORTED: return "head dim, group size or dtype not supported";
+    case GQA_ERR_WORKSPACE: return "split-K workspace too small";
+    case GQA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case GQA_ERR_ALIGN: return "pointer not aligned as required";
+    case GQA_ERR_VALUE: return "scalar argument out of range";
+    default: return "unknown status";
+  }
+}
+
+int gqa_qkv_prologue(const void* q, const void* k_new, const void* v_new,
+                     gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                     const float* q_norm_w, const float* k_norm_w, float eps,
+                     double rope_theta, const int32_t* pos, float* q_out,
+                     uint16_t* k_cache, uint16_t* v_cache,
+                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  if (!q || !k_new || !v_new || !pos || !q_out || !k_cache || !v_cache) return GQA_ERR_NULL;
+  if ((q_norm_w == nullptr) != (k_norm_w == nullptr)) return GQA_ERR_NULL;
+  int rc = check_shapes(B, Hq, Hkv, D, T);
+  if (rc) return rc;
+  if (!dtype_ok(in_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (q_bstride < (int64_t)Hq * D || kv_bstride < (int64_t)Hkv * D) return GQA_ERR_SHAPE;
+  if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
+  if (isnan(rope_theta) || isinf(rope_theta)) return GQA_ERR_VALUE;
+  const uintptr_t ea = in_dtype == GQA_BF16 ? 2 : 4;
+  if (!aligned(q, ea) || !aligned(k_new, ea) || !aligned(v_new, ea) || !aligned(q_out, 4) ||
+      !aligned(k_cache, 2) || !aligned(v_cache, 2) || !aligned(pos, 4) ||
+      !aligned(q_norm_w, 4) || !aligned(k_norm_w, 4))
+    return GQA_ERR_ALIGN;
+  gqa::PrologueArgs a{q, k_new, v_new, in_dtype == GQA_BF16, q_bstride, kv_bstride,
+                      q_norm_w, k_norm_w, eps, rope_theta, pos, q_out, k_cache, v_cache,
+                      B, Hq, Hkv, D, T};
+  return gqa::launch_prologue(a, stream);
+}
+
+int gqa_attn_decode(const void* q, gqa_dtype_t q_dtype,
+                    const uint16_t* k_cache, const uint16_t* v_cache,
+                    const int32_t* lens, int window, float scale,
+                    void* out, gqa_dtype_t out_dtype, float* lse_out,
+                    int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !lens || !out) return GQA_ERR_NULL;
+  int rc = check_shapes(B, Hq, Hkv, D, T);
+  if (rc) return rc;
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(lens, 4) || !aligned(lse_out, 4))
+    return GQA_ERR_ALIGN;
+  gqa::AttnArgs a{};
+  a.q = q; a.q_bf16 = q_dtype == GQA_BF16;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens; a.window = window;
+  a.qscale = softmax_qscale(scale, D);
+  a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T; a.split = false;
+  return gqa::launch_attn(a, stream);
+}
+
+int gqa_num_partitions(int T, int window, int part_tokens) {
+  if (T < 1 || part_tokens < 1) return 0;
+  const int64_t span = window > 0 && window < T ? window : T;
+  return (int)((span + part_tokens - 1) / part_tokens);
+}
+
+static size_t lse_bytes(int B, int Hq, int np) { return (size_t)B * Hq * np * sizeof(float); }
+
+size_t gqa_splitk_workspace_bytes(int B, int Hq, int D, int T, int window, int part_tokens) {
+  if (B < 1 || Hq < 1 || D < 1 || T < 1 || part_tokens < 1) return 0;
+  const int np = gqa_num_partitions(T, window, part_tokens);
+  return align256(lse_bytes(B, Hq, np)) + (size_t)B * Hq * np * D * sizeof(float);
+}
+
+int gqa_attn_decode_splitk(const void* q, gqa_dtype_t q_dtype,
+                           const uint16_t* k_cache, const uint16_t* v_cache,
+                           const int32_t* lens, int window, float scale,
+                           int part_tokens, void* workspace, size_t workspace_bytes,
+                           int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !lens || !workspace) return GQA_ERR_NULL;
+  int rc = check_shapes(B, Hq, Hkv, D, T);
+  if (rc) return rc;
+  if ((rc = check_split(T, window, part_tokens))) return rc;
+  if (!dtype_ok(q_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(lens, 4) || !aligned(workspace, 256))
+    return GQA_ERR_ALIGN;
+  if (workspace_bytes < gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens))
+    return GQA_ERR_WORKSPACE;
+  const int np = gqa_num_partitions(T, window, part_tokens);
+  gqa::AttnArgs a{};
+  a.q = q; a.q_bf16 = q_dtype == GQA_BF16;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens; a.window = window;
+  a.qscale = softmax_qscale(scale, D);
+  a.part_tokens = part_tokens; a.num_parts = np;
+  a.ws_lse = static_cast<float*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    align256(lse_bytes(B, Hq, np)));
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T; a.split = true;
+  return gqa::launch_attn(a, stream);
+}
+
+int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
+                          int window, int part_tokens,
+                          void* out, gqa_dtype_t out_dtype, float* lse_out,
+                          int B, int Hq, int D, int T, hipStream_t stream) {
+  if (!workspace || !out) return GQA_ERR_NULL;
+  if (B < 1 || Hq < 1 || T < 1) return GQA_ERR_SHAPE;
+  if ((int64_t)B * Hq > INT32_MAX / 2) return GQA_ERR_SHAPE;
+  if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
+  int rc = check_split(T, window, part_tokens);
+  if (rc) return rc;
+  if (!dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (!aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse_out, 4)) return GQA_ERR_ALIGN;
+  if (workspace_bytes < gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens))
+    return GQA_ERR_WORKSPACE;
+  const int np = gqa_num_partitions(T, window, part_tokens);
+  gqa::MergeArgs a{};
+  a.ws_lse = static_cast<const float*>(workspace);
+  a.ws_o = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
+                                          align256(lse_bytes(B, Hq, np)));
+  a.num_parts = np; a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
+  a.B = B; a.Hq = Hq; a.D = D;
+  return gqa::launch_merge(a, stream);
+}
+
+}  // extern "C"

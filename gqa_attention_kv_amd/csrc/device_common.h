@@ -1,0 +1,72 @@
+// Device helpers shared by the gfx950 kernels: bf16 packing, DPP lane
+// exchange, and wave-level reductions.  Internal header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// bf16 bit pattern -> float32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two bf16 packed in one dword -> float32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight bf16 in a 16-byte vector -> eight float32, element order preserved.
+__device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// float32 -> bf16 bits, round to nearest, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// DPP lane exchange within a 16-lane row (gfx9 encodings).
+enum : int {
+  kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141, // lane i <- lane 7-i inside each 8-lane half row
+  kDppMirror = 0x140,     // lane i <- lane 15-i inside each 16-lane row
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16), result in every lane of
+// the group.  After the two quad steps each lane holds its quad's sum; the
+// half-row mirror pairs quad 0 with quad 1, the row mirror pairs the halves.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  if constexpr (N == 16) v += dpp<kDppMirror>(v);
+  return v;
+}
+
+// Sum over aligned groups of N lanes for any power of two N <= 64 (shuffles).
+template <int N>
+__device__ __forceinline__ float group_sum_shfl(float v) {
+#pragma unroll
+  for (int m = 1; m < N; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace gqa

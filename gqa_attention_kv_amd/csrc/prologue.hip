@@ -1,0 +1,115 @@
+// Fused decode prologue for gfx950: per-head QK-RMSNorm, NeoX RoPE at the
+// sequence's position, and the append of the new K/V row to the bf16 cache.
+//
+// Follows the cutileGPT README feature "fused QK-Norm + RoPE + KV-cache
+// writes", the RMSNorm formula of its "Why tiles" figure (x * w / sqrt(
+// mean(x^2) + eps)), and the fusedtok 1.0.1 README "Operators" row RoPE
+// (NeoX layout, kv-cache position offset).
+//
+// Mapping: one head vector (a query head or a KV head of one sequence) per
+// D/2 consecutive lanes; lane i owns the NeoX pair (i, i + D/2), so the
+// rotation is lane-local and only the sum of squares crosses lanes.  For
+// D = 128 that is one wave64 per head vector.  The rotary angle
+// pos * theta^(-2i/D) is formed and reduced in float64 (at pos ~ 1e5 a
+// float32 angle would be off by ~1e-2 rad); the rotation itself is float32.
+#include "device_common.h"
+#include "launch.h"
+#include "../../include/gqa_decode.h"
+
+namespace gqa {
+
+template <typename IT>
+__device__ __forceinline__ float load_elem(const IT* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(const float* p, int64_t i) {
+  return f32_to_bf16(p[i]);
+}
+__device__ __forceinline__ uint16_t to_bf16_bits(const uint16_t* p, int64_t i) { return p[i]; }
+
+template <int D, typename IT>
+__global__ __launch_bounds__(256) void qkv_prologue_kernel(
+    const IT* __restrict__ q, const IT* __restrict__ k_new, const IT* __restrict__ v_new,
+    int64_t q_bstride, int64_t kv_bstride, const float* __restrict__ wq,
+    const float* __restrict__ wk, float eps, double theta, const int32_t* __restrict__ pos,
+    float* __restrict__ q_out, uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+    int B, int Hq, int Hkv, int T) {
+  constexpr int HALF = D / 2;        // lanes per head vector
+  constexpr int VPB = 256 / HALF;    // head vectors per workgroup
+  const int H = Hq + Hkv;
+  const int vec = blockIdx.x * VPB + threadIdx.x / HALF;
+  const int i = threadIdx.x % HALF;
+  const bool live = vec < B * H;     // lanes past the end compute on vector 0, store nothing
+  const int v = live ? vec : 0;
+  const int b = v / H;
+  const int hh = v % H;
+  const bool is_q = hh < Hq;
+  const int g = hh - Hq;
+
+  const IT* src = is_q ? q + (int64_t)b * q_bstride + (int64_t)hh * D
+                       : k_new + (int64_t)b * kv_bstride + (int64_t)g * D;
+  float x0 = load_elem<IT>(src, i);
+  float x1 = load_elem<IT>(src, i + HALF);
+
+  const float* w = is_q ? wq : wk;
+  if (w != nullptr) {
+    float ss = x0 * x0 + x1 * x1;
+    ss = group_sum_shfl<HALF>(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+    x0 = x0 * r * w[i];
+    x1 = x1 * r * w[i + HALF];
+  }
+
+  const int p = pos[b];
+  if (theta > 0.0) {
+    const double inv_freq = pow(theta, -2.0 * (double)i / (double)D);
+    double sn, cs;
+    sincos((double)p * inv_freq, &sn, &cs);
+    const float c = (float)cs, s = (float)sn;
+    const float y0 = x0 * c - x1 * s;
+    const float y1 = x1 * c + x0 * s;
+    x0 = y0;
+    x1 = y1;
+  }
+  if (!live) return;
+
+  if (is_q) {
+    float* dst = q_out + ((int64_t)b * Hq + hh) * D;
+    dst[i] = x0;
+    dst[i + HALF] = x1;
+  } else if (p >= 0 && p < T) {
+    const int64_t row = (((int64_t)b * Hkv + g) * T + p) * D;
+    k_cache[row + i] = f32_to_bf16(x0);
+    k_cache[row + i + HALF] = f32_to_bf16(x1);
+    const IT* vs = v_new + (int64_t)b * kv_bstride + (int64_t)g * D;
+    v_cache[row + i] = to_bf16_bits(vs, i);
+    v_cache[row + i + HALF] = to_bf16_bits(vs, i + HALF);
+  }
+}
+
+template <int D, typename IT>
+static int launch_prologue_t(const PrologueArgs& a, hipStream_t s) {
+  constexpr int VPB = 256 / (D / 2);
+  const int64_t vecs = (int64_t)a.B * (a.Hq + a.Hkv);
+  const unsigned blocks = (unsigned)((vecs + VPB - 1) / VPB);
+  hipLaunchKernelGGL((qkv_prologue_kernel<D, IT>), dim3(blocks), dim3(256), 0, s,
+                     (const IT*)a.q, (const IT*)a.k_new, (const IT*)a.v_new, a.q_bstride,
+                     a.kv_bstride, a.q_norm_w, a.k_norm_w, a.eps, a.theta, a.pos, a.q_out,
+                     a.k_cache, a.v_cache, a.B, a.Hq, a.Hkv, a.T);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+}
+
+int launch_prologue(const PrologueArgs& a, hipStream_t s) {
+  if (a.D == 128) return a.in_bf16 ? launch_prologue_t<128, uint16_t>(a, s)
+                                   : launch_prologue_t<128, float>(a, s);
+  if (a.D == 64) return a.in_bf16 ? launch_prologue_t<64, uint16_t>(a, s)
+                                  : launch_prologue_t<64, float>(a, s);
+  return GQA_ERR_UNSUPPORTED;
+}
+
+}  // namespace gqa

@@ -1,0 +1,123 @@
+"""Device-resident decode step: upload a workload once, then enqueue
+prologue -> attention (unsplit, or split-K partitions + merge) on torch's
+current stream as often as needed.
+
+Only plumbing lives here (uploads, buffer allocation, the order of the C-ABI
+calls); every arithmetic step runs in the HIP kernels.  The prologue's append
+is idempotent (same row, same bytes), so ``run()`` can be repeated.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import attn_decode, attn_decode_merge, attn_decode_splitk, qkv_prologue
+from . import splitk_workspace_bytes
+
+BF16_NAN = 0x7FC0
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bit patterns (host) -> torch.bfloat16 tensor on ``device``."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """torch.bfloat16 tensor -> uint16 bit patterns on the host."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DeviceStep:
+    """One decode step of workload ``w`` with all inputs resident in HBM.
+
+    ``split``: use split-K partitions of ``part_tokens`` rows plus the merge
+    (default: the workload's own partition size); otherwise the unsplit
+    kernel.  ``q_dtype`` selects the dtype attention reads q in when the
+    workload has no prologue.  ``poison`` writes bf16 NaN into every cache
+    row outside each sequence's attended range [lo, n) (rows the step must
+    never read); rows written by the prologue are left alone.
+    """
+
+    def __init__(self, w, device="cuda", split: bool = True,
+                 part_tokens: Optional[int] = None, out_dtype: Optional[str] = None,
+                 q_dtype: str = "bf16", poison: bool = False, scale: float = 0.0):
+        self.w = w
+        self.dev = torch.device(device)
+        self.split = split
+        self.part_tokens = int(part_tokens or w.part_tokens)
+        self.scale = float(scale)
+        od = out_dtype or w.out_dtype
+        self.out_dtype = torch.bfloat16 if od == "bf16" else torch.float32
+        kc, vc = w.k_cache, w.v_cache
+        if poison:
+            kc, vc = kc.copy(), vc.copy()
+            n = np.clip(w.lens.astype(np.int64), 0, w.T)
+            for b in range(w.B):
+                lo = max(0, int(n[b]) - w.window) if w.window > 0 else 0
+                keep = np.zeros(w.T, bool)
+                keep[lo:int(n[b])] = True
+                if w.pos is not None and 0 <= int(w.pos[b]) < w.T:
+                    keep[int(w.pos[b])] = True
+                kc[b][:, ~keep] = BF16_NAN
+                vc[b][:, ~keep] = BF16_NAN
+        d = self.dev
+        self.k_cache = bf16_tensor(kc, d)
+        self.v_cache = bf16_tensor(vc, d)
+        self.lens = torch.from_numpy(w.lens.astype(np.int32)).to(d)
+        if w.pos is not None:
+            self.q_in = bf16_tensor(w.q, d)
+            self.k_new = bf16_tensor(w.k_new, d)
+            self.v_new = bf16_tensor(w.v_new, d)
+            self.pos = torch.from_numpy(w.pos.astype(np.int32)).to(d)
+            self.w_q = None if w.w_q is None else torch.from_numpy(w.w_q).to(d)
+            self.w_k = None if w.w_k is None else torch.from_numpy(w.w_k).to(d)
+            self.q = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=d)
+        else:
+            qb = bf16_tensor(w.q, d)
+            self.q = qb if q_dtype == "bf16" else qb.float()
+        self.out = torch.empty((w.B, w.Hq, w.D), dtype=self.out_dtype, device=d)
+        self.lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=d)
+        self.ws = None
+        if split:
+            nb = splitk_workspace_bytes(w.B, w.Hq, w.D, w.T, w.window, self.part_tokens)
+            self.ws = torch.empty(nb, dtype=torch.uint8, device=d)
+
+    # -- the three stages, each one C-ABI call ------------------------------
+    def prologue(self):
+        w = self.w
+        if w.pos is None:
+            return
+        qkv_prologue(self.q_in, self.k_new, self.v_new, self.pos, self.k_cache, self.v_cache,
+                     q_norm_w=self.w_q, k_norm_w=self.w_k, eps=w.eps,
+                     rope_theta=w.theta, q_out=self.q)
+
+    def attention(self):
+        w = self.w
+        if self.split:
+            attn_decode_splitk(self.q, self.k_cache, self.v_cache, self.lens, self.part_tokens,
+                               window=w.window, scale=self.scale, workspace=self.ws)
+        else:
+            attn_decode(self.q, self.k_cache, self.v_cache, self.lens, window=w.window,
+                        scale=self.scale, out=self.out, lse_out=self.lse)
+
+    def merge(self):
+        if not self.split:
+            return
+        w = self.w
+        attn_decode_merge(self.ws, w.B, w.Hq, w.D, w.T, self.part_tokens, window=w.window,
+                          out=self.out, lse_out=self.lse)
+
+    def run(self):
+        self.prologue()
+        self.attention()
+        self.merge()
+
+    def results(self) -> dict:
+        torch.cuda.synchronize(self.dev)
+        out = self.out.float().cpu().numpy().astype(np.float64)
+        return dict(out=out, lse=self.lse.cpu().numpy().astype(np.float64),
+                    q=self.q.float().cpu().numpy().astype(np.float64),
+                    k_cache=bf16_bits(self.k_cache), v_cache=bf16_bits(self.v_cache))

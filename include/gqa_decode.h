@@ -1,0 +1,173 @@
+/*
+ * gqa_decode.h -- C ABI of an MI355X (gfx950) library for single-token
+ * grouped-query-attention decode over a bf16 KV cache.
+ *
+ * The operations are the ones two pages describe:
+ *   - fusedtok 1.0.1 README, "Operators" table, row attention_decode:
+ *     single-token causal attention with GQA over a contiguous KV cache,
+ *     online softmax, flash-decoding split over long caches, per-sequence
+ *     lengths; "Usage": attention_decode(q_heads [B,Hq,D],
+ *     k_cache/v_cache [B,Hkv,T,D], lens int32 [B]), rope(..., pos_offset,
+ *     neox=True), rmsnorm(x, w, eps); zero-copy device buffers, stream
+ *     ordered, no host synchronisation; bf16 tensors computed in float32
+ *     and converted at load and store.
+ *   - cutileGPT README, feature list: fused QK-Norm + RoPE + KV-cache
+ *     writes; MHA/GQA and sliding-window attention; "Why tiles" figure:
+ *     RMSNorm rstd = 1/sqrt(sum(x*x)/N + eps), y = x*rstd*w.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer, except where noted.  The
+ *     caller allocates and frees every buffer, including the split-K
+ *     workspace.  The library never allocates, frees, synchronises, or reads
+ *     device memory from the host; each call only enqueues kernels on
+ *     `stream` (0 = the null stream), so calls are asynchronous and may be
+ *     captured in a HIP graph.
+ *   - bf16 values are passed as their uint16 bit patterns.  Arithmetic is
+ *     float32; bf16 stores round to nearest, ties to even.
+ *   - Layouts are dense and row-major: q [B,Hq,D], caches [B,Hkv,T,D]
+ *     (element (b,g,t,d) at ((b*Hkv+g)*T+t)*D+d), outputs [B,Hq,D],
+ *     lse [B,Hq].  Query head h uses KV head h / (Hq/Hkv).
+ *   - Outputs must not alias inputs.
+ *   - Supported: D in {64, 128}; G = Hq/Hkv in {1, 2, 4, 8, 16}.
+ *   - Errors: arguments are checked on the host before anything is
+ *     enqueued; on error the call returns a negative status and enqueues
+ *     nothing.  A launch failure reported by HIP returns GQA_ERR_LAUNCH.
+ *   - Device values outside the contract are handled safely, not trapped:
+ *     lens[b] is clamped to [0, T]; a sequence with no attended rows
+ *     produces out = 0 and lse = -inf; a pos[b] outside [0, T) still
+ *     produces q_out but writes nothing to the cache.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype_t;
+
+enum {
+  GQA_OK = 0,
+  GQA_ERR_NULL = -1,        /* a required pointer is NULL                  */
+  GQA_ERR_SHAPE = -2,       /* a size is < 1, inconsistent, or overflows   */
+  GQA_ERR_UNSUPPORTED = -3, /* head dim, group size or dtype not built     */
+  GQA_ERR_WORKSPACE = -4,   /* split-K workspace too small                 */
+  GQA_ERR_LAUNCH = -5,      /* HIP reported an error for the launch        */
+  GQA_ERR_ALIGN = -6,       /* a pointer lacks the required alignment      */
+  GQA_ERR_VALUE = -7        /* a scalar argument is out of its range       */
+};
+
+/*
+ * Fused prologue for one decode step (cutileGPT: fused QK-Norm + RoPE +
+ * KV-cache writes; fusedtok: RMSNorm, RoPE NeoX layout with a position
+ * offset).  For every sequence b:
+ *   each query head:  q_out[b,h,:] = RoPE_pos[b]( RMSNorm(q[b,h,:], q_norm_w) )
+ *   each KV head g:   k_cache[b,g,pos[b],:] = bf16( RoPE_pos[b]( RMSNorm(k_new[b,g,:], k_norm_w) ) )
+ *                     v_cache[b,g,pos[b],:] = bf16( v_new[b,g,:] )
+ * RMSNorm: y = x * w / sqrt(mean(x^2) + eps).  RoPE (NeoX, rotate-half):
+ * element i < D/2 pairs with i + D/2 and both rotate by pos * theta^(-2i/D);
+ * angles are formed and reduced in float64.
+ *
+ *   q, k_new, v_new  [B,Hq,D] / [B,Hkv,D] / [B,Hkv,D] in `in_dtype`
+ *                    (GQA_F32 or GQA_BF16).  Heads are contiguous inside a
+ *                    batch row; consecutive batch rows are `q_bstride` /
+ *                    `kv_bstride` elements apart (>= Hq*D / Hkv*D), so one
+ *                    packed QKV projection output can be passed directly.
+ *   q_norm_w, k_norm_w  float32 [D] each, or both NULL for no QK-norm.
+ *   eps              >= 0, added to the mean of squares.
+ *   rope_theta       base of the rotary schedule; <= 0 disables RoPE.
+ *   pos              int32 [B]: RoPE position of the new token, which is
+ *                    also the cache row it is written to.
+ *   q_out            float32 [B,Hq,D] (dense), the rotated queries.
+ *   k_cache, v_cache bf16 [B,Hkv,T,D]; only rows pos[b] are written.
+ */
+int gqa_qkv_prologue(const void* q, const void* k_new, const void* v_new,
+                     gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                     const float* q_norm_w, const float* k_norm_w, float eps,
+                     double rope_theta, const int32_t* pos, float* q_out,
+                     uint16_t* k_cache, uint16_t* v_cache,
+                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
+/*
+ * Single-token GQA decode attention, one pass over the cache per KV head
+ * (fusedtok attention_decode; cutileGPT sliding-window attention).
+ * For sequence b let n = clamp(lens[b], 0, T) and lo = max(0, n - window)
+ * when window > 0, else 0.  For every query head h (KV head g = h/(Hq/Hkv)):
+ *   s_j = scale * <q[b,h,:], K[b,g,j,:]>   for j in [lo, n)
+ *   out[b,h,:] = sum_j softmax(s)_j V[b,g,j,:];  lse[b,h] = log sum_j exp(s_j)
+ *
+ *   q        [B,Hq,D] in q_dtype (GQA_F32 or GQA_BF16), 16-byte aligned.
+ *   k_cache, v_cache  bf16 [B,Hkv,T,D], 16-byte aligned.
+ *   lens     int32 [B]: rows [0, lens[b]) are valid.
+ *   window   <= 0: attend to all valid rows; > 0: only the last `window`.
+ *   scale    softmax scale; <= 0 selects 1/sqrt(D).
+ *   out      [B,Hq,D] in out_dtype (GQA_F32 or GQA_BF16), 16-byte aligned.
+ *   lse_out  float32 [B,Hq] natural-log log-sum-exp of the scores, or NULL.
+ * One workgroup per (sequence, KV head) streams the rows; for long caches
+ * use the split-K pair below.
+ */
+int gqa_attn_decode(const void* q, gqa_dtype_t q_dtype,
+                    const uint16_t* k_cache, const uint16_t* v_cache,
+                    const int32_t* lens, int window, float scale,
+                    void* out, gqa_dtype_t out_dtype, float* lse_out,
+                    int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
+/*
+ * Flash-decoding split (fusedtok attention_decode: "flash-decoding split
+ * over long caches").  The attended rows [lo, n) of each (sequence, KV head)
+ * are cut into partitions J_k = [lo + k*P, min(lo + (k+1)*P, n)),
+ * k < num_parts, P = part_tokens.  num_parts depends on host-known sizes
+ * only: ceil(min(T, window > 0 ? window : T) / P).
+ */
+int gqa_num_partitions(int T, int window, int part_tokens);
+
+/*
+ * Bytes of workspace gqa_attn_decode_splitk needs (0 for invalid sizes).
+ * Layout, with NP = num_parts:
+ *   offset 0:                 lse_k float32 [B,Hq,NP]   natural-log LSE of
+ *                             partition k, -inf for an empty partition
+ *   offset align256(4*B*Hq*NP): o_k float32 [B,Hq,NP,D] softmax-normalised
+ *                             partition output (undefined where lse_k=-inf)
+ */
+size_t gqa_splitk_workspace_bytes(int B, int Hq, int D, int T, int window,
+                                  int part_tokens);
+
+/*
+ * Partition pass: one workgroup per (partition, KV head, sequence) writes
+ * (o_k, lse_k) for the G query heads of its KV head into `workspace`
+ * (256-byte aligned, at least gqa_splitk_workspace_bytes bytes).  Every
+ * partition slot is written, empty ones with lse_k = -inf.  Other
+ * arguments as for gqa_attn_decode.
+ */
+int gqa_attn_decode_splitk(const void* q, gqa_dtype_t q_dtype,
+                           const uint16_t* k_cache, const uint16_t* v_cache,
+                           const int32_t* lens, int window, float scale,
+                           int part_tokens, void* workspace, size_t workspace_bytes,
+                           int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of the partitions written by gqa_attn_decode_splitk
+ * with the same (B, Hq, D, T, window, part_tokens):
+ *   M = max_k lse_k;  w_k = exp(lse_k - M);
+ *   out = sum_k w_k o_k / sum_k w_k;  lse = M + log sum_k w_k
+ * in ascending k, so results are bit-identical run to run.  All partitions
+ * empty: out = 0, lse = -inf.
+ */
+int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
+                          int window, int part_tokens,
+                          void* out, gqa_dtype_t out_dtype, float* lse_out,
+                          int B, int Hq, int D, int T, hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char* gqa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

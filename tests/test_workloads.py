@@ -14,13 +14,16 @@ def test_same_seed_same_bytes():
     assert not np.array_equal(a.k_cache, c.k_cache)
 
 
-def test_chunked_draws_equal_one_shot(monkeypatch):
-    full = W.make("2a", L=100)
+def test_cache_draws_independent_of_thread_count(monkeypatch):
     monkeypatch.setattr(W, "_CHUNK", 1000)
-    chunked = W.make("2a", L=100)
-    assert np.array_equal(full.k_cache, chunked.k_cache)
-    assert np.array_equal(full.v_cache, chunked.v_cache)
-    assert np.array_equal(full.w_k, chunked.w_k)
+    monkeypatch.setattr(W, "_THREADS", 1)
+    one = W.make("2a", L=100)
+    monkeypatch.setattr(W, "_THREADS", 7)
+    many = W.make("2a", L=100)
+    assert np.array_equal(one.k_cache, many.k_cache)
+    assert np.array_equal(one.v_cache, many.v_cache)
+    assert not np.array_equal(one.k_cache, one.v_cache)
+    assert np.array_equal(one.w_k, many.w_k)
 
 
 def test_bf16_rounding_of_draws_matches_torch():

@@ -13,16 +13,21 @@ ragged lengths, a 128K-token long-context split-K case with a peaky
 softmax, and a 70B-shaped sliding-window case.  Every array is produced
 from ``numpy.random.default_rng(seed)`` (PCG64) in a fixed draw order:
 
-    lens (ragged configs only), q, k_new, v_new, K cache, V cache,
+    lens (ragged configs only), q, k_new, v_new,
     w_q, w_k (QK-norm configs only), peaky row indices (peaky configs only)
 
 Normal draws are float32 ``standard_normal`` rounded to bf16 with
-round-to-nearest-even; caches are generated in chunks so that the host
-never holds a float32 copy of a whole cache.
+round-to-nearest-even.  The two caches are the exception to the single
+stream: each fixed chunk of 2**24 elements of a cache is drawn from its own
+PCG64 stream seeded with (seed, cache tag, chunk index), so chunks can be
+filled by parallel threads with results independent of the thread count,
+and the host never holds a float32 copy of a whole cache.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
 from typing import Dict, Optional
 
 import numpy as np
@@ -36,20 +41,45 @@ _CHUNK = 1 << 24
 def fp32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 samples to bf16 (nearest, ties to even); return uint16 bits.
 
-    Used only to turn freshly drawn finite float32 samples into bf16 inputs.
+    Used only to turn freshly drawn finite float32 samples into bf16 inputs
+    (finite inputs never overflow the 32-bit sum below).
     """
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) bf16 draws from the workload's main stream."""
+    return fp32_to_bf16_bits(rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
+                             ).reshape(shape)
+
+
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                      else (os.cpu_count() or 1)))
+
+
+def _cache_bf16(seed: int, tag: int, shape) -> np.ndarray:
+    """N(0,1) bf16 cache contents; chunk j comes from PCG64(SeedSequence((seed, tag, j)))."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, _CHUNK):
+
+    def fill(j):
+        s = j * _CHUNK
         e = min(n, s + _CHUNK)
-        out[s:e] = fp32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence((seed, tag, j))))
+        out[s:e] = fp32_to_bf16_bits(g.standard_normal(e - s, dtype=np.float32))
+
+    chunks = range(-(-n // _CHUNK))
+    if _THREADS > 1 and len(chunks) > 1:
+        with cf.ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, chunks))
+    else:
+        for j in chunks:
+            fill(j)
     return out.reshape(shape)
 
 
@@ -178,8 +208,8 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
         v_new = _normal_bf16(rng, (B, Hkv, D))
     else:
         k_new = v_new = None
-    k_cache = _normal_bf16(rng, (B, Hkv, T, D))
-    v_cache = _normal_bf16(rng, (B, Hkv, T, D))
+    k_cache = _cache_bf16(seed, 1, (B, Hkv, T, D))
+    v_cache = _cache_bf16(seed, 2, (B, Hkv, T, D))
     if p["norm"]:
         w_q = (1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)).astype(np.float32)
         w_k = (1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)).astype(np.float32)
