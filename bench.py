@@ -3,9 +3,9 @@
 One step = one pass of the whole decode hot path over one batch: the fused
 prologue (QK-RMSNorm + NeoX RoPE + K/V append), the split-K attention pass,
 and the log-sum-exp merge, each one C-ABI call on torch's current stream,
-with every input already resident in HBM.  Before each timed step, a 1 GiB
-read-modify-write sweeps the L2s and the Infinity Cache so the KV window is
-read from HBM (outside the timed region).
+with every input already resident in HBM.  Before each timed step, a
+read-only sweep of a 1 GiB buffer evicts the KV window from the L2s and the
+256 MB Infinity Cache so it is read from HBM (outside the timed region).
 
 Prints ONE JSON line.  ``value`` is the step's KV-read throughput: KV-cache
 bytes the step must read (K and V rows of every attended window, bf16) per
@@ -52,13 +52,16 @@ def _parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="5", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--no-flush", action="store_true",
-                    help="skip the cache sweep between steps (warm-cache figure)")
+    ap.add_argument("--flush", default="read", choices=["read", "rmw", "none"],
+                    help="cache sweep between steps: read a 1 GiB buffer (default), "
+                         "read-modify-write it, or none (warm-cache figure)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also time a plain device copy of this many MiB")
+    ap.add_argument("--part-tokens", type=int, default=0,
+                    help="override the workload's split-K partition size")
     return ap.parse_args()
 
 
@@ -126,13 +129,24 @@ def main():
     torch.cuda.set_device(dev)
 
     w = workloads.make(args.workload)
+    if args.part_tokens:
+        w.part_tokens = args.part_tokens
     kvb = workloads.kv_bytes(w)
     step = DeviceStep(w, device=dev, split=True)
-    flush = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+    flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
+                                                          device=dev)
+    flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def sweep():
+        # A read-only sweep leaves the caches full of clean lines, so the timed
+        # kernels pay no write-back of somebody else's dirty data.
+        if args.flush == "read":
+            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink)
+        elif args.flush == "rmw":
+            flush.add_(1)
 
     def one_step(evs=None):
-        if flush is not None:
-            flush.add_(1)
+        sweep()
         if evs is not None:
             evs[0].record()
         step.prologue()
@@ -177,8 +191,7 @@ def main():
         dst = torch.empty_like(src)
         ts = []
         for _ in range(5):
-            if flush is not None:
-                flush.add_(1)
+            sweep()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             dst.copy_(src)
@@ -213,7 +226,7 @@ def main():
             "prologue": ("qk_rmsnorm+rope+append" if w.w_q is not None else
                          "rope+append") if w.pos is not None else "none",
             "kv_bytes_per_step": kvb,
-            "cache_flush_between_steps": flush is not None,
+            "cache_sweep_between_steps": args.flush,
             "parallelism": "single GPU",
         },
         "roofline": {

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["api.cpp", "prologue.hip", "attn_decode.hip", "merge.hip"]
+SOURCES = ["api.cpp", "prologue.hip", "attn_decode.hip", "attn_decode_mfma.hip", "merge.hip"]
 ARCH = "gfx950"
 
 
@@ -31,7 +31,7 @@ def _hipcc() -> str:
 
 
 def _flags():
-    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    return ["-O3", *os.environ.get("GQA_EXTRA_CFLAGS", "").split(), "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 

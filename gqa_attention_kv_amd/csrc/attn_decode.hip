@@ -282,7 +282,7 @@ static int dispatch_g(const AttnArgs& a, hipStream_t s) {
   }
 }
 
-int launch_attn(const AttnArgs& a, hipStream_t s) {
+int launch_attn_valu(const AttnArgs& a, hipStream_t s) {
   if (a.D == 128) return a.q_bf16 ? dispatch_g<128, uint16_t>(a, s) : dispatch_g<128, float>(a, s);
   if (a.D == 64) return a.q_bf16 ? dispatch_g<64, uint16_t>(a, s) : dispatch_g<64, float>(a, s);
   return GQA_ERR_UNSUPPORTED;

@@ -55,7 +55,17 @@ struct MergeArgs {
 };
 
 int launch_prologue(const PrologueArgs& a, hipStream_t s);
-int launch_attn(const AttnArgs& a, hipStream_t s);
+int launch_attn_valu(const AttnArgs& a, hipStream_t s);   // VALU dot products
+int launch_attn_mfma(const AttnArgs& a, hipStream_t s);   // matrix-core dot products
 int launch_merge(const MergeArgs& a, hipStream_t s);
+
+// The attention pass used by the C ABI.
+inline int launch_attn(const AttnArgs& a, hipStream_t s) {
+#ifdef GQA_ATTN_VALU
+  return launch_attn_valu(a, s);
+#else
+  return launch_attn_mfma(a, s);
+#endif
+}
 
 }  // namespace gqa

@@ -154,14 +154,14 @@ CONFIGS: Dict[str, dict] = {
     # Llama-3-8B-shaped batch, ragged lens ~ U{128..4096}, bf16 output
     "3": dict(seed=3, B=32, Hq=32, Hkv=8, D=128, L=4096, layout="ragged",
               lmin=128, window=0, theta=5e5, norm=False, out_dtype="bf16",
-              part_tokens=512),
+              part_tokens=1024),
     # long context, no prologue, q given in bf16, 1% of K rows x4, P=2048
     "4": dict(seed=4, B=1, Hq=32, Hkv=8, D=128, L=131072, layout="noprologue",
               window=0, theta=0.0, norm=False, out_dtype="f32", part_tokens=2048,
               peaky=0.01),
     # 70B-shaped sliding window: B8 Hq64 Hkv8 L32768, W=4096
     "5": dict(seed=5, B=8, Hq=64, Hkv=8, D=128, L=32768, layout="last",
-              window=4096, theta=5e5, norm=True, out_dtype="f32", part_tokens=512),
+              window=4096, theta=5e5, norm=True, out_dtype="f32", part_tokens=1024),
 }
 
 
