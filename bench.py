@@ -21,7 +21,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import statistics
 import sys
@@ -34,7 +33,8 @@ if ROOT not in sys.path:
 METRIC = ("decode-attention µs/step and achieved KV-read HBM GB/s "
           "(% of MI355X peak)")
 HBM_PEAK_GBS = 8000.0
-ATTN_SRC = os.path.join(ROOT, "gqa_attention_kv_amd", "csrc", "attn_decode.hip")
+ATTN_SRC = os.path.join(ROOT, "gqa_attention_kv_amd", "csrc", "attn_decode_mfma.hip")
+ATTN_KERNEL = "attn_decode_mfma_kernel"
 
 WORKLOAD_NAMES = {
     "1": "tiny GQA decode step",
@@ -62,6 +62,13 @@ def _parse():
                     help="also time a plain device copy of this many MiB")
     ap.add_argument("--part-tokens", type=int, default=0,
                     help="override the workload's split-K partition size")
+    ap.add_argument("--mode", default="fused", choices=["fused", "split"],
+                    help="fused: the whole step as one launch (default); split: "
+                         "prologue, split-K pass and merge as three launches")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: turn two rocprofv3 --pmc output directories "
+                         "(FETCH_SIZE, WRITE_SIZE; each from a bench run with "
+                         "--copy-probe-mib) into profiles/attn_traffic_workload<W>.json")
     return ap.parse_args()
 
 
@@ -81,6 +88,53 @@ def _traffic(workload: str):
     if rec.get("attn_src_sha") != _src_sha(ATTN_SRC):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _pmc_rows(d: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_launch(rows, counter):
+    """(mean KiB per attention dispatch, calibration factor from the copy
+    probe: true bytes / counted bytes for a 256 MiB device copy)."""
+    rows = [r for r in rows if r["Counter_Name"] == counter]
+    attn = [float(r["Counter_Value"]) for r in rows if ATTN_KERNEL in r["Kernel_Name"]]
+    last_attn = max(int(r["Dispatch_Id"]) for r in rows if ATTN_KERNEL in r["Kernel_Name"])
+    copies = [float(r["Counter_Value"]) for r in rows
+              if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last_attn]
+    # the probe's 256 MiB copies are the largest copy dispatches after the timed loop
+    copies = [c for c in copies if copies and c >= 0.5 * max(copies)]
+    if not attn or not copies:
+        raise SystemExit(f"{counter}: attention or copy-probe dispatches missing")
+    probe_kib = 256 * 1024     # the copy probe reads 256 MiB and writes 256 MiB
+    factor = probe_kib / statistics.median(copies)
+    return statistics.fmean(attn), factor
+
+
+def _record_traffic(workload: str, fetch_dir: str, write_dir: str):
+    f_kib, f_fac = _per_launch(_pmc_rows(fetch_dir), "FETCH_SIZE")
+    w_kib, w_fac = _per_launch(_pmc_rows(write_dir), "WRITE_SIZE")
+    rec = {
+        "workload": workload,
+        "kernel": ATTN_KERNEL,
+        "attn_src_sha": _src_sha(ATTN_SRC),
+        "fetch_kib_counted": round(f_kib, 1), "fetch_calibration": round(f_fac, 4),
+        "write_kib_counted": round(w_kib, 1), "write_calibration": round(w_fac, 4),
+        "bytes_per_launch": int(round((f_kib * f_fac + w_kib * w_fac) * 1024)),
+        "read_bytes_per_launch": int(round(f_kib * f_fac * 1024)),
+        "write_bytes_per_launch": int(round(w_kib * w_fac * 1024)),
+    }
+    out = os.path.join(ROOT, "profiles", f"attn_traffic_workload{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def _cpu_baseline(w, min_seconds: float):
@@ -112,6 +166,9 @@ def _cpu_baseline(w, min_seconds: float):
 
 def main():
     args = _parse()
+    if args.record_traffic:
+        _record_traffic(args.workload, *args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -132,7 +189,8 @@ def main():
     if args.part_tokens:
         w.part_tokens = args.part_tokens
     kvb = workloads.kv_bytes(w)
-    step = DeviceStep(w, device=dev, split=True)
+    mode = args.mode
+    step = DeviceStep(w, device=dev, mode=mode)
     flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
                                                           device=dev)
     flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
@@ -149,6 +207,11 @@ def main():
         sweep()
         if evs is not None:
             evs[0].record()
+        if mode == "fused":      # one launch: bracket it with one event pair only
+            step.fused()
+            if evs is not None:
+                evs[3].record()
+            return
         step.prologue()
         if evs is not None:
             evs[1].record()
@@ -173,16 +236,19 @@ def main():
     wall = time.perf_counter() - wall0
 
     step_ms = [e[0].elapsed_time(e[3]) for e in evs]
-    pro_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    if mode == "fused":      # one kernel: the step is the dominant kernel
+        pro_ms = merge_ms = [0.0]
+        attn_ms = step_ms
+    else:
+        pro_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+        merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
     mean_step = statistics.fmean(step_ms)
     mean_attn = statistics.fmean(attn_ms)
     value = kvb / (mean_step * 1e-3) / 1e9
     achieved = kvb / (mean_attn * 1e-3) / 1e9
 
-    res = step.results()
-    finite = bool(all(math.isfinite(x) for x in res["out"].reshape(-1)[:4096]))
+    finite = bool(torch.isfinite(step.out.float()).all().item())
 
     copy_probe = None
     if args.copy_probe_mib:
@@ -223,6 +289,7 @@ def main():
             "workload": WORKLOAD_NAMES[args.workload],
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D, "T": w.T,
             "window": w.window, "part_tokens": w.part_tokens, "out_dtype": w.out_dtype,
+            "path": mode,
             "prologue": ("qk_rmsnorm+rope+append" if w.w_q is not None else
                          "rope+append") if w.pos is not None else "none",
             "kv_bytes_per_step": kvb,
@@ -231,7 +298,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_decode_kernel (split-K partition pass)",
+            "kernel": ATTN_KERNEL + (" (whole fused step)" if mode == "fused"
+                                     else " (split-K partition pass)"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -239,8 +307,9 @@ def main():
             "traffic": traffic,
         },
         "kernels_us": {
+            "mode": mode,
             "prologue": round(1e3 * statistics.fmean(pro_ms), 2),
-            "attn_splitk": round(1e3 * mean_attn, 2),
+            "attn": round(1e3 * mean_attn, 2),
             "merge": round(1e3 * statistics.fmean(merge_ms), 2),
             "step_p10": round(1e3 * sorted(step_ms)[len(step_ms) // 10], 2),
             "step_p90": round(1e3 * sorted(step_ms)[(9 * len(step_ms)) // 10], 2),

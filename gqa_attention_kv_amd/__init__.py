@@ -8,7 +8,8 @@ there is no fallback.  Importing fails loudly when the library is missing.
 
 Functions follow the C entry points' names without the ``gqa_`` prefix:
 ``qkv_prologue``, ``attn_decode``, ``attn_decode_splitk``,
-``attn_decode_merge``, ``splitk_workspace_bytes``, ``num_partitions``.
+``attn_decode_merge``, ``decode_step``, ``splitk_workspace_bytes``,
+``decode_step_workspace_bytes``, ``num_partitions``.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ from ._build import LIB_PATH
 __all__ = [
     "GQAError", "lib", "qkv_prologue", "attn_decode", "attn_decode_splitk",
     "attn_decode_merge", "splitk_workspace_bytes", "num_partitions",
-    "F32", "BF16", "SYMBOLS",
+    "decode_step", "decode_step_workspace_bytes", "F32", "BF16", "SYMBOLS",
 ]
 
 F32, BF16 = 0, 1
@@ -52,6 +53,9 @@ SYMBOLS = {
     "gqa_attn_decode_splitk": (_i, [_p, _i, _p, _p, _p, _i, _f, _i, _p, _sz,
                                     _i, _i, _i, _i, _i, _p]),
     "gqa_attn_decode_merge": (_i, [_p, _sz, _i, _i, _p, _i, _p, _i, _i, _i, _i, _p]),
+    "gqa_decode_step_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "gqa_decode_step": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _d, _p, _p, _p, _p,
+                             _i, _f, _i, _p, _sz, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
     "gqa_status_string": (ctypes.c_char_p, [_i]),
 }
 for _name, (_res, _args) in SYMBOLS.items():
@@ -245,3 +249,79 @@ def workspace_views(workspace, B: int, Hq: int, D: int, T: int, window: int,
     lse = flat[: n_lse * 4].view(torch.float32).view(B, Hq, npart)
     o = flat[off: off + n_lse * D * 4].view(torch.float32).view(B, Hq, npart, D)
     return lse, o
+
+
+def decode_step_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, T: int, window: int,
+                                part_tokens: int) -> int:
+    return int(lib.gqa_decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens))
+
+
+def decode_step(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens: int,
+                workspace=None, q_norm_w=None, k_norm_w=None, eps: float = 1e-6,
+                rope_theta: float = 0.0, window: int = 0, scale: float = 0.0, out=None,
+                out_dtype=torch.float32, lse_out=None, q_out=None):
+    """Whole decode step in one launch: prologue + split-K attention + merge.
+
+    Inputs as for ``qkv_prologue`` plus ``lens``; ``workspace`` is a uint8
+    device tensor whose arrival tickets start at zero (allocated zeroed when
+    None; reuse it across calls).  Returns ``(out, workspace)``.
+    """
+    dev = k_cache.device
+    pro = pos is not None
+    if (k_new is None) == pro or (v_new is None) == pro:
+        raise ValueError("pos, k_new and v_new come together (or all None: no prologue)")
+    for t, w in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (lens, "lens")):
+        _dev(t, w, dev)
+    B, Hq, D = q.shape
+    _, Hkv, T, _ = k_cache.shape
+    code = _dtype_code(q, "q")
+    news = ((k_new, "k_new", Hkv), (v_new, "v_new", Hkv)) if pro else ()
+    for t, w, h in ((q, "q", Hq),) + news:
+        _dev(t, w, dev)
+        if t.dtype != q.dtype:
+            raise TypeError("q, k_new and v_new must share a dtype")
+        if tuple(t.shape) != (B, h, D) or t.stride(2) != 1 or t.stride(1) != D:
+            raise ValueError(f"{w}: expected [B,{h},D] with contiguous heads")
+    if pro and k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must share a batch stride")
+    for t, w in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (B, Hkv, T, D):
+            raise ValueError(f"{w}: expected bfloat16 [B,Hkv,T,D]")
+        _contig(t, w)
+    for t, w in ((pos, "pos"), (lens, "lens")):
+        if t is None:
+            continue
+        _dev(t, w, dev)
+        if t.dtype != torch.int32 or tuple(t.shape) != (B,):
+            raise ValueError(f"{w} must be int32 [B]")
+        _contig(t, w)
+    for w, nm in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _dev(w, nm, dev)
+            if w.dtype != torch.float32 or tuple(w.shape) != (D,):
+                raise ValueError(f"{nm} must be float32 [D]")
+            _contig(w, nm)
+    need = decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", dev)
+    _contig(workspace, "workspace")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+    _dev(out, "out", dev)
+    _contig(out, "out")
+    _lse_check(lse_out, B, Hq, dev)
+    if q_out is not None:
+        _dev(q_out, "q_out", dev)
+        _contig(q_out, "q_out")
+        if q_out.dtype != torch.float32 or tuple(q_out.shape) != (B, Hq, D):
+            raise ValueError("q_out must be float32 [B,Hq,D]")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gqa_decode_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0),
+        k_new.stride(0) if pro else Hkv * D,
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), float(rope_theta), _ptr(pos),
+        _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(window), float(scale), int(part_tokens),
+        _ptr(workspace), nbytes, _ptr(out), _dtype_code(out, "out"), _ptr(lse_out),
+        _ptr(q_out), B, Hq, Hkv, D, T, _stream(dev)))
+    return out, workspace

@@ -100,13 +100,14 @@ int gqa_attn_decode(const void* q, gqa_dtype_t q_dtype,
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(lens, 4) || !aligned(lse_out, 4))
     return GQA_ERR_ALIGN;
-  gqa::AttnArgs a{};
-  a.q = q; a.q_bf16 = q_dtype == GQA_BF16;
+  gqa::KernelArgs a{};
+  a.q = q; a.q_bstride = (int64_t)Hq * D; a.in_bf16 = q_dtype == GQA_BF16;
   a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens; a.window = window;
   a.qscale = softmax_qscale(scale, D);
   a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T; a.split = false;
-  return gqa::launch_attn(a, stream);
+  a.num_parts = 1;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
+  return gqa::launch_attn_final(a, stream);
 }
 
 int gqa_num_partitions(int T, int window, int part_tokens) {
@@ -140,16 +141,16 @@ int gqa_attn_decode_splitk(const void* q, gqa_dtype_t q_dtype,
   if (workspace_bytes < gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens))
     return GQA_ERR_WORKSPACE;
   const int np = gqa_num_partitions(T, window, part_tokens);
-  gqa::AttnArgs a{};
-  a.q = q; a.q_bf16 = q_dtype == GQA_BF16;
+  gqa::KernelArgs a{};
+  a.q = q; a.q_bstride = (int64_t)Hq * D; a.in_bf16 = q_dtype == GQA_BF16;
   a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens; a.window = window;
   a.qscale = softmax_qscale(scale, D);
   a.part_tokens = part_tokens; a.num_parts = np;
   a.ws_lse = static_cast<float*>(workspace);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                     align256(lse_bytes(B, Hq, np)));
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T; a.split = true;
-  return gqa::launch_attn(a, stream);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
+  return gqa::launch_attn_split(a, stream);
 }
 
 int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
@@ -174,6 +175,71 @@ int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
   a.num_parts = np; a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
   a.B = B; a.Hq = Hq; a.D = D;
   return gqa::launch_merge(a, stream);
+}
+
+size_t gqa_decode_step_workspace_bytes(int B, int Hq, int Hkv, int D, int T, int window,
+                                       int part_tokens) {
+  const size_t base = gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens);
+  if (base == 0 || Hkv < 1) return 0;
+  return align256(base) + (size_t)B * Hkv * sizeof(uint32_t);
+}
+
+int gqa_decode_step(const void* q, const void* k_new, const void* v_new, gqa_dtype_t in_dtype,
+                    int64_t q_bstride, int64_t kv_bstride,
+                    const float* q_norm_w, const float* k_norm_w, float eps,
+                    double rope_theta, const int32_t* pos,
+                    uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                    int window, float scale, int part_tokens,
+                    void* workspace, size_t workspace_bytes,
+                    void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                    int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !lens || !workspace || !out) return GQA_ERR_NULL;
+  // the prologue inputs come all together or not at all
+  const bool pro = pos != nullptr;
+  if ((k_new != nullptr) != pro || (v_new != nullptr) != pro) return GQA_ERR_NULL;
+  if ((q_norm_w == nullptr) != (k_norm_w == nullptr)) return GQA_ERR_NULL;
+  if (!pro && (q_norm_w != nullptr || q_out != nullptr)) return GQA_ERR_NULL;
+  int rc = check_shapes(B, Hq, Hkv, D, T);
+  if (rc) return rc;
+  if ((rc = check_split(T, window, part_tokens))) return rc;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (q_bstride < (int64_t)Hq * D || kv_bstride < (int64_t)Hkv * D) return GQA_ERR_SHAPE;
+  if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
+  if (isnan(rope_theta) || isinf(rope_theta)) return GQA_ERR_VALUE;
+  if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
+  const uintptr_t ea = in_dtype == GQA_BF16 ? 2 : 4;
+  // q rows are read as 16-byte vectors: the batch stride must keep that alignment
+  if (!aligned(q, 16) || (q_bstride * (int64_t)ea) % 16 != 0 || !aligned(k_new, ea) ||
+      !aligned(v_new, ea) || !aligned(q_norm_w, 16) || !aligned(k_norm_w, 4) ||
+      !aligned(pos, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(lens, 4) ||
+      !aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse_out, 4) ||
+      !aligned(q_out, 16))
+    return GQA_ERR_ALIGN;
+  if (workspace_bytes < gqa_decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens))
+    return GQA_ERR_WORKSPACE;
+  const int np = gqa_num_partitions(T, window, part_tokens);
+  gqa::KernelArgs a{};
+  a.q = q; a.q_bstride = q_bstride; a.in_bf16 = in_dtype == GQA_BF16;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.k_cache_w = k_cache; a.v_cache_w = v_cache;
+  a.lens = lens; a.window = window; a.qscale = softmax_qscale(scale, D);
+  a.part_tokens = part_tokens; a.num_parts = np;
+  char* ws = static_cast<char*>(workspace);
+  const size_t lse_sz = align256(lse_bytes(B, Hq, np));
+  a.ws_lse = reinterpret_cast<float*>(ws);
+  a.ws_o = reinterpret_cast<float*>(ws + lse_sz);
+  a.ws_cnt = reinterpret_cast<uint32_t*>(
+      ws + align256(gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens)));
+  a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
+  a.k_new = k_new; a.v_new = v_new; a.kv_bstride = kv_bstride;
+  a.wq = q_norm_w; a.wk = k_norm_w; a.eps = eps;
+  a.rope = pro && rope_theta > 0.0;
+  a.pos = pos; a.q_out = q_out;
+  if (a.rope)
+    for (int i = 0; i < D / 2; ++i)
+      a.inv_freq_rev[i] = pow(rope_theta, -2.0 * i / D) / 6.283185307179586476925;
+  return gqa::launch_decode_step(a, stream);
 }
 
 }  // extern "C"

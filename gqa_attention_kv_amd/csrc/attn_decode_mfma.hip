@@ -1,11 +1,19 @@
-// Single-token GQA decode attention on gfx950 matrix cores.
+// Single-token GQA decode attention on gfx950 matrix cores, in three modes
+// that share one body:
+//   Final  one workgroup per (sequence, KV head) writes the output directly;
+//   Split  one workgroup per (partition, KV head, sequence) writes the
+//          partition's (o_k, lse_k) for the log-sum-exp merge;
+//   Step   the whole decode step in one launch: per-head QK-RMSNorm and NeoX
+//          RoPE of the new query, the K/V append, the split-K pass, and the
+//          merge, done by the last workgroup of each (sequence, KV head) to
+//          finish.
 //
 // Computes what the fusedtok 1.0.1 README ("Operators" row attention_decode)
 // describes -- single-token GQA attention over a contiguous KV cache with
 // online softmax, per-sequence lengths and a flash-decoding split -- plus the
-// sliding window of the cutileGPT README feature list.  Same decomposition
-// as the VALU kernel: one workgroup per (partition, KV head, sequence)
-// covering all G query heads of that KV head, each K/V row read once.
+// sliding window and the fused QK-Norm + RoPE + KV-cache write of the
+// cutileGPT README feature list.  A workgroup covers all G query heads of one
+// KV head, so each K/V row is read from HBM once.
 //
 // Why matrix cores.  Per cached row the G heads need 2*G*D multiply-adds;
 // at G = 8 the VALU form costs more issue cycles per row than HBM needs to
@@ -48,38 +56,50 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;   // 16 bytes, register type
 
+enum class Mode { Final, Split, Step };
+
 template <int D>
 struct VRow;   // lane's slice of one V row: D/16 bf16
 template <>
 struct VRow<128> {
   uint4 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void unpack(float f[8]) const { unpack8(v, f); }
 };
 template <>
 struct VRow<64> {
   uint2 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ void zero() { v = make_uint2(0, 0); }
   __device__ __forceinline__ void unpack(float f[4]) const {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
   }
 };
 
-template <typename QT>
-__device__ __forceinline__ void load_q8f(const QT* p, float f[8]);
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float f[8]);
 template <>
-__device__ __forceinline__ void load_q8f<float>(const float* p, float f[8]) {
+__device__ __forceinline__ void load8f<float>(const float* p, float f[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 template <>
-__device__ __forceinline__ void load_q8f<uint16_t>(const uint16_t* p, float f[8]) {
+__device__ __forceinline__ void load8f<uint16_t>(const uint16_t* p, float f[8]) {
   unpack8(*reinterpret_cast<const uint4*>(p), f);
 }
+
+template <typename T>
+__device__ __forceinline__ float load1f(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load1f<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load1f<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+__device__ __forceinline__ uint16_t bits_bf16(const float* p, int64_t i) { return f32_to_bf16(p[i]); }
+__device__ __forceinline__ uint16_t bits_bf16(const uint16_t* p, int64_t i) { return p[i]; }
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
   return (uint32_t)lo | ((uint32_t)hi << 16);
@@ -91,17 +111,20 @@ struct TileBuf {
   VRow<D> v[4];        // V rows 4i + g, i < 4
 };
 
-template <int D, int G, int NW, typename QT, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(
-    const QT* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ lens, int window,
-    float qscale, int part_tokens, int num_parts, int Hq, int Hkv, int T,
-    float* __restrict__ ws_lse, float* __restrict__ ws_o, void* __restrict__ out,
-    int out_bf16, float* __restrict__ lse_out) {
+#ifndef GQA_WAVES_PER_EU
+#define GQA_WAVES_PER_EU 3
+#endif
+
+template <int D, int G, int NW, typename IT, Mode MODE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQA_WAVES_PER_EU))) void
+attn_decode_mfma_kernel(const KernelArgs a) {
   static_assert(G <= 16, "one 16-column MFMA tile holds at most 16 heads");
   constexpr int KC = D / 32;          // QK calls per tile (per q part)
   constexpr int VB = D / 16;          // PV column blocks
-  constexpr bool kLo = sizeof(QT) == 4;   // fp32 q needs the lo part
+  constexpr int HALF = D / 2;
+  // fp32 q (given, or the prologue's rotated q) needs the lo part
+  constexpr bool kLo = sizeof(IT) == 4 || MODE == Mode::Step;
+  constexpr bool kPartial = MODE != Mode::Final;
 
   const int part = blockIdx.x;
   const int g = blockIdx.y;
@@ -110,38 +133,38 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
   const int lg = lane >> 4;
+  const int T = a.T;
+  const int Hq = a.Hq;
+  const int Hkv = a.Hkv;
+  const int num_parts = a.num_parts;
 
-  const int nrow = min(max(lens[b], 0), T);
-  const int lo = window > 0 ? max(0, nrow - window) : 0;
+  const int nrow = min(max(a.lens[b], 0), T);
+  const int lo = a.window > 0 ? max(0, nrow - a.window) : 0;
   int t0 = lo, t1 = nrow;
-  if (SPLIT) {
-    t0 = min(lo + part * part_tokens, nrow);
-    t1 = min(t0 + part_tokens, nrow);
+  if (kPartial) {
+    t0 = min(lo + part * a.part_tokens, nrow);
+    t1 = min(t0 + a.part_tokens, nrow);
   }
   const int64_t head0 = (int64_t)b * Hq + (int64_t)g * G;
 
-  if (t0 >= t1) {
-    if (SPLIT) {
-      for (int h = threadIdx.x; h < G; h += NW * 64)
-        ws_lse[(head0 + h) * num_parts + part] = -INFINITY;
-    } else {
-      for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-        if (out_bf16) reinterpret_cast<uint16_t*>(out)[head0 * D + e] = 0;
-        else reinterpret_cast<float*>(out)[head0 * D + e] = 0.0f;
+  if constexpr (MODE != Mode::Step) {
+    if (t0 >= t1) {   // nothing to attend in this range (uniform over the workgroup)
+      if (MODE == Mode::Split) {
+        for (int h = threadIdx.x; h < G; h += NW * 64)
+          a.ws_lse[(head0 + h) * num_parts + part] = -INFINITY;
+      } else {
+        for (int e = threadIdx.x; e < G * D; e += NW * 64) {
+          if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[head0 * D + e] = 0;
+          else reinterpret_cast<float*>(a.out)[head0 * D + e] = 0.0f;
+        }
+        if (a.lse_out != nullptr)
+          for (int h = threadIdx.x; h < G; h += NW * 64) a.lse_out[head0 + h] = -INFINITY;
       }
-      if (lse_out != nullptr)
-        for (int h = threadIdx.x; h < G; h += NW * 64) lse_out[head0 + h] = -INFINITY;
+      return;
     }
-    return;
   }
 
-  float m = -INFINITY;   // running max of head n (same in all four lane groups)
-  float l = 0.0f;        // partial sum over this lane's rows
-  f32x4_t o[VB];         // O[head 4lg + r][d = VB n + blk]
-#pragma unroll
-  for (int blk = 0; blk < VB; ++blk) o[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t slab = ((int64_t)b * Hkv + g) * T * D;
+  const int64_t slab_off = ((int64_t)b * Hkv + g) * T * D;
   // K whole-row layout: a load covers RPI rows; lane l takes 16-byte piece
   // kp = l % PPR of row RPI*i + kr.
   constexpr int PPR = D / 8;            // 16-byte pieces per row
@@ -149,9 +172,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(
   constexpr int ROWU4 = PPR + 1;        // padded LDS row, in 16-byte units
   const int kp = lane % PPR;
   const int kr = lane / PPR;
-  const uint16_t* Kbase = k_cache + slab + 8 * kp;           // + row*D
-  const uint16_t* Vbase = v_cache + slab + VB * n;           // + row*D
+  const uint16_t* Kbase = a.k_cache + slab_off + 8 * kp;        // + row*D
+  const uint16_t* Vbase = a.v_cache + slab_off + VB * n;        // + row*D
   __shared__ u32x4_t sk[NW][16][ROWU4];
+  u32x4_t* slab = &sk[wave][0][0];
 
   // Loads are unconditional: a row index past the range is clamped to the
   // last valid row (an attended row, so finite), and the softmax gives such
@@ -173,50 +197,176 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(
   constexpr int STEP = NW * 16;
   int base = t0 + wave * 16;
   TileBuf<D> b0, b1;
-  if (base < t1) issue(b0, base);      // first tile in flight before q is read
-  // Q^T operand: lane holds q[head n][32c + 8lg .. +8] as bf16 hi (+ lo).
-  // All q loads are issued before any is used (one memory round trip).
-  uint4 qhi[KC], qlo[KC];
-  {
-    // Columns n >= G are padding: they load head G-1 (no branch around the
-    // loads) and are zeroed.
-    const float keep = n < G ? 1.0f : 0.0f;
-    const int hq = min(n, G - 1);
-    float qf[KC][8];
+  if constexpr (MODE != Mode::Step) {
+    if (base < t1) issue(b0, base);    // first tile in flight before q is read
+  }
+
+  // q for head n (padding columns n >= G load head G-1 -- no branch around
+  // the loads -- and are zeroed): lane holds elements 32c + 8lg + j.
+  const float keep = n < G ? 1.0f : 0.0f;
+  const int hq = min(n, G - 1);
+  float qf[KC][8];
+
+  if constexpr (MODE == Mode::Step) {
+    // ---- fused prologue: QK-RMSNorm, NeoX RoPE at pos[b], K/V append ----
+    // (skipped when no prologue inputs are given: q is then used as is)
+    const bool has_pro = a.pos != nullptr;
+    const int p = has_pro ? a.pos[b] : -1;
+    // The row pos[b] is written by the workgroup whose partition attends it
+    // (or partition 0 when it is not attended); positions outside [0, T)
+    // write nothing.  Every other workgroup never reads that row, so it
+    // starts streaming before the prologue arithmetic.
+    const bool in_range = has_pro && p >= 0 && p < T;
+    const bool attended = p >= lo && p < nrow;
+    const bool writer = in_range && (attended ? (p >= t0 && p < t1) : part == 0);
+    if (!writer && base < t1) issue(b0, base);
+    // Rotary angle of frequency index i = lane (lanes < D/2): the phase
+    // p * theta^(-2i/D) / (2 pi) is formed and reduced in float64 from a
+    // host-computed table, leaving a float32 sincos of an angle in [-pi, pi].
+    float cs = 1.0f, sn = 0.0f;
+    if (has_pro && a.rope) {
+      const double rev = (double)p * a.inv_freq_rev[lane % HALF];
+      const double fr = rev - rint(rev);
+      sincosf((float)(fr * 6.283185307179586), &sn, &cs);
+    }
+    if (writer && wave == 0) {
+      const IT* ks = reinterpret_cast<const IT*>(a.k_new) + (int64_t)b * a.kv_bstride +
+                     (int64_t)g * D;
+      const IT* vs = reinterpret_cast<const IT*>(a.v_new) + (int64_t)b * a.kv_bstride +
+                     (int64_t)g * D;
+      const int i = lane % HALF;
+      float x0 = load1f<IT>(ks, i), x1 = load1f<IT>(ks, i + HALF);
+      if (a.wk != nullptr) {
+        const float ss = group_sum_shfl<HALF>(x0 * x0 + x1 * x1);
+        const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+        x0 = x0 * r * a.wk[i];
+        x1 = x1 * r * a.wk[i + HALF];
+      }
+      if (a.rope) {
+        const float y0 = x0 * cs - x1 * sn, y1 = x1 * cs + x0 * sn;
+        x0 = y0;
+        x1 = y1;
+      }
+      if (lane < HALF) {
+        uint16_t* krow = a.k_cache_w + slab_off + (int64_t)p * D;
+        uint16_t* vrow = a.v_cache_w + slab_off + (int64_t)p * D;
+        krow[i] = f32_to_bf16(x0);
+        krow[i + HALF] = f32_to_bf16(x1);
+        vrow[i] = bits_bf16(vs, i);
+        vrow[i + HALF] = bits_bf16(vs, i + HALF);
+      }
+      __threadfence_block();            // the row is visible before the barrier
+    }
+    // Query head g*G + hq: RMSNorm over D (the lane's D/4 elements, summed
+    // over the four lane groups of head n), then RoPE: element e < D/2 of
+    // slice c pairs with e + D/2 in slice c + KC/2 of the same lane.
+    const IT* qs = reinterpret_cast<const IT*>(a.q) + (int64_t)b * a.q_bstride +
+                   (int64_t)(g * G + hq) * D;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) load_q8f<QT>(q + (head0 + hq) * D + 32 * c + 8 * lg, qf[c]);
+    for (int c = 0; c < KC; ++c) load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
+    if (has_pro && a.wq != nullptr) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(qf[c][j], qf[c][j], ss);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        float w8[8];
+        load8f<float>(a.wq + 32 * c + 8 * lg, w8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qf[c][j] = qf[c][j] * r * w8[j];
+      }
+    }
+    if (has_pro && a.rope) {
+      // Hand the angles across lanes through this wave's LDS slab (in-order
+      // LDS; the asm hides the indices from per-lane alias analysis).
+      float* af = reinterpret_cast<float*>(slab);
+      int aidx = lane % HALF;
+      asm volatile("" : "+v"(aidx));
+      if (lane < HALF) {
+        af[aidx] = cs;
+        af[HALF + aidx] = sn;
+      }
+      int ridx = 8 * lg;
+      asm volatile("" : "+v"(ridx));
+#pragma unroll
+      for (int c = 0; c < KC / 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float cc = af[ridx + 32 * c + j], sv = af[HALF + ridx + 32 * c + j];
+          const float x1 = qf[c][j], x2 = qf[c + KC / 2][j];
+          qf[c][j] = x1 * cc - x2 * sv;
+          qf[c + KC / 2][j] = x2 * cc + x1 * sv;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[c][j] *= keep;
+    if (has_pro && a.q_out != nullptr && part == 0 && wave == 0 && n < G) {
+      float* qo = a.q_out + (head0 + n) * D;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        *reinterpret_cast<float4*>(qo + 32 * c + 8 * lg) =
+            make_float4(qf[c][0], qf[c][1], qf[c][2], qf[c][3]);
+        *reinterpret_cast<float4*>(qo + 32 * c + 8 * lg + 4) =
+            make_float4(qf[c][4], qf[c][5], qf[c][6], qf[c][7]);
+      }
+    }
+    if (writer) {
+      __syncthreads();                  // appended row written before any load
+      if (base < t1) issue(b0, base);
+    }
+  } else {
+    // All q loads are issued before any is used (one memory round trip).
+    const IT* qs = reinterpret_cast<const IT*>(a.q) + (head0 + hq) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
     __builtin_amdgcn_sched_barrier(0);   // keep the q loads in one batch
 #pragma unroll
     for (int c = 0; c < KC; ++c)
 #pragma unroll
       for (int j = 0; j < 8; ++j) qf[c][j] *= keep;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      uint16_t h16[8], l16[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        h16[j] = f32_to_bf16(qf[c][j]);
-        l16[j] = f32_to_bf16(qf[c][j] - bf16_to_f32(h16[j]));
-      }
-      qhi[c] = make_uint4(pack2(h16[0], h16[1]), pack2(h16[2], h16[3]),
-                          pack2(h16[4], h16[5]), pack2(h16[6], h16[7]));
-      qlo[c] = make_uint4(pack2(l16[0], l16[1]), pack2(l16[2], l16[3]),
-                          pack2(l16[4], l16[5]), pack2(l16[6], l16[7]));
-    }
   }
 
+  // Q^T operand: bf16 hi (+ lo) parts of q[head n][32c + 8lg .. +8].
+  uint4 qhi[KC], qlo[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    uint16_t h16[8], l16[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      h16[j] = f32_to_bf16(qf[c][j]);
+      l16[j] = f32_to_bf16(qf[c][j] - bf16_to_f32(h16[j]));
+    }
+    qhi[c] = make_uint4(pack2(h16[0], h16[1]), pack2(h16[2], h16[3]),
+                        pack2(h16[4], h16[5]), pack2(h16[6], h16[7]));
+    qlo[c] = make_uint4(pack2(l16[0], l16[1]), pack2(l16[2], l16[3]),
+                        pack2(l16[4], l16[5]), pack2(l16[6], l16[7]));
+  }
+
+  float m = -INFINITY;   // running max of head n (same in all four lane groups)
+  float l = 0.0f;        // partial sum over this lane's rows
+  f32x4_t o[VB];         // O[head 4lg + r][d = VB n + blk]
+#pragma unroll
+  for (int blk = 0; blk < VB; ++blk) o[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float qscale = a.qscale;
+
   auto compute = [&](const TileBuf<D>& buf, int base) {
-    // K rows -> LDS -> A operand (row n, elements 32c + 8lg .. +8).  The slab
-    // is private to the wave and the hardware runs one wave's LDS operations
-    // in order, so no barrier is needed.  But the data crosses lanes, and
-    // per-lane alias analysis would let the compiler hoist a lane's reads
-    // above the other lanes' writes (or the next tile's writes above these
-    // reads).  Passing each index through an empty asm statement hides it
-    // from that analysis and keeps program order without a fence (a fence
-    // pins the prefetch registers to scratch; volatile accesses wait for
-    // every outstanding global load).
-    u32x4_t* slab = &sk[wave][0][0];
-    int widx = (RPI * 0 + kr) * ROWU4 + kp;
+    // K rows -> LDS -> A operand (row pi(n), elements 32c + 8lg .. +8).  The
+    // slab is private to the wave and the hardware runs one wave's LDS
+    // operations in order, so no barrier is needed.  But the data crosses
+    // lanes, and per-lane alias analysis would let the compiler hoist a
+    // lane's reads above the other lanes' writes (or the next tile's writes
+    // above these reads).  Passing each index through an empty asm statement
+    // hides it from that analysis and keeps program order without a fence
+    // (a fence pins the prefetch registers to scratch; volatile accesses
+    // wait for every outstanding global load).
+    int widx = kr * ROWU4 + kp;
     asm volatile("" : "+v"(widx));
 #pragma unroll
     for (int i = 0; i < 16 / RPI; ++i) slab[widx + RPI * i * ROWU4] = buf.k[i];
@@ -260,9 +410,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(
     // Rescale O rows: row 4lg + r belongs to the head held by lane 4lg + r.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float a = __shfl(alpha, 4 * lg + r, 64);
+      const float al = __shfl(alpha, 4 * lg + r, 64);
 #pragma unroll
-      for (int blk = 0; blk < VB; ++blk) o[blk][r] *= a;
+      for (int blk = 0; blk < VB; ++blk) o[blk][r] *= al;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -312,6 +462,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(
   }
   __syncthreads();
 
+  // Step with a single partition writes the final output like Final.
+  const bool write_final = MODE == Mode::Final || (MODE == Mode::Step && num_parts == 1);
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
     const int h = idx / D;
     const int d = idx % D;
@@ -329,14 +481,116 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(
     const bool any = L > 0.0f;
     const float ov = any ? A / L : 0.0f;
     const float lse = any ? (M + log2f(L)) * kLn2 : -INFINITY;
-    if (SPLIT) {
-      ws_o[((head0 + h) * num_parts + part) * D + d] = ov;
-      if (d == 0) ws_lse[(head0 + h) * num_parts + part] = lse;
+    if (write_final) {
+      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[(head0 + h) * D + d] = f32_to_bf16(ov);
+      else reinterpret_cast<float*>(a.out)[(head0 + h) * D + d] = ov;
+      if (d == 0 && a.lse_out != nullptr) a.lse_out[head0 + h] = lse;
+    } else if (MODE == Mode::Split) {
+      if (any) a.ws_o[((head0 + h) * num_parts + part) * D + d] = ov;
+      if (d == 0) a.ws_lse[(head0 + h) * num_parts + part] = lse;
     } else {
-      if (out_bf16) reinterpret_cast<uint16_t*>(out)[(head0 + h) * D + d] = f32_to_bf16(ov);
-      else reinterpret_cast<float*>(out)[(head0 + h) * D + d] = ov;
-      if (d == 0 && lse_out != nullptr) lse_out[head0 + h] = lse;
+      // Agent-scope stores write through to the coherence point, so the
+      // merging workgroup (possibly on another XCD) can read them without
+      // any L2 writeback.
+      if (any)
+        __hip_atomic_store(a.ws_o + ((head0 + h) * num_parts + part) * D + d, ov,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0)
+        __hip_atomic_store(a.ws_lse + (head0 + h) * num_parts + part, lse, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+
+  if constexpr (MODE == Mode::Step) {
+    if (num_parts == 1) return;
+    // Arrival ticket: every workgroup of this (sequence, KV head) publishes
+    // its partial, waits until those write-through stores have completed,
+    // and takes a ticket; the last one reads the partials back with
+    // agent-scope loads (which do not hit stale L2 lines), merges them in
+    // ascending partition order, and resets the ticket for the next launch.
+    // No workgroup waits on another.  Agent-scope fences would write back or
+    // invalidate a whole L2 per workgroup, which costs more than the step.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // stores completed
+    __syncthreads();
+    __shared__ int s_last;
+    uint32_t* ticket = a.ws_cnt + (int64_t)b * Hkv + g;
+    if (threadIdx.x == 0) {
+      const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == (uint32_t)(num_parts - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // Merge in chunks of MC partitions: the chunk's LSEs go through LDS
+    // (one coalesced round trip), then each thread issues the chunk's partial
+    // loads back to back and folds them in, in ascending partition order.
+    constexpr int NTH = NW * 64;
+    constexpr int PAIRS = (G * D + NTH - 1) / NTH;   // (head, d) outputs per thread
+    constexpr int MC = 16;
+    __shared__ float s_l[G][MC];
+    float Mx[PAIRS], Wx[PAIRS], Ax[PAIRS];
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+      Mx[j] = -INFINITY;
+      Wx[j] = 0.0f;
+      Ax[j] = 0.0f;
+    }
+    for (int kb = 0; kb < num_parts; kb += MC) {
+      const int kn = min(MC, num_parts - kb);
+      __syncthreads();
+      for (int t = threadIdx.x; t < G * MC; t += NTH) {
+        const int h = t / MC, k = t % MC;
+        s_l[h][k] = k < kn ? __hip_atomic_load(a.ws_lse + (head0 + h) * num_parts + kb + k,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : -INFINITY;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < PAIRS; ++j) {
+        const int idx = threadIdx.x + j * NTH;
+        if (idx >= G * D) break;
+        const int h = idx / D;
+        const int d = idx % D;
+        const float* Op = a.ws_o + ((head0 + h) * num_parts + kb) * D + d;
+        float ov[MC];
+#pragma unroll
+        for (int k = 0; k < MC; ++k)    // rows past kn stay inside the workspace
+          ov[k] = __hip_atomic_load(const_cast<float*>(Op) + (int64_t)min(k, kn - 1) * D,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float cm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < MC; ++k) cm = fmaxf(cm, s_l[h][k]);
+        const float Mn = fmaxf(Mx[j], cm);
+        if (Mn == -INFINITY) continue;
+        const float sc = __expf(Mx[j] - Mn);          // 0 while nothing was seen
+        float W = Wx[j] * sc, A = Ax[j] * sc;
+#pragma unroll
+        for (int k = 0; k < MC; ++k) {
+          const float lk = s_l[h][k];
+          const float w = lk == -INFINITY ? 0.0f : __expf(lk - Mn);
+          W += w;
+          A = fmaf(w, lk == -INFINITY ? 0.0f : ov[k], A);   // undefined o_k where empty
+        }
+        Mx[j] = Mn;
+        Wx[j] = W;
+        Ax[j] = A;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+      const int idx = threadIdx.x + j * NTH;
+      if (idx >= G * D) break;
+      const int h = idx / D;
+      const int d = idx % D;
+      const bool any = Wx[j] > 0.0f;
+      const float ov = any ? Ax[j] / Wx[j] : 0.0f;
+      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[(head0 + h) * D + d] = f32_to_bf16(ov);
+      else reinterpret_cast<float*>(a.out)[(head0 + h) * D + d] = ov;
+      if (d == 0 && a.lse_out != nullptr)
+        a.lse_out[head0 + h] = any ? Mx[j] + logf(Wx[j]) : -INFINITY;
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -344,44 +598,37 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_mfma_kernel(
 #define GQA_MFMA_NW 4
 #endif
 
-template <int D, int G, typename QT>
-static int launch_mfma_t(const AttnArgs& a, hipStream_t s) {
+template <int D, int G, typename IT, Mode MODE>
+static int launch_mode(const KernelArgs& a, hipStream_t s) {
   constexpr int NW = GQA_MFMA_NW;
-  const dim3 block(NW * 64);
-  if (a.split) {
-    const dim3 grid(a.num_parts, a.Hkv, a.B);
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, G, NW, QT, true>), grid, block, 0, s,
-                       (const QT*)a.q, a.k_cache, a.v_cache, a.lens, a.window, a.qscale,
-                       a.part_tokens, a.num_parts, a.Hq, a.Hkv, a.T, a.ws_lse, a.ws_o,
-                       nullptr, 0, nullptr);
-  } else {
-    const dim3 grid(1, a.Hkv, a.B);
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, G, NW, QT, false>), grid, block, 0, s,
-                       (const QT*)a.q, a.k_cache, a.v_cache, a.lens, a.window, a.qscale,
-                       0, 1, a.Hq, a.Hkv, a.T, nullptr, nullptr, a.out, a.out_bf16,
-                       a.lse_out);
-  }
+  const dim3 grid(MODE == Mode::Final ? 1 : a.num_parts, a.Hkv, a.B);
+  hipLaunchKernelGGL((attn_decode_mfma_kernel<D, G, NW, IT, MODE>), grid, dim3(NW * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
-template <int D, typename QT>
-static int dispatch_mfma_g(const AttnArgs& a, hipStream_t s) {
+template <int D, typename IT, Mode MODE>
+static int dispatch_g(const KernelArgs& a, hipStream_t s) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_mfma_t<D, 1, QT>(a, s);
-    case 2: return launch_mfma_t<D, 2, QT>(a, s);
-    case 4: return launch_mfma_t<D, 4, QT>(a, s);
-    case 8: return launch_mfma_t<D, 8, QT>(a, s);
-    case 16: return launch_mfma_t<D, 16, QT>(a, s);
+    case 1: return launch_mode<D, 1, IT, MODE>(a, s);
+    case 2: return launch_mode<D, 2, IT, MODE>(a, s);
+    case 4: return launch_mode<D, 4, IT, MODE>(a, s);
+    case 8: return launch_mode<D, 8, IT, MODE>(a, s);
+    case 16: return launch_mode<D, 16, IT, MODE>(a, s);
     default: return GQA_ERR_UNSUPPORTED;
   }
 }
 
-int launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
+template <Mode MODE>
+static int dispatch(const KernelArgs& a, hipStream_t s) {
   if (a.D == 128)
-    return a.q_bf16 ? dispatch_mfma_g<128, uint16_t>(a, s) : dispatch_mfma_g<128, float>(a, s);
+    return a.in_bf16 ? dispatch_g<128, uint16_t, MODE>(a, s) : dispatch_g<128, float, MODE>(a, s);
   if (a.D == 64)
-    return a.q_bf16 ? dispatch_mfma_g<64, uint16_t>(a, s) : dispatch_mfma_g<64, float>(a, s);
+    return a.in_bf16 ? dispatch_g<64, uint16_t, MODE>(a, s) : dispatch_g<64, float, MODE>(a, s);
   return GQA_ERR_UNSUPPORTED;
 }
+
+int launch_attn_final(const KernelArgs& a, hipStream_t s) { return dispatch<Mode::Final>(a, s); }
+int launch_attn_split(const KernelArgs& a, hipStream_t s) { return dispatch<Mode::Split>(a, s); }
+int launch_decode_step(const KernelArgs& a, hipStream_t s) { return dispatch<Mode::Step>(a, s); }
 
 }  // namespace gqa

@@ -25,23 +25,41 @@ struct PrologueArgs {
   int B, Hq, Hkv, D, T;
 };
 
-struct AttnArgs {
+constexpr int kMaxHalfDim = 64;   // D/2 for the largest supported head dim
+
+// Arguments of the attention kernel in all three modes, passed by value.
+struct KernelArgs {
+  // query: dense [B,Hq,D] (Final, Split) or rows q_bstride apart (Step)
   const void* q;
-  int q_bf16;
+  int64_t q_bstride;
+  int in_bf16;                 // q (and, in Step, k_new / v_new) are bf16
   const uint16_t* k_cache;
   const uint16_t* v_cache;
   const int32_t* lens;
   int window;
-  float qscale;        // softmax scale * log2(e)
-  int part_tokens;     // split mode: partition length
-  int num_parts;       // split mode: partitions per (sequence, KV head)
-  float* ws_lse;       // split mode: [B,Hq,num_parts]
-  float* ws_o;         // split mode: [B,Hq,num_parts,D]
-  void* out;           // final mode
+  float qscale;                // softmax scale * log2(e)
+  int part_tokens;             // Split / Step
+  int num_parts;
+  float* ws_lse;               // [B,Hq,num_parts]
+  float* ws_o;                 // [B,Hq,num_parts,D]
+  uint32_t* ws_cnt;            // Step: [B,Hkv] arrival tickets, zero between launches
+  void* out;                   // Final / Step
   int out_bf16;
-  float* lse_out;      // final mode, may be null
+  float* lse_out;              // may be null
   int B, Hq, Hkv, D, T;
-  bool split;
+  // Step only: the fused prologue
+  const void* k_new;
+  const void* v_new;
+  int64_t kv_bstride;
+  const float* wq;             // null: no QK-norm
+  const float* wk;
+  float eps;
+  int rope;                    // 0: no RoPE
+  const int32_t* pos;
+  float* q_out;                // may be null
+  uint16_t* k_cache_w;         // same buffers as k_cache / v_cache
+  uint16_t* v_cache_w;
+  double inv_freq_rev[kMaxHalfDim];   // theta^(-2i/D) / (2 pi), float64
 };
 
 struct MergeArgs {
@@ -55,17 +73,9 @@ struct MergeArgs {
 };
 
 int launch_prologue(const PrologueArgs& a, hipStream_t s);
-int launch_attn_valu(const AttnArgs& a, hipStream_t s);   // VALU dot products
-int launch_attn_mfma(const AttnArgs& a, hipStream_t s);   // matrix-core dot products
+int launch_attn_final(const KernelArgs& a, hipStream_t s);   // one pass per (seq, KV head)
+int launch_attn_split(const KernelArgs& a, hipStream_t s);   // partition pass
+int launch_decode_step(const KernelArgs& a, hipStream_t s);  // fused whole step
 int launch_merge(const MergeArgs& a, hipStream_t s);
-
-// The attention pass used by the C ABI.
-inline int launch_attn(const AttnArgs& a, hipStream_t s) {
-#ifdef GQA_ATTN_VALU
-  return launch_attn_valu(a, s);
-#else
-  return launch_attn_mfma(a, s);
-#endif
-}
 
 }  // namespace gqa

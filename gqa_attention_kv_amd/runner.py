@@ -13,8 +13,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import attn_decode, attn_decode_merge, attn_decode_splitk, qkv_prologue
-from . import splitk_workspace_bytes
+from . import attn_decode, attn_decode_merge, attn_decode_splitk, decode_step, qkv_prologue
+from . import decode_step_workspace_bytes, splitk_workspace_bytes
 
 BF16_NAN = 0x7FC0
 
@@ -33,9 +33,11 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 class DeviceStep:
     """One decode step of workload ``w`` with all inputs resident in HBM.
 
-    ``split``: use split-K partitions of ``part_tokens`` rows plus the merge
-    (default: the workload's own partition size); otherwise the unsplit
-    kernel.  ``q_dtype`` selects the dtype attention reads q in when the
+    ``mode``: "fused" runs the whole step as one launch (gqa_decode_step);
+    "split" runs the prologue, the split-K partition pass over
+    ``part_tokens``-row partitions (default: the workload's own size) and the
+    merge as three launches; "unsplit" runs the prologue and the unsplit
+    kernel.  ``split`` (bool) is the older spelling of split/unsplit.  ``q_dtype`` selects the dtype attention reads q in when the
     workload has no prologue.  ``poison`` writes bf16 NaN into every cache
     row outside each sequence's attended range [lo, n) (rows the step must
     never read); rows written by the prologue are left alone.
@@ -43,10 +45,12 @@ class DeviceStep:
 
     def __init__(self, w, device="cuda", split: bool = True,
                  part_tokens: Optional[int] = None, out_dtype: Optional[str] = None,
-                 q_dtype: str = "bf16", poison: bool = False, scale: float = 0.0):
+                 q_dtype: str = "bf16", poison: bool = False, scale: float = 0.0,
+                 mode: Optional[str] = None):
         self.w = w
         self.dev = torch.device(device)
-        self.split = split
+        self.mode = mode or ("split" if split else "unsplit")
+        self.split = self.mode == "split"
         self.part_tokens = int(part_tokens or w.part_tokens)
         self.scale = float(scale)
         od = out_dtype or w.out_dtype
@@ -81,9 +85,13 @@ class DeviceStep:
         self.out = torch.empty((w.B, w.Hq, w.D), dtype=self.out_dtype, device=d)
         self.lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=d)
         self.ws = None
-        if split:
+        if self.mode == "split":
             nb = splitk_workspace_bytes(w.B, w.Hq, w.D, w.T, w.window, self.part_tokens)
             self.ws = torch.empty(nb, dtype=torch.uint8, device=d)
+        elif self.mode == "fused":
+            nb = decode_step_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.T, w.window,
+                                             self.part_tokens)
+            self.ws = torch.zeros(nb, dtype=torch.uint8, device=d)   # tickets start at 0
 
     # -- the three stages, each one C-ABI call ------------------------------
     def prologue(self):
@@ -110,7 +118,22 @@ class DeviceStep:
         attn_decode_merge(self.ws, w.B, w.Hq, w.D, w.T, self.part_tokens, window=w.window,
                           out=self.out, lse_out=self.lse)
 
+    def fused(self):
+        w = self.w
+        if w.pos is None:        # no prologue: attention and merge in one launch
+            decode_step(self.q, None, None, None, self.k_cache, self.v_cache, self.lens,
+                        self.part_tokens, workspace=self.ws, window=w.window,
+                        scale=self.scale, out=self.out, lse_out=self.lse)
+            return
+        decode_step(self.q_in, self.k_new, self.v_new, self.pos, self.k_cache, self.v_cache,
+                    self.lens, self.part_tokens, workspace=self.ws, q_norm_w=self.w_q,
+                    k_norm_w=self.w_k, eps=w.eps, rope_theta=w.theta, window=w.window,
+                    scale=self.scale, out=self.out, lse_out=self.lse, q_out=self.q)
+
     def run(self):
+        if self.mode == "fused":
+            self.fused()
+            return
         self.prologue()
         self.attention()
         self.merge()

@@ -163,6 +163,43 @@ int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
                           void* out, gqa_dtype_t out_dtype, float* lse_out,
                           int B, int Hq, int D, int T, hipStream_t stream);
 
+/*
+ * The whole decode step in one launch (cutileGPT README: fused QK-Norm +
+ * RoPE + KV-cache writes; fusedtok 1.0.1 README: attention_decode with the
+ * flash-decoding split): the effect of gqa_qkv_prologue followed by
+ * gqa_attn_decode_splitk and gqa_attn_decode_merge, with q_out optional.
+ * Each (partition, KV head, sequence) workgroup rotates the new query
+ * itself; the workgroup whose partition holds row pos[b] (partition 0 when
+ * that row is not attended) computes and writes the appended K/V row before
+ * reading it; the last workgroup of each (sequence, KV head) to finish
+ * merges the partitions in ascending order.  Rotary angles are reduced in
+ * float64 (a host-computed theta^(-2i/D) table) before a float32 sincos.
+ *
+ * Arguments are those of the three calls it replaces, plus:
+ *   workspace  256-byte aligned, gqa_decode_step_workspace_bytes() bytes:
+ *              the split-K layout above, then (at the next 256-byte
+ *              boundary) uint32 [B,Hkv] arrival tickets.  The tickets must be
+ *              zero before the first call (e.g. a zero-filled allocation);
+ *              every call that completes leaves them zero again.  Calls that
+ *              share a workspace must not overlap in time.
+ *   q          16-byte aligned and q_bstride * element size a multiple of 16.
+ *   q_out      float32 [B,Hq,D] rotated queries, or NULL.
+ * With pos, k_new and v_new all NULL (and no norm weights, no q_out) the
+ * prologue is skipped: q [B,Hq,D] in in_dtype is attended as given and the
+ * cache is only read -- the split-K pass and the merge in one launch.
+ */
+size_t gqa_decode_step_workspace_bytes(int B, int Hq, int Hkv, int D, int T, int window,
+                                       int part_tokens);
+int gqa_decode_step(const void* q, const void* k_new, const void* v_new, gqa_dtype_t in_dtype,
+                    int64_t q_bstride, int64_t kv_bstride,
+                    const float* q_norm_w, const float* k_norm_w, float eps,
+                    double rope_theta, const int32_t* pos,
+                    uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                    int window, float scale, int part_tokens,
+                    void* workspace, size_t workspace_bytes,
+                    void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                    int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char* gqa_status_string(int status);
 

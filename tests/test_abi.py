@@ -116,6 +116,42 @@ def test_prologue_validation(G):
     assert call(q=A_ODD + 1, dt=0) == -6
 
 
+def test_decode_step_validation(G):
+    f = G.lib.gqa_decode_step
+    need = G.decode_step_workspace_bytes(1, 8, 2, 128, 1000, 0, 64)
+
+    def call(**kw):
+        a = dict(q=A16, kn=A16, vn=A16, dt=1, qs=8 * 128, kvs=2 * 128, wq=None, wk=None,
+                 eps=1e-6, theta=1e4, pos=A16, kc=A16, vc=A16, lens=A16, window=0,
+                 scale=0.0, P=64, ws=A16, wsb=need, out=A16, od=0, lse=None, qo=None,
+                 B=1, Hq=8, Hkv=2, D=128, T=1000)
+        a.update(kw)
+        return f(a["q"], a["kn"], a["vn"], a["dt"], a["qs"], a["kvs"], a["wq"], a["wk"],
+                 a["eps"], a["theta"], a["pos"], a["kc"], a["vc"], a["lens"], a["window"],
+                 a["scale"], a["P"], a["ws"], a["wsb"], a["out"], a["od"], a["lse"], a["qo"],
+                 a["B"], a["Hq"], a["Hkv"], a["D"], a["T"], None)
+    assert call(ws=None) == -1
+    assert call(lens=None) == -1
+    assert call(kn=None) == -1                  # pos without k_new
+    assert call(pos=None, kn=None) == -1        # v_new without pos
+    assert call(pos=None, kn=None, vn=None, qo=A16) == -1     # q_out needs the prologue
+    assert call(pos=None, kn=None, vn=None, wq=A16, wk=A16) == -1
+    assert call(wk=A16) == -1
+    assert call(Hq=7) == -2                     # Hq not a multiple of Hkv
+    assert call(qs=100) == -2
+    assert call(P=0) == -7
+    assert call(eps=float("nan")) == -7
+    assert call(theta=float("nan")) == -7
+    assert call(D=96) == -3
+    assert call(dt=3) == -3
+    assert call(qs=8 * 128 + 1) == -6           # q rows lose 16-byte alignment
+    assert call(ws=A16 + 16) == -6
+    assert call(wsb=need - 1) == -4
+    # split-K workspace rounded to 256 B, then one ticket per (seq, KV head)
+    base = G.splitk_workspace_bytes(1, 8, 128, 1000, 0, 64)
+    assert need == base + (-base) % 256 + 2 * 4
+
+
 def test_partition_counts_and_workspace(G):
     assert G.num_partitions(131072, 0, 2048) == 64
     assert G.num_partitions(32768, 4096, 512) == 8

@@ -72,14 +72,20 @@ def check_prologue(w, got, ref, what=""):
             np.testing.assert_array_equal(ref["v_cache"][b, :, p], w.v_new[b])
 
 
+def modes_for(w):
+    """Paths every workload runs through."""
+    return ["unsplit", "split", "fused"]
+
+
 def run_and_check(gpu, w, split=True, part_tokens=None, out_dtype=None, q_dtype="bf16",
-                  poison=False, scale=0.0, what=""):
+                  poison=False, scale=0.0, what="", mode=None):
     od = out_dtype or w.out_dtype
     pt = part_tokens or w.part_tokens
+    mode = mode or ("split" if split else "unsplit")
     _say(f"{what} cfg={w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} T={w.T} "
-         f"window={w.window} split={split} P={pt} out={od} q={q_dtype} poison={poison}")
-    step = gpu.DeviceStep(w, split=split, part_tokens=pt, out_dtype=od, q_dtype=q_dtype,
-                          poison=poison, scale=scale)
+         f"window={w.window} mode={mode} P={pt} out={od} q={q_dtype} poison={poison}")
+    step = gpu.DeviceStep(w, part_tokens=pt, out_dtype=od, q_dtype=q_dtype,
+                          poison=poison, scale=scale, mode=mode)
     step.run()
     got = step.results()
     # q in float32 holds the exact widening of the bf16 draws, and the oracle
@@ -107,6 +113,12 @@ def test_full_size_unsplit(gpu, name):
     run_and_check(gpu, w, split=False, what="full unsplit")
 
 
+@pytest.mark.parametrize("name", ["1", "2a", "2b", "3", "4", "5"])
+def test_full_size_fused(gpu, name):
+    w = W.make(name)
+    run_and_check(gpu, w, mode="fused", what="full fused")
+
+
 # ---------------------------------------------------------------------------
 # Reduced sizes spanning several tiles and a ragged tail
 # ---------------------------------------------------------------------------
@@ -123,14 +135,15 @@ REDUCED = [
 def test_reduced_split_sweep(gpu, name, over, parts):
     w = W.make(name, **over)
     ref = O.decode_step(w)
-    for pt in parts:
-        _say(f"reduced cfg={name} {over} P={pt}")
-        step = gpu.DeviceStep(w, split=True, part_tokens=pt)
-        step.run()
-        got = step.results()
-        check_attention(got, ref, w.out_dtype, f"cfg {name} P={pt}")
-        if w.pos is not None:
-            check_prologue(w, got, ref, f"cfg {name} P={pt}")
+    for mode in [m for m in modes_for(w) if m != "unsplit"]:
+        for pt in parts:
+            _say(f"reduced cfg={name} {over} mode={mode} P={pt}")
+            step = gpu.DeviceStep(w, part_tokens=pt, mode=mode)
+            step.run()
+            got = step.results()
+            check_attention(got, ref, w.out_dtype, f"cfg {name} {mode} P={pt}")
+            if w.pos is not None:
+                check_prologue(w, got, ref, f"cfg {name} {mode} P={pt}")
 
 
 @pytest.mark.parametrize("name,over,parts", REDUCED, ids=[r[0] for r in REDUCED])
@@ -181,45 +194,46 @@ def _edge_workload(G=4, D=128, T=200, B=3, Hkv=2, name="3", lens=None, window=0,
 @pytest.mark.parametrize("D", [64, 128])
 def test_group_sizes_and_head_dims(gpu, G, D):
     w = _edge_workload(G=G, D=D, T=300, B=2, Hkv=2, lens=[300, 77])
-    for split, pt in ((True, 64), (False, None)):
-        run_and_check(gpu, w, split=split, part_tokens=pt, what=f"G={G} D={D}")
+    for mode in modes_for(w):
+        run_and_check(gpu, w, mode=mode, part_tokens=64, what=f"G={G} D={D}")
 
 
 @pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 127, 128, 129, 256])
 def test_lengths_around_tiles(gpu, n):
     P = 128
     w = _edge_workload(G=4, D=128, T=256, B=2, lens=[n, max(1, 256 - n)])
-    for split in (True, False):
-        run_and_check(gpu, w, split=split, part_tokens=P, what=f"n={n}")
+    for mode in modes_for(w):
+        run_and_check(gpu, w, mode=mode, part_tokens=P, what=f"n={n}")
 
 
 @pytest.mark.parametrize("window", [1, 2, 99, 100, 101, 500])
 def test_windows(gpu, window):
     w = _edge_workload(G=8, D=128, T=256, B=3, lens=[100, 256, 1], window=window)
-    for split, pt in ((True, 32), (True, 1), (False, None)):
-        run_and_check(gpu, w, split=split, part_tokens=pt, what=f"window={window}")
+    for mode, pt in (("split", 32), ("split", 1), ("unsplit", None), ("fused", 32),
+                     ("fused", 1), ("fused", 4096)):
+        run_and_check(gpu, w, mode=mode, part_tokens=pt, what=f"window={window}")
 
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("q_dtype", ["f32", "bf16"])
 def test_dtypes(gpu, out_dtype, q_dtype):
     w = W.make("4", L=3000, out_dtype=out_dtype)
-    for split in (True, False):
-        run_and_check(gpu, w, split=split, part_tokens=512, out_dtype=out_dtype,
+    for mode in modes_for(w):
+        run_and_check(gpu, w, mode=mode, part_tokens=512, out_dtype=out_dtype,
                       q_dtype=q_dtype, what=f"dtypes q={q_dtype} out={out_dtype}")
 
 
 def test_explicit_scale(gpu):
     w = W.make("4", L=1000)
-    for split in (True, False):
-        run_and_check(gpu, w, split=split, part_tokens=128, scale=0.3, what="scale=0.3")
+    for mode in modes_for(w):
+        run_and_check(gpu, w, mode=mode, part_tokens=128, scale=0.3, what="scale=0.3")
 
 
 def test_out_of_contract_lens(gpu):
     """lens = 0 / negative -> out 0, lse -inf; lens > T clamped to T."""
     w = _edge_workload(name="4", G=4, D=128, T=256, B=4, lens=[0, -5, 10_000, 256])
-    for split in (True, False):
-        step, got, ref, _ = run_and_check(gpu, w, split=split, part_tokens=64,
+    for mode in modes_for(w):
+        step, got, ref, _ = run_and_check(gpu, w, mode=mode, part_tokens=64,
                                           what="lens out of contract")
         assert np.all(got["out"][:2] == 0) and np.all(got["lse"][:2] == -math.inf)
 
@@ -247,9 +261,10 @@ def test_nan_poison_outside_window(gpu):
         w = W.make(name, **over)
         if name == "4":
             w.lens = np.array([1777], np.int32)
-        for split, pt in ((True, 64), (True, 100), (False, None)):
-            run_and_check(gpu, w, split=split, part_tokens=pt, poison=True,
-                          what=f"poison cfg {name}")
+        for mode in modes_for(w):
+            for pt in ((64, 100) if mode != "unsplit" else (None,)):
+                run_and_check(gpu, w, mode=mode, part_tokens=pt, poison=True,
+                              what=f"poison cfg {name}")
 
 
 def test_prologue_fp32_inputs_and_packed_qkv(gpu):
@@ -281,12 +296,14 @@ def test_prologue_fp32_inputs_and_packed_qkv(gpu):
 
 def test_bit_identical_reruns(gpu):
     import torch
-    for name, over, split in (("5", dict(B=2, L=3000, window=1000), True),
-                              ("3", dict(B=4, L=2000), True),
-                              ("3", dict(B=4, L=2000), False)):
+    for name, over, mode in (("5", dict(B=2, L=3000, window=1000), "split"),
+                             ("3", dict(B=4, L=2000), "split"),
+                             ("3", dict(B=4, L=2000), "unsplit"),
+                             ("5", dict(B=2, L=3000, window=1000), "fused"),
+                             ("3", dict(B=4, L=2000), "fused")):
         w = W.make(name, **over)
-        _say(f"determinism cfg {name} split={split}")
-        step = gpu.DeviceStep(w, split=split, part_tokens=256)
+        _say(f"determinism cfg {name} mode={mode}")
+        step = gpu.DeviceStep(w, mode=mode, part_tokens=256)
         step.run()
         a = (step.out.clone(), step.lse.clone())
         for _ in range(3):
@@ -304,3 +321,83 @@ def test_split_matches_unsplit(gpu):
         outs.append(s.results()["out"])
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) <= 2e-5
+
+
+# ---------------------------------------------------------------------------
+# The fused whole-step launch
+# ---------------------------------------------------------------------------
+def test_fused_pos_not_attended_still_appends(gpu):
+    """pos outside the attended window / past lens: the row is still written
+    (by partition 0) and attention ignores it."""
+    w = W.make("5", B=3, L=600, window=100)
+    w.pos = np.array([599, 10, 300], np.int32)       # attended, before lo, before lo
+    w.lens = np.array([600, 600, 200], np.int32)      # b=2: pos 300 >= n = 200
+    run_and_check(gpu, w, mode="fused", part_tokens=32, what="fused pos not attended")
+
+
+def test_fused_pos_out_of_range_and_empty(gpu):
+    w = W.make("5", B=4, L=300, window=100)
+    w.pos = np.array([-1, 300, 5000, 299], np.int32)
+    w.lens = np.array([300, 0, 300, -7], np.int32)
+    _say("fused pos out of range / empty lens")
+    step = gpu.DeviceStep(w, mode="fused", part_tokens=32)
+    step.run()
+    got = step.results()
+    ref = O.decode_step(w)
+    check_attention(got, ref, "f32", "fused oob")
+    assert np.all(got["out"][1] == 0) and np.all(got["out"][3] == 0)
+    # rows of b=0..2 untouched; b=3 writes row 299
+    kc = got["k_cache"]
+    assert np.array_equal(kc[:3], w.k_cache[:3])
+    check_prologue(w, got, ref, "fused oob")
+
+
+def test_fused_single_partition_and_q_out(gpu):
+    """One partition per (sequence, KV head): the workgroup writes the final
+    output itself; q_out equals the oracle's rotated query."""
+    w = W.make("2a", B=2, L=200)
+    run_and_check(gpu, w, mode="fused", part_tokens=100000, what="fused one partition")
+
+
+def test_fused_fp32_inputs_and_packed_qkv(gpu):
+    import torch
+    import gqa_attention_kv_amd as G
+    from gqa_attention_kv_amd.runner import bf16_tensor, bf16_bits
+    w = W.make("5", B=3, L=700, window=300)
+    B, Hq, Hkv, D, T = w.B, w.Hq, w.Hkv, w.D, w.T
+    ref = O.decode_step(w)
+    for dt in (torch.bfloat16, torch.float32):
+        _say(f"fused packed qkv dtype={dt}")
+        packed = torch.empty((B, Hq + 2 * Hkv, D), dtype=dt, device="cuda")
+        packed[:, :Hq] = bf16_tensor(w.q, "cuda").to(dt)
+        packed[:, Hq:Hq + Hkv] = bf16_tensor(w.k_new, "cuda").to(dt)
+        packed[:, Hq + Hkv:] = bf16_tensor(w.v_new, "cuda").to(dt)
+        kc = bf16_tensor(w.k_cache, "cuda")
+        vc = bf16_tensor(w.v_cache, "cuda")
+        q_out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        out, _ = G.decode_step(packed[:, :Hq], packed[:, Hq:Hq + Hkv], packed[:, Hq + Hkv:],
+                               torch.from_numpy(w.pos).cuda(), kc, vc,
+                               torch.from_numpy(w.lens).cuda(), 64,
+                               q_norm_w=torch.from_numpy(w.w_q).cuda(),
+                               k_norm_w=torch.from_numpy(w.w_k).cuda(), eps=w.eps,
+                               rope_theta=w.theta, window=w.window, lse_out=lse, q_out=q_out)
+        torch.cuda.synchronize()
+        got = dict(out=out.cpu().numpy().astype(np.float64),
+                   lse=lse.cpu().numpy().astype(np.float64),
+                   q=q_out.cpu().numpy().astype(np.float64),
+                   k_cache=bf16_bits(kc), v_cache=bf16_bits(vc))
+        check_attention(got, ref, "f32", f"fused packed {dt}")
+        check_prologue(w, got, ref, f"fused packed {dt}")
+
+
+def test_fused_matches_three_launch_path(gpu):
+    w = W.make("3", B=6, L=3000, lmin=1)
+    res = {}
+    for mode in ("split", "fused"):
+        _say(f"fused vs split {mode}")
+        s = gpu.DeviceStep(w, mode=mode, part_tokens=256, out_dtype="f32")
+        s.run()
+        res[mode] = s.results()
+    assert np.max(np.abs(res["split"]["out"] - res["fused"]["out"])) <= 2e-5
+    assert np.max(np.abs(res["split"]["q"] - res["fused"]["q"])) <= 1e-5
