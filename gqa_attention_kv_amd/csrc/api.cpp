@@ -11,6 +11,9 @@
 namespace {
 
 constexpr int64_t kMaxIndex = INT64_C(1) << 62;
+// Workgroups per launch: one-dimensional grids of up to 512 threads per
+// workgroup stay below 2^32 threads.
+constexpr int64_t kMaxWorkgroups = INT64_C(1) << 23;
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -23,16 +26,23 @@ int check_shapes(int B, int Hq, int Hkv, int D, int T) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || T < 1) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_SHAPE;
   if ((int64_t)B * Hkv * T > kMaxIndex / D) return GQA_ERR_SHAPE;
-  if ((int64_t)B * Hq > INT32_MAX / 2) return GQA_ERR_SHAPE;
-  if (B > 65535 || Hkv > 65535) return GQA_ERR_SHAPE;   // grid y/z limits
+  if ((int64_t)B * Hq > kMaxWorkgroups) return GQA_ERR_SHAPE;
   if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
   if (!group_ok(Hq / Hkv)) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
 
-int check_split(int T, int window, int part_tokens) {
+int num_parts(int T, int window, int part_tokens) {
+  const int64_t span = window > 0 && window < T ? window : T;
+  return (int)((span + part_tokens - 1) / part_tokens);
+}
+
+// Split-K checks; B * Hkv * partitions is the attention pass's grid.
+int check_split(int B, int Hkv, int T, int window, int part_tokens) {
   if (part_tokens < 1) return GQA_ERR_VALUE;
   if ((int64_t)T + part_tokens >= INT32_MAX) return GQA_ERR_SHAPE;
+  if ((int64_t)B * Hkv * num_parts(T, window, part_tokens) > kMaxWorkgroups)
+    return GQA_ERR_SHAPE;
   return GQA_OK;
 }
 
@@ -112,8 +122,7 @@ int gqa_attn_decode(const void* q, gqa_dtype_t q_dtype,
 
 int gqa_num_partitions(int T, int window, int part_tokens) {
   if (T < 1 || part_tokens < 1) return 0;
-  const int64_t span = window > 0 && window < T ? window : T;
-  return (int)((span + part_tokens - 1) / part_tokens);
+  return num_parts(T, window, part_tokens);
 }
 
 static size_t lse_bytes(int B, int Hq, int np) { return (size_t)B * Hq * np * sizeof(float); }
@@ -132,7 +141,7 @@ int gqa_attn_decode_splitk(const void* q, gqa_dtype_t q_dtype,
   if (!q || !k_cache || !v_cache || !lens || !workspace) return GQA_ERR_NULL;
   int rc = check_shapes(B, Hq, Hkv, D, T);
   if (rc) return rc;
-  if ((rc = check_split(T, window, part_tokens))) return rc;
+  if ((rc = check_split(B, Hkv, T, window, part_tokens))) return rc;
   if (!dtype_ok(q_dtype)) return GQA_ERR_UNSUPPORTED;
   if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -159,9 +168,9 @@ int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
                           int B, int Hq, int D, int T, hipStream_t stream) {
   if (!workspace || !out) return GQA_ERR_NULL;
   if (B < 1 || Hq < 1 || T < 1) return GQA_ERR_SHAPE;
-  if ((int64_t)B * Hq > INT32_MAX / 2) return GQA_ERR_SHAPE;
+  if ((int64_t)B * Hq > kMaxWorkgroups) return GQA_ERR_SHAPE;
   if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
-  int rc = check_split(T, window, part_tokens);
+  int rc = check_split(1, 1, T, window, part_tokens);
   if (rc) return rc;
   if (!dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
   if (!aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse_out, 4)) return GQA_ERR_ALIGN;
@@ -201,7 +210,7 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, gqa_dty
   if (!pro && (q_norm_w != nullptr || q_out != nullptr)) return GQA_ERR_NULL;
   int rc = check_shapes(B, Hq, Hkv, D, T);
   if (rc) return rc;
-  if ((rc = check_split(T, window, part_tokens))) return rc;
+  if ((rc = check_split(B, Hkv, T, window, part_tokens))) return rc;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
   if (q_bstride < (int64_t)Hq * D || kv_bstride < (int64_t)Hkv * D) return GQA_ERR_SHAPE;
   if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;

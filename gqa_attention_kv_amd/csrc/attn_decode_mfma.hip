@@ -98,6 +98,9 @@ __device__ __forceinline__ float load1f<uint16_t>(const uint16_t* p, int64_t i) 
   return bf16_to_f32(p[i]);
 }
 
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+
 __device__ __forceinline__ uint16_t bits_bf16(const float* p, int64_t i) { return f32_to_bf16(p[i]); }
 __device__ __forceinline__ uint16_t bits_bf16(const uint16_t* p, int64_t i) { return p[i]; }
 
@@ -114,6 +117,9 @@ struct TileBuf {
 #ifndef GQA_WAVES_PER_EU
 #define GQA_WAVES_PER_EU 3
 #endif
+#ifndef GQA_STAGES
+#define GQA_STAGES 2
+#endif
 
 template <int D, int G, int NW, typename IT, Mode MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQA_WAVES_PER_EU))) void
@@ -126,9 +132,29 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   constexpr bool kLo = sizeof(IT) == 4 || MODE == Mode::Step;
   constexpr bool kPartial = MODE != Mode::Final;
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // One-dimensional grid.  The hardware hands workgroup i to XCD i % 8.
+  // With 8 or more partitions per (sequence, KV head) the partition index
+  // runs fastest, so consecutive partitions of one sequence land on
+  // consecutive XCDs.  With fewer, it runs slowest: workgroup i takes
+  // partition i / (B*Hkv) of (sequence, KV head) i % (B*Hkv), so every XCD
+  // gets the same mix of partitions -- partition 0 of every sequence is the
+  // one that is never empty under ragged lengths -- and the dispatcher
+  // starts all first partitions before any later one.  (Partition-fastest
+  // order with few partitions puts every partition 0 on the same two XCDs;
+  // partition-major order with many partitions per sequence measured slower
+  // and sensitive to where the K and V caches sit relative to each other.)
+  const int nbg = a.B * a.Hkv;
+  const int npg = MODE == Mode::Final ? 1 : a.num_parts;
+  int part, bg;
+  if (npg >= 8) {
+    bg = (int)blockIdx.x / npg;
+    part = (int)blockIdx.x - bg * npg;
+  } else {
+    part = (int)blockIdx.x / nbg;
+    bg = (int)blockIdx.x - part * nbg;
+  }
+  const int g = bg % a.Hkv;
+  const int b = bg / a.Hkv;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n = lane & 15;
@@ -178,28 +204,34 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   u32x4_t* slab = &sk[wave][0][0];
 
   // Loads are unconditional: a row index past the range is clamped to the
-  // last valid row (an attended row, so finite), and the softmax gives such
-  // rows p = 0.  With no branches around the loads the compiler can count
-  // them exactly and wait only for the tile being computed.
-  auto issue = [&](TileBuf<D>& buf, int base) {
+  // last valid row (an attended row, so finite; row 0 when the range is
+  // empty), and the softmax gives such rows p = 0.  With no branches around
+  // the loads the compiler can count them exactly and wait only for the tile
+  // being computed.
+  const int rlast = max(t1 - 1, 0);
+  auto issue_from = [&](TileBuf<D>& buf, int base, const uint16_t* kb, const uint16_t* vb,
+                        int rstride) {
 #pragma unroll
     for (int i = 0; i < 16 / RPI; ++i) {
-      const int rk = min(base + RPI * i + kr, t1 - 1);
-      buf.k[i] = *reinterpret_cast<const u32x4_t*>(Kbase + (int64_t)rk * D);
+      const int rk = min(base + RPI * i + kr, rlast);
+      buf.k[i] = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)rk * rstride);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rv = min(base + 4 * i + lg, t1 - 1);
-      buf.v[i].load(Vbase + (int64_t)rv * D);
+      const int rv = min(base + 4 * i + lg, rlast);
+      buf.v[i].load(vb + (int64_t)rv * rstride);
     }
   };
+  auto issue = [&](TileBuf<D>& buf, int base) { issue_from(buf, base, Kbase, Vbase, D); };
 
   constexpr int STEP = NW * 16;
+  constexpr int S = GQA_STAGES;        // register tile buffers
   int base = t0 + wave * 16;
-  TileBuf<D> b0, b1;
-  if constexpr (MODE != Mode::Step) {
-    if (base < t1) issue(b0, base);    // first tile in flight before q is read
-  }
+  TileBuf<D> bf[S];
+  auto prime = [&]() {                 // the S tiles of the first trip
+#pragma unroll
+    for (int s = 0; s < S; ++s) issue(bf[s], base + s * STEP);
+  };
 
   // q for head n (padding columns n >= G load head G-1 -- no branch around
   // the loads -- and are zeroed): lane holds elements 32c + 8lg + j.
@@ -214,33 +246,78 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     const int p = has_pro ? a.pos[b] : -1;
     // The row pos[b] is written by the workgroup whose partition attends it
     // (or partition 0 when it is not attended); positions outside [0, T)
-    // write nothing.  Every other workgroup never reads that row, so it
-    // starts streaming before the prologue arithmetic.
+    // write nothing.  No other workgroup reads that row.
     const bool in_range = has_pro && p >= 0 && p < T;
     const bool attended = p >= lo && p < nrow;
     const bool writer = in_range && (attended ? (p >= t0 && p < t1) : part == 0);
-    if (!writer && base < t1) issue(b0, base);
-    // Rotary angle of frequency index i = lane (lanes < D/2): the phase
-    // p * theta^(-2i/D) / (2 pi) is formed and reduced in float64 from a
-    // host-computed table, leaving a float32 sincos of an angle in [-pi, pi].
-    float cs = 1.0f, sn = 0.0f;
-    if (has_pro && a.rope) {
-      const double rev = (double)p * a.inv_freq_rev[lane % HALF];
-      const double fr = rev - rint(rev);
-      sincosf((float)(fr * 6.283185307179586), &sn, &cs);
+    const bool reads_row = writer && attended;
+    // Every global load of the prologue is issued before the first tiles:
+    // loads complete in order, so waiting for these never waits for a tile.
+    const IT* qs = reinterpret_cast<const IT*>(a.q) + (int64_t)b * a.q_bstride +
+                   (int64_t)(g * G + hq) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
+    const bool qnorm = has_pro && a.wq != nullptr;
+    const bool rope = has_pro && a.rope;
+    float wq8[KC][8];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (qnorm) load8f<float>(a.wq + 32 * c + 8 * lg, wq8[c]);
     }
-    if (writer && wave == 0) {
+    const int fi = lane % HALF;               // rotary frequency index of this lane
+    const double inv_rev = rope ? a.inv_freq_rev[fi] : 0.0;
+    const bool kwrite = writer && wave == 0;
+    // raw values: converted only after the tiles are issued
+    IT rx0 = 0, rx1 = 0, rv0 = 0, rv1 = 0;
+    float wk0 = 1.0f, wk1 = 1.0f;
+    if (kwrite) {
       const IT* ks = reinterpret_cast<const IT*>(a.k_new) + (int64_t)b * a.kv_bstride +
                      (int64_t)g * D;
       const IT* vs = reinterpret_cast<const IT*>(a.v_new) + (int64_t)b * a.kv_bstride +
                      (int64_t)g * D;
-      const int i = lane % HALF;
-      float x0 = load1f<IT>(ks, i), x1 = load1f<IT>(ks, i + HALF);
+      rx0 = ks[fi];
+      rx1 = ks[fi + HALF];
+      rv0 = vs[fi];
+      rv1 = vs[fi + HALF];
+      if (a.wk != nullptr) {
+        wk0 = a.wk[fi];
+        wk1 = a.wk[fi + HALF];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // A writer whose appended row falls in the first tiles issues them only
+    // after the append; until then its buffers are filled from its own q row
+    // (same number of loads, so the compiler still counts them exactly, and
+    // every lane's pieces stay inside that row: it holds D elements of at
+    // least 2 bytes).  Otherwise no primed row is the appended one: a
+    // partition holding pos past its first S tiles has more rows than those
+    // tiles cover, so none of their rows is clamped.
+    const bool late = reads_row && (p - t0) < S * STEP;
+    {
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(qs);
+      const uint16_t* kb = late ? qrow + 8 * kp : Kbase;
+      const uint16_t* vb = late ? qrow + VB * n : Vbase;
+      const int rs = late ? 0 : D;
+#pragma unroll
+      for (int s2 = 0; s2 < S; ++s2) issue_from(bf[s2], base + s2 * STEP, kb, vb, rs);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Rotary angle of frequency index fi: the phase p * theta^(-2fi/D) / (2 pi)
+    // is formed and reduced in float64 from a host-computed table, leaving a
+    // float32 sincos of an angle in [-pi, pi].
+    float cs = 1.0f, sn = 0.0f;
+    if (rope) {
+      const double rev = (double)p * inv_rev;
+      const double fr = rev - rint(rev);
+      sincosf((float)(fr * 6.283185307179586), &sn, &cs);
+    }
+    if (kwrite) {
+      float x0 = to_f32(rx0), x1 = to_f32(rx1);
       if (a.wk != nullptr) {
         const float ss = group_sum_shfl<HALF>(x0 * x0 + x1 * x1);
         const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
-        x0 = x0 * r * a.wk[i];
-        x1 = x1 * r * a.wk[i + HALF];
+        x0 = x0 * r * wk0;
+        x1 = x1 * r * wk1;
       }
       if (a.rope) {
         const float y0 = x0 * cs - x1 * sn, y1 = x1 * cs + x0 * sn;
@@ -250,21 +327,17 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       if (lane < HALF) {
         uint16_t* krow = a.k_cache_w + slab_off + (int64_t)p * D;
         uint16_t* vrow = a.v_cache_w + slab_off + (int64_t)p * D;
-        krow[i] = f32_to_bf16(x0);
-        krow[i + HALF] = f32_to_bf16(x1);
-        vrow[i] = bits_bf16(vs, i);
-        vrow[i + HALF] = bits_bf16(vs, i + HALF);
+        krow[fi] = f32_to_bf16(x0);
+        krow[fi + HALF] = f32_to_bf16(x1);
+        vrow[fi] = bits_bf16(&rv0, 0);
+        vrow[fi + HALF] = bits_bf16(&rv1, 0);
       }
-      __threadfence_block();            // the row is visible before the barrier
+      if (reads_row) __threadfence_block();   // the row is visible before the barrier
     }
     // Query head g*G + hq: RMSNorm over D (the lane's D/4 elements, summed
     // over the four lane groups of head n), then RoPE: element e < D/2 of
     // slice c pairs with e + D/2 in slice c + KC/2 of the same lane.
-    const IT* qs = reinterpret_cast<const IT*>(a.q) + (int64_t)b * a.q_bstride +
-                   (int64_t)(g * G + hq) * D;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
-    if (has_pro && a.wq != nullptr) {
+    if (qnorm) {
       float ss = 0.0f;
 #pragma unroll
       for (int c = 0; c < KC; ++c)
@@ -274,18 +347,15 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       ss += __shfl_xor(ss, 32, 64);
       const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        float w8[8];
-        load8f<float>(a.wq + 32 * c + 8 * lg, w8);
+      for (int c = 0; c < KC; ++c)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qf[c][j] = qf[c][j] * r * w8[j];
-      }
+        for (int j = 0; j < 8; ++j) qf[c][j] = qf[c][j] * r * wq8[c][j];
     }
-    if (has_pro && a.rope) {
+    if (rope) {
       // Hand the angles across lanes through this wave's LDS slab (in-order
       // LDS; the asm hides the indices from per-lane alias analysis).
       float* af = reinterpret_cast<float*>(slab);
-      int aidx = lane % HALF;
+      int aidx = fi;
       asm volatile("" : "+v"(aidx));
       if (lane < HALF) {
         af[aidx] = cs;
@@ -298,9 +368,9 @@ attn_decode_mfma_kernel(const KernelArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float cc = af[ridx + 32 * c + j], sv = af[HALF + ridx + 32 * c + j];
-          const float x1 = qf[c][j], x2 = qf[c + KC / 2][j];
-          qf[c][j] = x1 * cc - x2 * sv;
-          qf[c + KC / 2][j] = x2 * cc + x1 * sv;
+          const float y1 = qf[c][j], y2 = qf[c + KC / 2][j];
+          qf[c][j] = y1 * cc - y2 * sv;
+          qf[c + KC / 2][j] = y2 * cc + y1 * sv;
         }
     }
 #pragma unroll
@@ -317,16 +387,19 @@ attn_decode_mfma_kernel(const KernelArgs a) {
             make_float4(qf[c][4], qf[c][5], qf[c][6], qf[c][7]);
       }
     }
-    if (writer) {
-      __syncthreads();                  // appended row written before any load
-      if (base < t1) issue(b0, base);
+    if (reads_row) {
+      __syncthreads();                  // appended row written before it is loaded
+      if (late) prime();
     }
   } else {
-    // All q loads are issued before any is used (one memory round trip).
+    // The q loads go out first and the first tiles right behind them, so
+    // waiting for q never waits for a tile (loads complete in order).
     const IT* qs = reinterpret_cast<const IT*>(a.q) + (head0 + hq) * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
-    __builtin_amdgcn_sched_barrier(0);   // keep the q loads in one batch
+    __builtin_amdgcn_sched_barrier(0);
+    prime();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
 #pragma unroll
@@ -424,20 +497,24 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
   };
 
-  // Two tiles per trip, no branch inside the trip: the second tile may lie
-  // wholly past the range, and then every row is masked (p = 0, and alpha = 1
-  // because the running max is already finite), which leaves the state
-  // unchanged.  A branch between a prefetch and its use would let the
-  // compiler sink the loads past the compute they are meant to overlap; the
-  // scheduling barriers keep the machine scheduler from doing the same.
+  // S tiles per trip, no branch inside the trip: tiles after the first may
+  // lie wholly past the range, and then every row is masked (p = 0, and
+  // alpha = 1 because the running max is already finite), which leaves the
+  // state unchanged.  As soon as tile s is computed its buffer is refilled
+  // with the tile one trip ahead, so S - 1 tiles are in flight behind each
+  // compute (and S were issued before the first).  A branch between a
+  // prefetch and its use would let the compiler sink the loads past the
+  // compute they are meant to overlap; the scheduling barriers keep the
+  // machine scheduler from doing the same.
   if (base < t1) {
-    for (; base < t1; base += 2 * STEP) {
-      issue(b1, base + STEP);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(b0, base);
-      issue(b0, base + 2 * STEP);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(b1, base + STEP);
+    for (; base < t1; base += S * STEP) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        compute(bf[s], base + s * STEP);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(bf[s], base + (s + S) * STEP);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
@@ -521,13 +598,14 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    // Merge in chunks of MC partitions: the chunk's LSEs go through LDS
-    // (one coalesced round trip), then each thread issues the chunk's partial
-    // loads back to back and folds them in, in ascending partition order.
+    // Merge, in ascending partition order.  Thread pair j owns output (h, d);
+    // h is the same across a wave (G*D and D are multiples of 64).  The LSEs
+    // of 64 partitions sit one per lane and are read back with readlane, and
+    // each chunk of MC partials is loaded in one batch together with them,
+    // so a merge of up to MC partitions is a single memory round trip.
     constexpr int NTH = NW * 64;
     constexpr int PAIRS = (G * D + NTH - 1) / NTH;   // (head, d) outputs per thread
-    constexpr int MC = 16;
-    __shared__ float s_l[G][MC];
+    constexpr int MC = PAIRS >= 8 ? 4 : 32 / PAIRS;
     float Mx[PAIRS], Wx[PAIRS], Ax[PAIRS];
 #pragma unroll
     for (int j = 0; j < PAIRS; ++j) {
@@ -535,45 +613,50 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       Wx[j] = 0.0f;
       Ax[j] = 0.0f;
     }
-    for (int kb = 0; kb < num_parts; kb += MC) {
-      const int kn = min(MC, num_parts - kb);
-      __syncthreads();
-      for (int t = threadIdx.x; t < G * MC; t += NTH) {
-        const int h = t / MC, k = t % MC;
-        s_l[h][k] = k < kn ? __hip_atomic_load(a.ws_lse + (head0 + h) * num_parts + kb + k,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                           : -INFINITY;
-      }
-      __syncthreads();
+    for (int kb = 0; kb < num_parts; kb += 64) {
+      const int kn = min(64, num_parts - kb);
+      float lsev[PAIRS];
 #pragma unroll
       for (int j = 0; j < PAIRS; ++j) {
-        const int idx = threadIdx.x + j * NTH;
-        if (idx >= G * D) break;
-        const int h = idx / D;
-        const int d = idx % D;
-        const float* Op = a.ws_o + ((head0 + h) * num_parts + kb) * D + d;
-        float ov[MC];
-#pragma unroll
-        for (int k = 0; k < MC; ++k)    // rows past kn stay inside the workspace
-          ov[k] = __hip_atomic_load(const_cast<float*>(Op) + (int64_t)min(k, kn - 1) * D,
+        const int h = min((int)(threadIdx.x + j * NTH) / D, G - 1);
+        lsev[j] = __hip_atomic_load(a.ws_lse + (head0 + h) * num_parts + kb + min(lane, kn - 1),
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        float cm = -INFINITY;
+      }
+      for (int kc = 0; kc < kn; kc += MC) {
+        float ov[PAIRS][MC];
 #pragma unroll
-        for (int k = 0; k < MC; ++k) cm = fmaxf(cm, s_l[h][k]);
-        const float Mn = fmaxf(Mx[j], cm);
-        if (Mn == -INFINITY) continue;
-        const float sc = __expf(Mx[j] - Mn);          // 0 while nothing was seen
-        float W = Wx[j] * sc, A = Ax[j] * sc;
+        for (int j = 0; j < PAIRS; ++j) {
+          const int idx = min((int)threadIdx.x + j * NTH, G * D - 1);
+          const float* Op = a.ws_o + ((head0 + idx / D) * num_parts + kb) * D + idx % D;
 #pragma unroll
-        for (int k = 0; k < MC; ++k) {
-          const float lk = s_l[h][k];
-          const float w = lk == -INFINITY ? 0.0f : __expf(lk - Mn);
-          W += w;
-          A = fmaf(w, lk == -INFINITY ? 0.0f : ov[k], A);   // undefined o_k where empty
+          for (int k = 0; k < MC; ++k)    // rows past kn stay inside the workspace
+            ov[j][k] = __hip_atomic_load(const_cast<float*>(Op) + (int64_t)min(kc + k, kn - 1) * D,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        Mx[j] = Mn;
-        Wx[j] = W;
-        Ax[j] = A;
+#pragma unroll
+        for (int j = 0; j < PAIRS; ++j) {
+          float lk[MC];
+          float cm = -INFINITY;
+#pragma unroll
+          for (int k = 0; k < MC; ++k) {
+            const float v = __builtin_amdgcn_readlane(__float_as_int(lsev[j]), min(kc + k, 63));
+            lk[k] = kc + k < kn ? __int_as_float(v) : -INFINITY;
+            cm = fmaxf(cm, lk[k]);
+          }
+          const float Mn = fmaxf(Mx[j], cm);
+          if (Mn == -INFINITY) continue;
+          const float sc = __expf(Mx[j] - Mn);          // 0 while nothing was seen
+          float W = Wx[j] * sc, A = Ax[j] * sc;
+#pragma unroll
+          for (int k = 0; k < MC; ++k) {
+            const float w = lk[k] == -INFINITY ? 0.0f : __expf(lk[k] - Mn);
+            W += w;
+            A = fmaf(w, lk[k] == -INFINITY ? 0.0f : ov[j][k], A);   // undefined o_k where empty
+          }
+          Mx[j] = Mn;
+          Wx[j] = W;
+          Ax[j] = A;
+        }
       }
     }
 #pragma unroll
@@ -601,7 +684,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
 template <int D, int G, typename IT, Mode MODE>
 static int launch_mode(const KernelArgs& a, hipStream_t s) {
   constexpr int NW = GQA_MFMA_NW;
-  const dim3 grid(MODE == Mode::Final ? 1 : a.num_parts, a.Hkv, a.B);
+  const dim3 grid((MODE == Mode::Final ? 1 : a.num_parts) * a.B * a.Hkv);
   hipLaunchKernelGGL((attn_decode_mfma_kernel<D, G, NW, IT, MODE>), grid, dim3(NW * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
