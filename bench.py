@@ -1,18 +1,23 @@
 """Decode-attention benchmark on one MI355X.
 
 One step = one pass of the whole decode hot path over one batch: the fused
-prologue (QK-RMSNorm + NeoX RoPE + K/V append), the split-K attention pass,
-and the log-sum-exp merge, each one C-ABI call on torch's current stream,
-with every input already resident in HBM.  Before each timed step, a
-read-only sweep of a 1 GiB buffer evicts the KV window from the L2s and the
+prologue (QK-RMSNorm + NeoX RoPE + K/V append), the split-K attention pass
+and the log-sum-exp merge.  By default (--mode fused) that is one C-ABI call,
+gqa_decode_step, i.e. one kernel launch; --mode split makes it three calls
+(prologue, split-K pass, merge).  Every launch goes to torch's current
+stream and every input is already resident in HBM.  Before each timed step,
+a read-only sweep of a 1 GiB buffer evicts the KV window from the L2s and the
 256 MB Infinity Cache so it is read from HBM (outside the timed region).
 
 Prints ONE JSON line.  ``value`` is the step's KV-read throughput: KV-cache
 bytes the step must read (K and V rows of every attended window, bf16) per
 second of whole-step time, in GB/s.  ``roofline`` rates the dominant kernel
-(the split-K attention pass) against MI355X's 8 TB/s HBM peak, with its
-duration from HIP events on the launch stream.  ``cpu_baseline`` times the
-fp64 CPU oracle on the same workload on this host.
+(the fused step kernel, or the split-K pass with --mode split) against
+MI355X's 8 TB/s HBM peak, with its duration from HIP events (created without
+the system-scope fence) recorded on the launch stream around the kernel;
+``traffic`` is the measured HBM bytes per launch from committed rocprofv3
+counters when they were taken on the current kernel source.
+``cpu_baseline`` times the fp64 CPU oracle on the same workload on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
 """
@@ -137,6 +142,53 @@ def _record_traffic(workload: str, fetch_dir: str, write_dir: str):
     print(json.dumps(rec))
 
 
+class _HipEvents:
+    """Timing events of the HIP runtime torch has loaded, created without the
+    system-scope release (hipEventDisableSystemFence), which costs several
+    microseconds per record; recorded on the stream the kernels run on."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, count: int):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self._c = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i: int, stream: int):
+        if self.hip.hipEventRecord(self.ev[i], self._c.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i: int, j: int) -> float:
+        t = self._c.c_float()
+        if self.hip.hipEventElapsedTime(self._c.byref(t), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
 def _cpu_baseline(w, min_seconds: float):
     """Time the fp64 oracle's decode step on this host (a baseline, not a target)."""
     import threadpoolctl
@@ -150,7 +202,7 @@ def _cpu_baseline(w, min_seconds: float):
         oracle.decode_step(w, split=False)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= min_seconds or reps >= 20:
+        if el >= min_seconds:
             break
     kvb = workloads.kv_bytes(w)
     return {
@@ -203,46 +255,42 @@ def main():
         elif args.flush == "rmw":
             flush.add_(1)
 
-    def one_step(evs=None):
+    stream = torch.cuda.current_stream(dev).cuda_stream   # every launch goes here
+    timer = _HipEvents(4 * args.steps)
+
+    def one_step(i=None):
         sweep()
-        if evs is not None:
-            evs[0].record()
+        rec = (lambda k: timer.record(4 * i + k, stream)) if i is not None else (lambda k: None)
+        rec(0)
         if mode == "fused":      # one launch: bracket it with one event pair only
             step.fused()
-            if evs is not None:
-                evs[3].record()
+            rec(3)
             return
         step.prologue()
-        if evs is not None:
-            evs[1].record()
+        rec(1)
         step.attention()
-        if evs is not None:
-            evs[2].record()
+        rec(2)
         step.merge()
-        if evs is not None:
-            evs[3].record()
+        rec(3)
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        one_step(evs[i])
+        one_step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    step_ms = [timer.ms(4 * i, 4 * i + 3) for i in range(args.steps)]
     if mode == "fused":      # one kernel: the step is the dominant kernel
         pro_ms = merge_ms = [0.0]
         attn_ms = step_ms
     else:
-        pro_ms = [e[0].elapsed_time(e[1]) for e in evs]
-        attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
-        merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+        pro_ms = [timer.ms(4 * i, 4 * i + 1) for i in range(args.steps)]
+        attn_ms = [timer.ms(4 * i + 1, 4 * i + 2) for i in range(args.steps)]
+        merge_ms = [timer.ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]
+    timer.close()
     mean_step = statistics.fmean(step_ms)
     mean_attn = statistics.fmean(attn_ms)
     value = kvb / (mean_step * 1e-3) / 1e9
