@@ -26,6 +26,9 @@ int check_shapes(int B, int Hq, int Hkv, int D, int T) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || T < 1) return GQA_ERR_SHAPE;
   if (Hq % Hkv != 0) return GQA_ERR_SHAPE;
   if ((int64_t)B * Hkv * T > kMaxIndex / D) return GQA_ERR_SHAPE;
+  // the attention kernels address one (sequence, KV head) slab of T rows
+  // with 32-bit byte offsets
+  if ((int64_t)T * D * 2 > (int64_t)UINT32_MAX) return GQA_ERR_SHAPE;
   if ((int64_t)B * Hq > kMaxWorkgroups) return GQA_ERR_SHAPE;
   if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
   if (!group_ok(Hq / Hkv)) return GQA_ERR_UNSUPPORTED;

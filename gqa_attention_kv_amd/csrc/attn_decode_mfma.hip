@@ -17,8 +17,8 @@
 //
 // Why matrix cores.  Per cached row the G heads need 2*G*D multiply-adds;
 // at G = 8 the VALU form costs more issue cycles per row than HBM needs to
-// deliver it at 6.4 TB/s.  Both contractions run on MFMA instead, leaving
-// the VALU only the bf16->fp32 widening of V and the softmax.
+// deliver it at 6.4 TB/s.  Both contractions run on bf16 MFMA instead,
+// leaving the VALU the softmax and some operand packing.
 //
 // Tiles of 16 rows.  Lane l, with n = l % 16 and g = l / 16:
 //   QK: S^T[16 rows x 16 heads] += K[16 x 32] * Q^T[32 x 16] with
@@ -29,23 +29,28 @@
 //       instructions that read whole 256-byte rows.  So K is loaded like V,
 //       whole rows, and passes through a wave-private LDS slab (rows padded
 //       to D*2+16 bytes: conflict-free for both the row writes and the
-//       operand reads).  q is split into bf16 hi + lo parts (two calls) so
-//       scores keep ~16 mantissa bits; a bf16 q needs the hi call only.
-//       Heads >= G are zero columns.  A-operand row m is fed tile row
-//       pi(m) = 4(m%4) + m/4, so the result leaves lane l holding S for tile
-//       rows 4r + g (r < 4) of head n.
-//   PV: O[16 heads x 16 cols] += P[16 x 4] * V[4 x 16] with
-//       v_mfma_f32_16x16x4_f32, four calls per tile (call i takes tile rows
-//       4i..4i+3, row 4i + g in lane group g) times D/16 column blocks.
-//       P's A operand (head n, row 4i+g) is exactly the register the QK step
-//       left in lane l, so no cross-lane movement is needed.  Output column
-//       n of block b stands for d = (D/16) n + b, which makes lane l's V
-//       operand for all blocks one contiguous (D/8)-byte load of row 4i+g:
-//       a wave-wide load reads 4 consecutive rows, 1 KiB contiguous for
-//       D = 128.  fp32 keeps P and V exact.
-// Loads for tile j+1 are issued before tile j is computed (register double
-// buffer, branch-free trips of two tiles), and waves of a workgroup take
-// interleaved tiles.
+//       operand reads).  An fp32 q is split into bf16 hi + lo parts so the
+//       scores keep ~16 mantissa bits: with G <= 8 the lo parts fill columns
+//       8..15 of the same operand and one DPP step adds column n + 8 to
+//       column n; with G = 16 they take a second call.  A bf16 q needs the
+//       hi part only.  Heads >= G are zero columns.  A-operand row m is fed
+//       tile row pi(m) = 4(m%4) + m/4, so the result leaves lane l holding S
+//       for tile rows 4r + g (r < 4) of head n.
+//   PV: O[16 heads x 16 cols] += P[16 x 32] * V[32 x 16] with
+//       v_mfma_f32_16x16x32_bf16, one call per D/16 column block.  The 16
+//       tile rows become 32 k-indices, k = 8g + 2r + x for tile row 4r + g,
+//       with x = 0 carrying the bf16 hi part of P and x = 1 its lo part
+//       (P keeps ~16 mantissa bits; V is exact in bf16 and appears at both
+//       k of its row).  Lane l's P operand is the four scores the QK step
+//       left in it, so no cross-lane movement is needed.  Output column n of
+//       block b stands for d = (D/16) n + b, which makes lane l's V operand
+//       for every block one contiguous (D/8)-byte load per row: a wave-wide
+//       load reads 4 consecutive rows, 1 KiB contiguous for D = 128.
+// Each wave streams units of two tiles (32 rows): the loads of the next
+// unit's tile are issued as soon as a tile is computed (register double
+// buffer, branch-free trips), and the waves of a workgroup take
+// interleaved units.  K and V are read through buffer resources (the slab
+// base in scalar registers, 32-bit lane offsets).
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/gqa_decode.h"
@@ -53,10 +58,18 @@
 namespace gqa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;   // 16 bytes, register type
 
 enum class Mode { Final, Split, Step };
+
+// Buffer resource over `bytes` bytes from `base` (raw, unswizzled); loads
+// through it take 32-bit byte offsets and return zeros past the end.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
 
 template <int D>
 struct VRow;   // lane's slice of one V row: D/16 bf16
@@ -64,16 +77,37 @@ template <>
 struct VRow<128> {
   uint4 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void unpack(float f[8]) const { unpack8(v, f); }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ __forceinline__ uint32_t word(int w) const {
+    return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
+  }
 };
 template <>
 struct VRow<64> {
   uint2 v;
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ void unpack(float f[4]) const {
-    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
   }
+  __device__ __forceinline__ uint32_t word(int w) const { return w == 0 ? v.x : v.y; }
 };
+
+// bf16 element e of a V slice, copied into both halves of a dword.
+template <int D>
+__device__ __forceinline__ uint32_t dup_bf16(const VRow<D>& r, int e) {
+  const uint32_t w = r.word(e >> 1);
+  return __builtin_amdgcn_perm(w, w, (e & 1) ? 0x03020302u : 0x01000100u);
+}
+
+// x as a bf16 pair (hi, lo) with hi = bf16(x) and lo = bf16(x - hi): hi + lo
+// carries ~16 significant bits of x.  hi in the low half of the dword.
+__device__ __forceinline__ uint32_t split_bf16(float x) {
+  const __bf16 h = (__bf16)x;
+  const bf16x2_t v = {h, (__bf16)(x - (float)h)};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 template <typename T>
 __device__ __forceinline__ void load8f(const T* p, float f[8]);
@@ -114,35 +148,175 @@ struct TileBuf {
   VRow<D> v[4];        // V rows 4i + g, i < 4
 };
 
+// Register budget: three waves per SIMD (168 VGPRs); G = 16 keeps two q
+// operands (hi and lo) live and gets two waves (256 VGPRs) so that nothing
+// spills to scratch inside the tile loop.
 #ifndef GQA_WAVES_PER_EU
 #define GQA_WAVES_PER_EU 3
 #endif
-#ifndef GQA_STAGES
-#define GQA_STAGES 2
-#endif
+
+// The last workgroup of a (sequence, KV head) team merges the team's
+// partitions (one per member): M = max_k lse_k, w_k = e^(lse_k - M),
+// out = sum_k w_k o_k / sum_k w_k, lse = M + log sum_k w_k.  Thread t owns
+// float4 group(s) of the G*D outputs; when there are fewer groups than
+// threads, KS subsets of threads take partitions s, s + KS, ... and are
+// combined through LDS at the end.  Every order is fixed, so the result is
+// bit-identical from run to run.  Partials are read with agent-scope loads
+// (8 bytes each), which do not hit stale L2 lines; a batch of up to MB
+// partitions is one memory round trip.
+template <int D, int G, int NW>
+__device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head0) {
+  constexpr int NTH = NW * 64;
+  constexpr int NG = G * D / 4;                 // float4 output groups
+  constexpr int GPT = NG > NTH ? NG / NTH : 1;  // groups per thread
+  constexpr int TPS = NG < NTH ? NG : NTH;      // threads per partition subset
+  constexpr int KS = NTH / TPS;                 // partition subsets
+  constexpr int MB = 16 / GPT;                  // partitions per batch
+  const int num_parts = a.num_parts;
+  const int t = threadIdx.x;
+  const int s = t / TPS;
+  float Mx[GPT], Wx[GPT];
+  float Ax[GPT][4];
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    Mx[j] = -INFINITY;
+    Wx[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ax[j][e] = 0.0f;
+  }
+  for (int k0 = s; k0 < num_parts; k0 += KS * MB) {
+    float lk[GPT][MB];
+    uint64_t ov[GPT][MB][2];
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      const int gi = t % TPS + j * TPS;
+      const int h = gi / (D / 4);
+      const int d4 = gi % (D / 4);
+      const float* Lh = a.ws_lse + (head0 + h) * num_parts;
+      const float* Oh = a.ws_o + (head0 + h) * num_parts * D + 4 * d4;
+#pragma unroll
+      for (int k = 0; k < MB; ++k) {
+        const int kk = k0 + k * KS;
+        lk[j][k] = -INFINITY;
+        ov[j][k][0] = ov[j][k][1] = 0;
+        if (kk < num_parts) {
+          lk[j][k] = __hip_atomic_load(Lh + kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t* op = reinterpret_cast<const uint64_t*>(Oh + (int64_t)kk * D);
+          ov[j][k][0] = __hip_atomic_load(op, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ov[j][k][1] = __hip_atomic_load(op + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      float cm = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < MB; ++k) cm = fmaxf(cm, lk[j][k]);
+      const float Mn = fmaxf(Mx[j], cm);
+      if (Mn == -INFINITY) continue;
+      const float sc = __expf(Mx[j] - Mn);          // 0 while nothing was seen
+      float W = Wx[j] * sc;
+      float A[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) A[e] = Ax[j][e] * sc;
+#pragma unroll
+      for (int k = 0; k < MB; ++k) {
+        // an empty partition (lse = -inf) has weight 0 and an undefined o_k
+        const bool ok = lk[j][k] != -INFINITY;
+        const float w = ok ? __expf(lk[j][k] - Mn) : 0.0f;
+        const float o4[4] = {__uint_as_float((uint32_t)ov[j][k][0]),
+                             __uint_as_float((uint32_t)(ov[j][k][0] >> 32)),
+                             __uint_as_float((uint32_t)ov[j][k][1]),
+                             __uint_as_float((uint32_t)(ov[j][k][1] >> 32))};
+        W += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) A[e] = fmaf(w, ok ? o4[e] : 0.0f, A[e]);
+      }
+      Mx[j] = Mn;
+      Wx[j] = W;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ax[j][e] = A[e];
+    }
+  }
+  if constexpr (KS > 1) {   // GPT == 1: combine the subsets in ascending order
+    __shared__ float sm_mx[NTH], sm_wx[NTH];
+    __shared__ float4 sm_ax[NTH];
+    sm_mx[t] = Mx[0];
+    sm_wx[t] = Wx[0];
+    sm_ax[t] = make_float4(Ax[0][0], Ax[0][1], Ax[0][2], Ax[0][3]);
+    __syncthreads();
+    if (t >= TPS) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) M = fmaxf(M, sm_mx[q * TPS + t]);
+    float W = 0.0f, A[4] = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        const float f = __expf(sm_mx[q * TPS + t] - M);
+        const float4 av = sm_ax[q * TPS + t];
+        W = fmaf(sm_wx[q * TPS + t], f, W);
+        A[0] = fmaf(av.x, f, A[0]);
+        A[1] = fmaf(av.y, f, A[1]);
+        A[2] = fmaf(av.z, f, A[2]);
+        A[3] = fmaf(av.w, f, A[3]);
+      }
+    }
+    Mx[0] = M;
+    Wx[0] = W;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ax[0][e] = A[e];
+  }
+#pragma unroll
+  for (int j = 0; j < GPT; ++j) {
+    const int gi = t % TPS + j * TPS;
+    const int h = gi / (D / 4);
+    const int d4 = gi % (D / 4);
+    const bool any = Wx[j] > 0.0f;
+    float ov[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ov[e] = any ? Ax[j][e] / Wx[j] : 0.0f;
+    const int64_t oi = (head0 + h) * D + 4 * d4;
+    if (a.out_bf16) {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
+          make_uint2(pack2(f32_to_bf16(ov[0]), f32_to_bf16(ov[1])),
+                     pack2(f32_to_bf16(ov[2]), f32_to_bf16(ov[3])));
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
+          make_float4(ov[0], ov[1], ov[2], ov[3]);
+    }
+    if (d4 == 0 && a.lse_out != nullptr)
+      a.lse_out[head0 + h] = any ? Mx[j] + logf(Wx[j]) : -INFINITY;
+  }
+}
 
 template <int D, int G, int NW, typename IT, Mode MODE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQA_WAVES_PER_EU))) void
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(G >= 16 ? 2 : GQA_WAVES_PER_EU))) void
 attn_decode_mfma_kernel(const KernelArgs a) {
   static_assert(G <= 16, "one 16-column MFMA tile holds at most 16 heads");
   constexpr int KC = D / 32;          // QK calls per tile (per q part)
   constexpr int VB = D / 16;          // PV column blocks
   constexpr int HALF = D / 2;
+  constexpr int UR = 32;              // rows per unit of work: two 16-row tiles
   // fp32 q (given, or the prologue's rotated q) needs the lo part
   constexpr bool kLo = sizeof(IT) == 4 || MODE == Mode::Step;
+  // With at most 8 heads the lo part takes columns 8..15 of the same
+  // operand (column n + 8 holds head n's lo part) instead of a second call.
+  constexpr bool kFold = kLo && G <= 8;
   constexpr bool kPartial = MODE != Mode::Final;
 
   // One-dimensional grid.  The hardware hands workgroup i to XCD i % 8.
   // With 8 or more partitions per (sequence, KV head) the partition index
   // runs fastest, so consecutive partitions of one sequence land on
-  // consecutive XCDs.  With fewer, it runs slowest: workgroup i takes
-  // partition i / (B*Hkv) of (sequence, KV head) i % (B*Hkv), so every XCD
-  // gets the same mix of partitions -- partition 0 of every sequence is the
-  // one that is never empty under ragged lengths -- and the dispatcher
-  // starts all first partitions before any later one.  (Partition-fastest
-  // order with few partitions puts every partition 0 on the same two XCDs;
-  // partition-major order with many partitions per sequence measured slower
-  // and sensitive to where the K and V caches sit relative to each other.)
+  // consecutive XCDs and the workgroups in flight read one stretch of the
+  // cache.  With fewer, it runs slowest: workgroup i takes partition
+  // i / (B*Hkv) of (sequence, KV head) i % (B*Hkv), so every XCD gets the
+  // same mix of partitions -- partition 0 of every sequence is the one that
+  // is never empty under ragged lengths -- and the dispatcher starts all
+  // first partitions before any later one.  (Partition-slowest order with
+  // many partitions puts partitions of every sequence in flight at once,
+  // streams 32 MiB or more apart, and measured slower and sensitive to where
+  // the K and V caches sit relative to each other.)
   const int nbg = a.B * a.Hkv;
   const int npg = MODE == Mode::Final ? 1 : a.num_parts;
   int part, bg;
@@ -166,6 +340,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
 
   const int nrow = min(max(a.lens[b], 0), T);
   const int lo = a.window > 0 ? max(0, nrow - a.window) : 0;
+  // Rows this workgroup attends: the whole range, or its partition.
   int t0 = lo, t1 = nrow;
   if (kPartial) {
     t0 = min(lo + part * a.part_tokens, nrow);
@@ -198,8 +373,12 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   constexpr int ROWU4 = PPR + 1;        // padded LDS row, in 16-byte units
   const int kp = lane % PPR;
   const int kr = lane / PPR;
-  const uint16_t* Kbase = a.k_cache + slab_off + 8 * kp;        // + row*D
-  const uint16_t* Vbase = a.v_cache + slab_off + VB * n;        // + row*D
+  // This (sequence, KV head)'s T x D slab of each cache, as a buffer
+  // resource: T * D * 2 < 2^32 bytes (checked on the host).
+  const __amdgpu_buffer_rsrc_t Krs = make_rsrc(a.k_cache + slab_off, (uint32_t)T * D * 2u);
+  const __amdgpu_buffer_rsrc_t Vrs = make_rsrc(a.v_cache + slab_off, (uint32_t)T * D * 2u);
+  const uint32_t koff = 16u * kp;          // + row * 2D bytes
+  const uint32_t voff = 2u * VB * n;
   __shared__ u32x4_t sk[NW][16][ROWU4];
   u32x4_t* slab = &sk[wave][0][0];
 
@@ -209,48 +388,58 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   // the loads the compiler can count them exactly and wait only for the tile
   // being computed.
   const int rlast = max(t1 - 1, 0);
-  auto issue_from = [&](TileBuf<D>& buf, int base, const uint16_t* kb, const uint16_t* vb,
-                        int rstride) {
+  auto issue = [&](TileBuf<D>& buf, int base) {
 #pragma unroll
     for (int i = 0; i < 16 / RPI; ++i) {
-      const int rk = min(base + RPI * i + kr, rlast);
-      buf.k[i] = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)rk * rstride);
+      const uint32_t rk = (uint32_t)min(base + RPI * i + kr, rlast);
+      buf.k[i] = __builtin_amdgcn_raw_buffer_load_b128(Krs, rk * (2u * D) + koff, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rv = min(base + 4 * i + lg, rlast);
-      buf.v[i].load(vb + (int64_t)rv * rstride);
+      const uint32_t rv = (uint32_t)min(base + 4 * i + lg, rlast);
+      buf.v[i].load(Vrs, rv * (2u * D) + voff);
     }
   };
-  auto issue = [&](TileBuf<D>& buf, int base) { issue_from(buf, base, Kbase, Vbase, D); };
 
-  constexpr int STEP = NW * 16;
-  constexpr int S = GQA_STAGES;        // register tile buffers
-  int base = t0 + wave * 16;
-  TileBuf<D> bf[S];
-  auto prime = [&]() {                 // the S tiles of the first trip
-#pragma unroll
-    for (int s = 0; s < S; ++s) issue(bf[s], base + s * STEP);
+  // Units of UR rows: wave w takes units w, w + NW, w + 2 NW, ... of the
+  // workgroup's range.
+  auto unit_row = [&](int64_t u) -> int {
+    return (int)min((int64_t)t0 + (int64_t)UR * u, (int64_t)t1);
+  };
+  int64_t ustep = wave;
+  int rcur = unit_row(ustep);
+
+  TileBuf<D> bf[2];
+  auto prime = [&]() {
+    issue(bf[0], rcur);
+    issue(bf[1], rcur + 16);
   };
 
-  // q for head n (padding columns n >= G load head G-1 -- no branch around
-  // the loads -- and are zeroed): lane holds elements 32c + 8lg + j.
-  const float keep = n < G ? 1.0f : 0.0f;
-  const int hq = min(n, G - 1);
+  // q for head hn = n (n % 8 when folded; padding columns hn >= G load head
+  // G-1 -- no branch around the loads -- and are zeroed): lane holds
+  // elements 32c + 8lg + j.
+  const int hn = kFold ? (n & 7) : n;
+  const float keep = hn < G ? 1.0f : 0.0f;
+  const int hq = min(hn, G - 1);
   float qf[KC][8];
+  // Step: the appended row (bf16 K row, then V row, per wave), substituted
+  // into the one tile that holds row psub.
+  __shared__ u32x4_t snew[NW][2][PPR];
+  int psub = -1;
 
   if constexpr (MODE == Mode::Step) {
     // ---- fused prologue: QK-RMSNorm, NeoX RoPE at pos[b], K/V append ----
     // (skipped when no prologue inputs are given: q is then used as is)
     const bool has_pro = a.pos != nullptr;
     const int p = has_pro ? a.pos[b] : -1;
-    // The row pos[b] is written by the workgroup whose partition attends it
-    // (or partition 0 when it is not attended); positions outside [0, T)
-    // write nothing.  No other workgroup reads that row.
+    // Partition 0 writes row pos[b] of the cache; positions outside [0, T)
+    // write nothing.  The workgroup whose partition attends that row uses
+    // the values it computes itself in place of loading it, so no
+    // workgroup waits for the write.
     const bool in_range = has_pro && p >= 0 && p < T;
-    const bool attended = p >= lo && p < nrow;
-    const bool writer = in_range && (attended ? (p >= t0 && p < t1) : part == 0);
-    const bool reads_row = writer && attended;
+    const bool attended = has_pro && p >= t0 && p < t1;
+    const bool kwrite = in_range && part == 0 && wave == 0;
+    const bool need_k = attended || kwrite;
     // Every global load of the prologue is issued before the first tiles:
     // loads complete in order, so waiting for these never waits for a tile.
     const IT* qs = reinterpret_cast<const IT*>(a.q) + (int64_t)b * a.q_bstride +
@@ -266,11 +455,10 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
     const int fi = lane % HALF;               // rotary frequency index of this lane
     const double inv_rev = rope ? a.inv_freq_rev[fi] : 0.0;
-    const bool kwrite = writer && wave == 0;
     // raw values: converted only after the tiles are issued
     IT rx0 = 0, rx1 = 0, rv0 = 0, rv1 = 0;
     float wk0 = 1.0f, wk1 = 1.0f;
-    if (kwrite) {
+    if (need_k) {
       const IT* ks = reinterpret_cast<const IT*>(a.k_new) + (int64_t)b * a.kv_bstride +
                      (int64_t)g * D;
       const IT* vs = reinterpret_cast<const IT*>(a.v_new) + (int64_t)b * a.kv_bstride +
@@ -285,22 +473,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // A writer whose appended row falls in the first tiles issues them only
-    // after the append; until then its buffers are filled from its own q row
-    // (same number of loads, so the compiler still counts them exactly, and
-    // every lane's pieces stay inside that row: it holds D elements of at
-    // least 2 bytes).  Otherwise no primed row is the appended one: a
-    // partition holding pos past its first S tiles has more rows than those
-    // tiles cover, so none of their rows is clamped.
-    const bool late = reads_row && (p - t0) < S * STEP;
-    {
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(qs);
-      const uint16_t* kb = late ? qrow + 8 * kp : Kbase;
-      const uint16_t* vb = late ? qrow + VB * n : Vbase;
-      const int rs = late ? 0 : D;
-#pragma unroll
-      for (int s2 = 0; s2 < S; ++s2) issue_from(bf[s2], base + s2 * STEP, kb, vb, rs);
-    }
+    prime();
     __builtin_amdgcn_sched_barrier(0);
     // Rotary angle of frequency index fi: the phase p * theta^(-2fi/D) / (2 pi)
     // is formed and reduced in float64 from a host-computed table, leaving a
@@ -311,7 +484,11 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       const double fr = rev - rint(rev);
       sincosf((float)(fr * 6.283185307179586), &sn, &cs);
     }
-    if (kwrite) {
+    // Angles and the new K row cross lanes through this wave's LDS slab (in
+    // order within the wave; each asm hides an index from per-lane alias
+    // analysis, so the compiler keeps program order).
+    float* af = reinterpret_cast<float*>(slab);
+    if (need_k) {
       float x0 = to_f32(rx0), x1 = to_f32(rx1);
       if (a.wk != nullptr) {
         const float ss = group_sum_shfl<HALF>(x0 * x0 + x1 * x1);
@@ -324,15 +501,26 @@ attn_decode_mfma_kernel(const KernelArgs a) {
         x0 = y0;
         x1 = y1;
       }
-      if (lane < HALF) {
+      const uint16_t k0 = f32_to_bf16(x0), k1 = f32_to_bf16(x1);
+      const uint16_t v0 = bits_bf16(&rv0, 0), v1 = bits_bf16(&rv1, 0);
+      if (kwrite && lane < HALF) {
         uint16_t* krow = a.k_cache_w + slab_off + (int64_t)p * D;
         uint16_t* vrow = a.v_cache_w + slab_off + (int64_t)p * D;
-        krow[fi] = f32_to_bf16(x0);
-        krow[fi + HALF] = f32_to_bf16(x1);
-        vrow[fi] = bits_bf16(&rv0, 0);
-        vrow[fi + HALF] = bits_bf16(&rv1, 0);
+        krow[fi] = k0;
+        krow[fi + HALF] = k1;
+        vrow[fi] = v0;
+        vrow[fi + HALF] = v1;
       }
-      if (reads_row) __threadfence_block();   // the row is visible before the barrier
+      if (attended && lane < HALF) {
+        uint16_t* kh = reinterpret_cast<uint16_t*>(&snew[wave][0][0]);
+        int kidx = fi;
+        asm volatile("" : "+v"(kidx));
+        kh[kidx] = k0;
+        kh[kidx + HALF] = k1;
+        kh[D + kidx] = v0;
+        kh[D + kidx + HALF] = v1;
+      }
+      if (attended) psub = p;
     }
     // Query head g*G + hq: RMSNorm over D (the lane's D/4 elements, summed
     // over the four lane groups of head n), then RoPE: element e < D/2 of
@@ -352,9 +540,6 @@ attn_decode_mfma_kernel(const KernelArgs a) {
         for (int j = 0; j < 8; ++j) qf[c][j] = qf[c][j] * r * wq8[c][j];
     }
     if (rope) {
-      // Hand the angles across lanes through this wave's LDS slab (in-order
-      // LDS; the asm hides the indices from per-lane alias analysis).
-      float* af = reinterpret_cast<float*>(slab);
       int aidx = fi;
       asm volatile("" : "+v"(aidx));
       if (lane < HALF) {
@@ -387,10 +572,6 @@ attn_decode_mfma_kernel(const KernelArgs a) {
             make_float4(qf[c][4], qf[c][5], qf[c][6], qf[c][7]);
       }
     }
-    if (reads_row) {
-      __syncthreads();                  // appended row written before it is loaded
-      if (late) prime();
-    }
   } else {
     // The q loads go out first and the first tiles right behind them, so
     // waiting for q never waits for a tile (loads complete in order).
@@ -406,8 +587,10 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       for (int j = 0; j < 8; ++j) qf[c][j] *= keep;
   }
 
-  // Q^T operand: bf16 hi (+ lo) parts of q[head n][32c + 8lg .. +8].
+  // Q^T operand: bf16 hi (+ lo) parts of q[head hn][32c + 8lg .. +8]; when
+  // folded, columns n >= 8 take the lo part into qhi.
   uint4 qhi[KC], qlo[KC];
+  const bool lo_col = kFold && n >= 8;
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
     uint16_t h16[8], l16[8];
@@ -415,6 +598,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     for (int j = 0; j < 8; ++j) {
       h16[j] = f32_to_bf16(qf[c][j]);
       l16[j] = f32_to_bf16(qf[c][j] - bf16_to_f32(h16[j]));
+      if (lo_col) h16[j] = l16[j];
     }
     qhi[c] = make_uint4(pack2(h16[0], h16[1]), pack2(h16[2], h16[3]),
                         pack2(h16[4], h16[5]), pack2(h16[6], h16[7]));
@@ -429,7 +613,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   for (int blk = 0; blk < VB; ++blk) o[blk] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const float qscale = a.qscale;
 
-  auto compute = [&](const TileBuf<D>& buf, int base) {
+  auto compute = [&](TileBuf<D>& buf, int base) {
     // K rows -> LDS -> A operand (row pi(n), elements 32c + 8lg .. +8).  The
     // slab is private to the wave and the hardware runs one wave's LDS
     // operations in order, so no barrier is needed.  But the data crosses
@@ -443,6 +627,22 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     asm volatile("" : "+v"(widx));
 #pragma unroll
     for (int i = 0; i < 16 / RPI; ++i) slab[widx + RPI * i * ROWU4] = buf.k[i];
+    // The appended row (Step only) replaces whatever was loaded for it, in
+    // the slab (K) and in the registers (V): a wave-uniform test, taken for
+    // at most one tile of the range.
+    const int dp = psub - base;
+    if ((unsigned)dp < 16u) {
+      int cidx = dp * ROWU4 + lane;
+      asm volatile("" : "+v"(cidx));
+      if (lane < PPR) slab[cidx] = snew[wave][0][lane];
+      int vidx = VB * n;
+      asm volatile("" : "+v"(vidx));
+      VRow<D> vn;
+      vn.load(reinterpret_cast<const uint16_t*>(&snew[wave][1][0]) + vidx);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * r + lg == dp) buf.v[r] = vn;
+    }
     int ridx = (4 * (n & 3) + (n >> 2)) * ROWU4 + lg;
     asm volatile("" : "+v"(ridx));
     u32x4_t ka[KC];
@@ -454,10 +654,16 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[c]),
                                                   __builtin_bit_cast(bf16x8_t, qhi[c]), s,
                                                   0, 0, 0);
-      if constexpr (kLo)
+      if constexpr (kLo && !kFold)
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka[c]),
                                                     __builtin_bit_cast(bf16x8_t, qlo[c]), s,
                                                     0, 0, 0);
+    }
+    // Folded: hi (column n) + lo (column n + 8) of head n % 8, in both lanes.
+    // Rows of heads >= G in the PV operand below are never stored.
+    if constexpr (kFold) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] += dpp<kDppRowRor8>(s[r]);
     }
     float p[4];
     float tmax = -INFINITY;
@@ -469,7 +675,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // finite: the trip's first tile always holds a valid row
+    // finite: the unit's first tile always holds a valid row
     const float mnew = fmaxf(m, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
@@ -487,35 +693,47 @@ attn_decode_mfma_kernel(const KernelArgs a) {
 #pragma unroll
       for (int blk = 0; blk < VB; ++blk) o[blk][r] *= al;
     }
+    // PV on one bf16 call per column block, with the 16 tile rows as 32
+    // k-indices: k = 8lg + 2r + x stands for tile row 4r + lg, x = 0 taking
+    // the bf16 hi part of P and x = 1 its lo part, so V (exact in bf16) is
+    // the same at both k of a row.  Lane (n, lg) already holds P[head n] of
+    // exactly those rows (the A operand) and loaded V of the same rows at
+    // columns VB n .. VB n + VB - 1 (the B operand of every block).
+    u32x4_t pa;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float vf[VB];
-      buf.v[i].unpack(vf);
+    for (int r = 0; r < 4; ++r) pa[r] = split_bf16(p[r]);
 #pragma unroll
-      for (int blk = 0; blk < VB; ++blk)
-        o[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[i], vf[blk], o[blk], 0, 0, 0);
+    for (int blk = 0; blk < VB; ++blk) {
+      u32x4_t vb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vb[r] = dup_bf16<D>(buf.v[r], blk);
+      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pa),
+                                                       __builtin_bit_cast(bf16x8_t, vb), o[blk],
+                                                       0, 0, 0);
     }
   };
 
-  // S tiles per trip, no branch inside the trip: tiles after the first may
-  // lie wholly past the range, and then every row is masked (p = 0, and
-  // alpha = 1 because the running max is already finite), which leaves the
-  // state unchanged.  As soon as tile s is computed its buffer is refilled
-  // with the tile one trip ahead, so S - 1 tiles are in flight behind each
-  // compute (and S were issued before the first).  A branch between a
-  // prefetch and its use would let the compiler sink the loads past the
-  // compute they are meant to overlap; the scheduling barriers keep the
-  // machine scheduler from doing the same.
-  if (base < t1) {
-    for (; base < t1; base += S * STEP) {
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        compute(bf[s], base + s * STEP);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(bf[s], base + (s + S) * STEP);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+  // One unit per trip, no branch inside the trip: the second tile may lie
+  // wholly past the range, and then every row is masked (p = 0, and alpha =
+  // 1 because the running max is already finite), which leaves the state
+  // unchanged.  As soon as a tile is computed its buffer is refilled with
+  // the same tile of the next unit.  A branch between a prefetch and its
+  // use would let the compiler sink the loads past the compute they are
+  // meant to overlap; the scheduling barriers keep the machine scheduler
+  // from doing the same.
+  while (rcur < t1) {
+    ustep += NW;
+    const int rnext = unit_row(ustep);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bf[0], rcur);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(bf[0], rnext);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(bf[1], rcur + 16);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(bf[1], rnext + 16);
+    __builtin_amdgcn_sched_barrier(0);
+    rcur = rnext;
   }
 
   // Sum l over the four lane groups (rows), per head n.
@@ -583,9 +801,9 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     // Arrival ticket: every workgroup of this (sequence, KV head) publishes
     // its partial, waits until those write-through stores have completed,
     // and takes a ticket; the last one reads the partials back with
-    // agent-scope loads (which do not hit stale L2 lines), merges them in
-    // ascending partition order, and resets the ticket for the next launch.
-    // No workgroup waits on another.  Agent-scope fences would write back or
+    // agent-scope loads (which do not hit stale L2 lines), merges them, and
+    // resets the ticket for the next launch.  No
+    // workgroup waits on another.  Agent-scope fences would write back or
     // invalidate a whole L2 per workgroup, which costs more than the step.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // stores completed
     __syncthreads();
@@ -598,80 +816,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    // Merge, in ascending partition order.  Thread pair j owns output (h, d);
-    // h is the same across a wave (G*D and D are multiples of 64).  The LSEs
-    // of 64 partitions sit one per lane and are read back with readlane, and
-    // each chunk of MC partials is loaded in one batch together with them,
-    // so a merge of up to MC partitions is a single memory round trip.
-    constexpr int NTH = NW * 64;
-    constexpr int PAIRS = (G * D + NTH - 1) / NTH;   // (head, d) outputs per thread
-    constexpr int MC = PAIRS >= 8 ? 4 : 32 / PAIRS;
-    float Mx[PAIRS], Wx[PAIRS], Ax[PAIRS];
-#pragma unroll
-    for (int j = 0; j < PAIRS; ++j) {
-      Mx[j] = -INFINITY;
-      Wx[j] = 0.0f;
-      Ax[j] = 0.0f;
-    }
-    for (int kb = 0; kb < num_parts; kb += 64) {
-      const int kn = min(64, num_parts - kb);
-      float lsev[PAIRS];
-#pragma unroll
-      for (int j = 0; j < PAIRS; ++j) {
-        const int h = min((int)(threadIdx.x + j * NTH) / D, G - 1);
-        lsev[j] = __hip_atomic_load(a.ws_lse + (head0 + h) * num_parts + kb + min(lane, kn - 1),
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      for (int kc = 0; kc < kn; kc += MC) {
-        float ov[PAIRS][MC];
-#pragma unroll
-        for (int j = 0; j < PAIRS; ++j) {
-          const int idx = min((int)threadIdx.x + j * NTH, G * D - 1);
-          const float* Op = a.ws_o + ((head0 + idx / D) * num_parts + kb) * D + idx % D;
-#pragma unroll
-          for (int k = 0; k < MC; ++k)    // rows past kn stay inside the workspace
-            ov[j][k] = __hip_atomic_load(const_cast<float*>(Op) + (int64_t)min(kc + k, kn - 1) * D,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-#pragma unroll
-        for (int j = 0; j < PAIRS; ++j) {
-          float lk[MC];
-          float cm = -INFINITY;
-#pragma unroll
-          for (int k = 0; k < MC; ++k) {
-            const float v = __builtin_amdgcn_readlane(__float_as_int(lsev[j]), min(kc + k, 63));
-            lk[k] = kc + k < kn ? __int_as_float(v) : -INFINITY;
-            cm = fmaxf(cm, lk[k]);
-          }
-          const float Mn = fmaxf(Mx[j], cm);
-          if (Mn == -INFINITY) continue;
-          const float sc = __expf(Mx[j] - Mn);          // 0 while nothing was seen
-          float W = Wx[j] * sc, A = Ax[j] * sc;
-#pragma unroll
-          for (int k = 0; k < MC; ++k) {
-            const float w = lk[k] == -INFINITY ? 0.0f : __expf(lk[k] - Mn);
-            W += w;
-            A = fmaf(w, lk[k] == -INFINITY ? 0.0f : ov[j][k], A);   // undefined o_k where empty
-          }
-          Mx[j] = Mn;
-          Wx[j] = W;
-          Ax[j] = A;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < PAIRS; ++j) {
-      const int idx = threadIdx.x + j * NTH;
-      if (idx >= G * D) break;
-      const int h = idx / D;
-      const int d = idx % D;
-      const bool any = Wx[j] > 0.0f;
-      const float ov = any ? Ax[j] / Wx[j] : 0.0f;
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[(head0 + h) * D + d] = f32_to_bf16(ov);
-      else reinterpret_cast<float*>(a.out)[(head0 + h) * D + d] = ov;
-      if (d == 0 && a.lse_out != nullptr)
-        a.lse_out[head0 + h] = any ? Mx[j] + logf(Wx[j]) : -INFINITY;
-    }
+    merge_partials<D, G, NW>(a, head0);
     if (threadIdx.x == 0)
       __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

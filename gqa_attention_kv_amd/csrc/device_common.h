@@ -41,6 +41,7 @@ enum : int {
   kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
   kDppHalfMirror = 0x141, // lane i <- lane 7-i inside each 8-lane half row
   kDppMirror = 0x140,     // lane i <- lane 15-i inside each 16-lane row
+  kDppRowRor8 = 0x128,    // lane i <- lane i^8 inside each 16-lane row (rotate by 8)
 };
 
 template <int CTRL>

@@ -130,6 +130,14 @@ class DeviceStep:
                     k_norm_w=self.w_k, eps=w.eps, rope_theta=w.theta, window=w.window,
                     scale=self.scale, out=self.out, lse_out=self.lse, q_out=self.q)
 
+    def ws_counters(self) -> torch.Tensor:
+        """The fused step's arrival tickets (int32 view of the workspace
+        tail, [B*Hkv]); they are zero between calls."""
+        w = self.w
+        base = splitk_workspace_bytes(w.B, w.Hq, w.D, w.T, w.window, self.part_tokens)
+        off = base + (-base) % 256
+        return self.ws[off:off + 4 * w.B * w.Hkv].view(torch.int32)
+
     def run(self):
         if self.mode == "fused":
             self.fused()

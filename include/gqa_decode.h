@@ -28,7 +28,9 @@
  *     (element (b,g,t,d) at ((b*Hkv+g)*T+t)*D+d), outputs [B,Hq,D],
  *     lse [B,Hq].  Query head h uses KV head h / (Hq/Hkv).
  *   - Outputs must not alias inputs.
- *   - Supported: D in {64, 128}; G = Hq/Hkv in {1, 2, 4, 8, 16}.
+ *   - Supported: D in {64, 128}; G = Hq/Hkv in {1, 2, 4, 8, 16}; one
+ *     (sequence, KV head) slab of the cache below 4 GiB (T * D * 2 bytes
+ *     < 2^32, i.e. T < 16,777,216 rows at D = 128), else GQA_ERR_SHAPE.
  *   - Errors: arguments are checked on the host before anything is
  *     enqueued; on error the call returns a negative status and enqueues
  *     nothing.  A launch failure reported by HIP returns GQA_ERR_LAUNCH.
@@ -169,10 +171,11 @@ int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
  * flash-decoding split): the effect of gqa_qkv_prologue followed by
  * gqa_attn_decode_splitk and gqa_attn_decode_merge, with q_out optional.
  * Each (partition, KV head, sequence) workgroup rotates the new query
- * itself; the workgroup whose partition holds row pos[b] (partition 0 when
- * that row is not attended) computes and writes the appended K/V row before
- * reading it; the last workgroup of each (sequence, KV head) to finish
- * merges the partitions in ascending order.  Rotary angles are reduced in
+ * itself and writes its partition's partial (o, lse); the last workgroup of
+ * each (sequence, KV head) to finish merges the partials in a fixed order,
+ * so reruns are bit-identical.  The workgroup whose partition attends row
+ * pos[b] computes the appended K/V row and uses it in place of reading that
+ * row; partition 0 writes it to the cache.  Rotary angles are reduced in
  * float64 (a host-computed theta^(-2i/D) table) before a float32 sincos.
  *
  * Arguments are those of the three calls it replaces, plus:

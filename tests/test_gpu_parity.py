@@ -295,6 +295,8 @@ def test_prologue_fp32_inputs_and_packed_qkv(gpu):
 
 
 def test_bit_identical_reruns(gpu):
+    # Every order is fixed (partitions, the merge, no float atomics): reruns
+    # are bit-identical in all three modes.
     import torch
     for name, over, mode in (("5", dict(B=2, L=3000, window=1000), "split"),
                              ("3", dict(B=4, L=2000), "split"),
@@ -309,6 +311,21 @@ def test_bit_identical_reruns(gpu):
         for _ in range(3):
             step.run()
             assert torch.equal(step.out, a[0]) and torch.equal(step.lse, a[1])
+
+
+def test_fused_leaves_tickets_zero(gpu):
+    # Every fused call leaves the arrival tickets at zero for the next one
+    # (a stale ticket would make the wrong workgroup merge, or none).
+    import torch
+    for name, over in (("5", dict(B=2, L=3000, window=1000)), ("3", dict(B=4, L=2000)),
+                       ("4", dict(L=20000))):
+        w = W.make(name, **over)
+        _say(f"fused tickets cfg {name}")
+        step = gpu.DeviceStep(w, mode="fused", part_tokens=256, out_dtype="f32")
+        for _ in range(3):
+            step.run()
+            torch.cuda.synchronize()
+            assert int(step.ws_counters().abs().sum().item()) == 0
 
 
 def test_split_matches_unsplit(gpu):
