@@ -7,8 +7,9 @@ status.  Every step of the computation runs in the library's HIP kernels;
 there is no fallback.  Importing fails loudly when the library is missing.
 
 Functions follow the C entry points' names without the ``gqa_`` prefix:
-``qkv_prologue``, ``attn_decode``, ``attn_decode_splitk``,
-``attn_decode_merge``, ``decode_step``, ``splitk_workspace_bytes``,
+``qkv_prologue``, ``qkv_prologue_ex``, ``attn_decode``,
+``attn_decode_splitk``, ``attn_decode_merge``, ``decode_step``,
+``decode_step_ex``, ``rope_table``, ``splitk_workspace_bytes``,
 ``decode_step_workspace_bytes``, ``num_partitions``.
 """
 from __future__ import annotations
@@ -22,12 +23,15 @@ import torch
 from ._build import LIB_PATH
 
 __all__ = [
-    "GQAError", "lib", "qkv_prologue", "attn_decode", "attn_decode_splitk",
-    "attn_decode_merge", "splitk_workspace_bytes", "num_partitions",
-    "decode_step", "decode_step_workspace_bytes", "F32", "BF16", "SYMBOLS",
+    "GQAError", "lib", "qkv_prologue", "qkv_prologue_ex", "attn_decode",
+    "attn_decode_splitk", "attn_decode_merge", "splitk_workspace_bytes", "num_partitions",
+    "decode_step", "decode_step_ex", "decode_step_workspace_bytes", "rope_table",
+    "F32", "BF16", "SYMBOLS", "ROPE_NEOX", "ROPE_INTERLEAVED", "ROPE_KINDS",
 ]
 
 F32, BF16 = 0, 1
+ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
+ROPE_KINDS = {"default": 0, "linear": 1, "ntk": 2, "yarn": 3}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -57,6 +61,12 @@ SYMBOLS = {
     "gqa_decode_step": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _d, _p, _p, _p, _p,
                              _i, _f, _i, _p, _sz, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
     "gqa_status_string": (ctypes.c_char_p, [_i]),
+    "gqa_rope_table": (_i, [_i, _i, _d, _d, _i, _d, _d, _p, _p]),
+    "gqa_qkv_prologue_ex": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _p,
+                                 _p, _p, _i, _i, _i, _i, _i, _p]),
+    "gqa_decode_step_ex": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _p,
+                                _p, _p, _i, _f, _i, _p, _sz, _p, _i, _p, _p, _i, _i, _i, _i,
+                                _i, _p]),
 }
 for _name, (_res, _args) in SYMBOLS.items():
     _fn = getattr(lib, _name)
@@ -113,6 +123,38 @@ def splitk_workspace_bytes(B: int, Hq: int, D: int, T: int, window: int,
     return int(lib.gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens))
 
 
+def rope_table(kind: str, D: int, theta: float, factor: float = 1.0, orig_ctx: int = 0,
+               beta_fast: float = 32.0, beta_slow: float = 1.0):
+    """Host table of rotary frequencies for a scheme ("default", "linear",
+    "ntk", "yarn"): returns (float64 numpy array [D/2], mscale)."""
+    import numpy as np
+    f = np.zeros(D // 2, dtype=np.float64)
+    m = ctypes.c_double(0.0)
+    _check(lib.gqa_rope_table(ROPE_KINDS[kind], int(D), float(theta), float(factor),
+                              int(orig_ctx), float(beta_fast), float(beta_slow),
+                              f.ctypes.data, ctypes.addressof(m)))
+    return f, m.value
+
+
+def _host_table(inv_freq, D):
+    """A host float64 [D/2] array for the C ABI (kept alive by the caller)."""
+    import numpy as np
+    if inv_freq is None:
+        return None
+    f = np.ascontiguousarray(np.asarray(inv_freq, dtype=np.float64))
+    if f.shape != (D // 2,):
+        raise ValueError(f"inv_freq must have D/2 = {D // 2} entries")
+    return f
+
+
+def _layout_code(layout) -> int:
+    if layout in (ROPE_NEOX, "neox"):
+        return ROPE_NEOX
+    if layout in (ROPE_INTERLEAVED, "interleaved"):
+        return ROPE_INTERLEAVED
+    raise ValueError(f"unknown RoPE layout {layout!r}")
+
+
 def qkv_prologue(q, k_new, v_new, pos, k_cache, v_cache, q_norm_w=None, k_norm_w=None,
                  eps: float = 1e-6, rope_theta: float = 0.0, q_out=None):
     """QK-RMSNorm + NeoX RoPE at pos[b] + append of k/v at row pos[b].
@@ -122,6 +164,33 @@ def qkv_prologue(q, k_new, v_new, pos, k_cache, v_cache, q_norm_w=None, k_norm_w
     pos int32 [B]; caches bfloat16 [B,Hkv,T,D] (written in place);
     norm weights float32 [D] or None.  Returns q_out float32 [B,Hq,D].
     """
+    dev, B, Hq, Hkv, D, T, code, q_out = _prologue_checks(
+        q, k_new, v_new, pos, k_cache, v_cache, q_norm_w, k_norm_w, q_out)
+    _check(lib.gqa_qkv_prologue(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0), k_new.stride(0),
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), float(rope_theta), _ptr(pos),
+        _ptr(q_out), _ptr(k_cache), _ptr(v_cache), B, Hq, Hkv, D, T, _stream(dev)))
+    return q_out
+
+
+def qkv_prologue_ex(q, k_new, v_new, pos, k_cache, v_cache, inv_freq=None,
+                    rope_mscale: float = 1.0, rope_layout="neox", q_norm_w=None,
+                    k_norm_w=None, eps: float = 1e-6, q_out=None):
+    """``qkv_prologue`` with an explicit rotary table (host float64 [D/2] or
+    None for no RoPE), magnitude factor and pair layout ("neox" or
+    "interleaved")."""
+    dev, B, Hq, Hkv, D, T, code, q_out = _prologue_checks(
+        q, k_new, v_new, pos, k_cache, v_cache, q_norm_w, k_norm_w, q_out)
+    f = _host_table(inv_freq, D)
+    _check(lib.gqa_qkv_prologue_ex(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0), k_new.stride(0),
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), None if f is None else f.ctypes.data,
+        float(rope_mscale), _layout_code(rope_layout), _ptr(pos), _ptr(q_out),
+        _ptr(k_cache), _ptr(v_cache), B, Hq, Hkv, D, T, _stream(dev)))
+    return q_out
+
+
+def _prologue_checks(q, k_new, v_new, pos, k_cache, v_cache, q_norm_w, k_norm_w, q_out):
     dev = k_cache.device
     for t, w in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (pos, "pos"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -151,11 +220,11 @@ def qkv_prologue(q, k_new, v_new, pos, k_cache, v_cache, q_norm_w=None, k_norm_w
             _contig(w, nm)
     if q_out is None:
         q_out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    _check(lib.gqa_qkv_prologue(
-        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0), k_new.stride(0),
-        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), float(rope_theta), _ptr(pos),
-        _ptr(q_out), _ptr(k_cache), _ptr(v_cache), B, Hq, Hkv, D, T, _stream(dev)))
-    return q_out
+    _dev(q_out, "q_out", dev)
+    _contig(q_out, "q_out")
+    if q_out.dtype != torch.float32 or tuple(q_out.shape) != (B, Hq, D):
+        raise ValueError("q_out must be float32 [B,Hq,D]")
+    return dev, B, Hq, Hkv, D, T, code, q_out
 
 
 def _attn_common(q, k_cache, v_cache, lens):
@@ -266,6 +335,43 @@ def decode_step(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens: int,
     device tensor whose arrival tickets start at zero (allocated zeroed when
     None; reuse it across calls).  Returns ``(out, workspace)``.
     """
+    a = _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, workspace,
+                     q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out)
+    dev, B, Hq, Hkv, D, T, code, workspace, out, nbytes, pro = a
+    _check(lib.gqa_decode_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0),
+        k_new.stride(0) if pro else Hkv * D,
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), float(rope_theta), _ptr(pos),
+        _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(window), float(scale), int(part_tokens),
+        _ptr(workspace), nbytes, _ptr(out), _dtype_code(out, "out"), _ptr(lse_out),
+        _ptr(q_out), B, Hq, Hkv, D, T, _stream(dev)))
+    return out, workspace
+
+
+def decode_step_ex(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens: int,
+                   workspace=None, inv_freq=None, rope_mscale: float = 1.0,
+                   rope_layout="neox", q_norm_w=None, k_norm_w=None, eps: float = 1e-6,
+                   window: int = 0, scale: float = 0.0, out=None, out_dtype=torch.float32,
+                   lse_out=None, q_out=None):
+    """``decode_step`` with an explicit rotary table (host float64 [D/2] or
+    None), magnitude factor and pair layout."""
+    a = _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, workspace,
+                     q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out)
+    dev, B, Hq, Hkv, D, T, code, workspace, out, nbytes, pro = a
+    f = _host_table(inv_freq, D)
+    _check(lib.gqa_decode_step_ex(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0),
+        k_new.stride(0) if pro else Hkv * D,
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), None if f is None else f.ctypes.data,
+        float(rope_mscale), _layout_code(rope_layout), _ptr(pos),
+        _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(window), float(scale), int(part_tokens),
+        _ptr(workspace), nbytes, _ptr(out), _dtype_code(out, "out"), _ptr(lse_out),
+        _ptr(q_out), B, Hq, Hkv, D, T, _stream(dev)))
+    return out, workspace
+
+
+def _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, workspace,
+                 q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out):
     dev = k_cache.device
     pro = pos is not None
     if (k_new is None) == pro or (v_new is None) == pro:
@@ -317,11 +423,4 @@ def decode_step(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens: int,
         if q_out.dtype != torch.float32 or tuple(q_out.shape) != (B, Hq, D):
             raise ValueError("q_out must be float32 [B,Hq,D]")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib.gqa_decode_step(
-        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0),
-        k_new.stride(0) if pro else Hkv * D,
-        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), float(rope_theta), _ptr(pos),
-        _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(window), float(scale), int(part_tokens),
-        _ptr(workspace), nbytes, _ptr(out), _dtype_code(out, "out"), _ptr(lse_out),
-        _ptr(q_out), B, Hq, Hkv, D, T, _stream(dev)))
-    return out, workspace
+    return dev, B, Hq, Hkv, D, T, code, workspace, out, nbytes, pro

@@ -51,6 +51,17 @@ int check_split(int B, int Hkv, int T, int window, int part_tokens) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// A rotary table (host, D/2 finite non-negative frequencies, or NULL for no
+// RoPE), its magnitude factor and its pair layout.
+int check_rope(const double* inv_freq, double mscale, int layout, int D) {
+  if (layout != GQA_ROPE_NEOX && layout != GQA_ROPE_INTERLEAVED) return GQA_ERR_VALUE;
+  if (!(mscale > 0.0) || !isfinite(mscale)) return GQA_ERR_VALUE;
+  if (inv_freq)
+    for (int i = 0; i < D / 2; ++i)
+      if (!(inv_freq[i] >= 0.0) || !isfinite(inv_freq[i])) return GQA_ERR_VALUE;
+  return GQA_OK;
+}
+
 float softmax_qscale(float scale, int D) {
   const double s = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)D);
   return (float)(s * 1.4426950408889634);
@@ -74,12 +85,53 @@ const char* gqa_status_string(int status) {
   }
 }
 
-int gqa_qkv_prologue(const void* q, const void* k_new, const void* v_new,
-                     gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
-                     const float* q_norm_w, const float* k_norm_w, float eps,
-                     double rope_theta, const int32_t* pos, float* q_out,
-                     uint16_t* k_cache, uint16_t* v_cache,
-                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+int gqa_rope_table(int kind, int D, double theta, double factor, int orig_ctx,
+                   double beta_fast, double beta_slow, double* inv_freq, double* mscale) {
+  if (!inv_freq) return GQA_ERR_NULL;
+  if (D < 2 || D % 2 != 0) return GQA_ERR_SHAPE;
+  if (!(theta > 0.0) || !isfinite(theta)) return GQA_ERR_VALUE;
+  if (kind < GQA_ROPE_DEFAULT || kind > GQA_ROPE_YARN) return GQA_ERR_VALUE;
+  if (kind != GQA_ROPE_DEFAULT && (!(factor >= 1.0) || !isfinite(factor)))
+    return GQA_ERR_VALUE;
+  if (kind == GQA_ROPE_NTK && D < 4) return GQA_ERR_SHAPE;
+  if (kind == GQA_ROPE_YARN &&
+      (orig_ctx < 1 || !(beta_slow >= 0.0) || !(beta_fast > beta_slow) || !isfinite(beta_fast)))
+    return GQA_ERR_VALUE;
+  const double two_pi = 6.283185307179586476925;
+  for (int i = 0; i < D / 2; ++i) {
+    const double e = -2.0 * i / D;
+    const double f = pow(theta, e);
+    double out = f;
+    switch (kind) {
+      case GQA_ROPE_LINEAR:   // positions divided by the factor
+        out = f / factor;
+        break;
+      case GQA_ROPE_NTK:      // base stretched so the lowest frequency drops by the factor
+        out = pow(theta * pow(factor, D / (D - 2.0)), e);
+        break;
+      case GQA_ROPE_YARN: {   // blend by rotations over the original context
+        const double r = (double)orig_ctx * f / two_pi;
+        double gm = (r - beta_slow) / (beta_fast - beta_slow);
+        gm = gm < 0.0 ? 0.0 : (gm > 1.0 ? 1.0 : gm);
+        out = (1.0 - gm) * f / factor + gm * f;
+        break;
+      }
+      default:
+        break;
+    }
+    inv_freq[i] = out;
+  }
+  if (mscale) *mscale = kind == GQA_ROPE_YARN ? 1.0 + 0.1 * log(factor) : 1.0;
+  return GQA_OK;
+}
+
+int gqa_qkv_prologue_ex(const void* q, const void* k_new, const void* v_new,
+                        gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                        const float* q_norm_w, const float* k_norm_w, float eps,
+                        const double* inv_freq, double rope_mscale, int rope_layout,
+                        const int32_t* pos, float* q_out,
+                        uint16_t* k_cache, uint16_t* v_cache,
+                        int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
   if (!q || !k_new || !v_new || !pos || !q_out || !k_cache || !v_cache) return GQA_ERR_NULL;
   if ((q_norm_w == nullptr) != (k_norm_w == nullptr)) return GQA_ERR_NULL;
   int rc = check_shapes(B, Hq, Hkv, D, T);
@@ -88,16 +140,42 @@ int gqa_qkv_prologue(const void* q, const void* k_new, const void* v_new,
   if (q_bstride < (int64_t)Hq * D || kv_bstride < (int64_t)Hkv * D) return GQA_ERR_SHAPE;
   if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
   if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
-  if (isnan(rope_theta) || isinf(rope_theta)) return GQA_ERR_VALUE;
+  if ((rc = check_rope(inv_freq, rope_mscale, rope_layout, D))) return rc;
   const uintptr_t ea = in_dtype == GQA_BF16 ? 2 : 4;
   if (!aligned(q, ea) || !aligned(k_new, ea) || !aligned(v_new, ea) || !aligned(q_out, 4) ||
       !aligned(k_cache, 2) || !aligned(v_cache, 2) || !aligned(pos, 4) ||
       !aligned(q_norm_w, 4) || !aligned(k_norm_w, 4))
     return GQA_ERR_ALIGN;
-  gqa::PrologueArgs a{q, k_new, v_new, in_dtype == GQA_BF16, q_bstride, kv_bstride,
-                      q_norm_w, k_norm_w, eps, rope_theta, pos, q_out, k_cache, v_cache,
-                      B, Hq, Hkv, D, T};
+  gqa::PrologueArgs a{};
+  a.q = q; a.k_new = k_new; a.v_new = v_new; a.in_bf16 = in_dtype == GQA_BF16;
+  a.q_bstride = q_bstride; a.kv_bstride = kv_bstride;
+  a.q_norm_w = q_norm_w; a.k_norm_w = k_norm_w; a.eps = eps;
+  a.rope = inv_freq != nullptr;
+  a.rope_interleaved = rope_layout == GQA_ROPE_INTERLEAVED;
+  a.rope_mscale = (float)rope_mscale;
+  if (a.rope)
+    for (int i = 0; i < D / 2; ++i) a.inv_freq[i] = inv_freq[i];
+  a.pos = pos; a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   return gqa::launch_prologue(a, stream);
+}
+
+int gqa_qkv_prologue(const void* q, const void* k_new, const void* v_new,
+                     gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                     const float* q_norm_w, const float* k_norm_w, float eps,
+                     double rope_theta, const int32_t* pos, float* q_out,
+                     uint16_t* k_cache, uint16_t* v_cache,
+                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  if (isnan(rope_theta) || isinf(rope_theta)) return GQA_ERR_VALUE;
+  double table[gqa::kMaxHalfDim];
+  const double* f = nullptr;
+  if (rope_theta > 0.0 && (D == 64 || D == 128)) {
+    gqa_rope_table(GQA_ROPE_DEFAULT, D, rope_theta, 1.0, 0, 0.0, 0.0, table, nullptr);
+    f = table;
+  }
+  return gqa_qkv_prologue_ex(q, k_new, v_new, in_dtype, q_bstride, kv_bstride, q_norm_w,
+                             k_norm_w, eps, f, 1.0, GQA_ROPE_NEOX, pos, q_out, k_cache,
+                             v_cache, B, Hq, Hkv, D, T, stream);
 }
 
 int gqa_attn_decode(const void* q, gqa_dtype_t q_dtype,
@@ -196,21 +274,23 @@ size_t gqa_decode_step_workspace_bytes(int B, int Hq, int Hkv, int D, int T, int
   return align256(base) + (size_t)B * Hkv * sizeof(uint32_t);
 }
 
-int gqa_decode_step(const void* q, const void* k_new, const void* v_new, gqa_dtype_t in_dtype,
-                    int64_t q_bstride, int64_t kv_bstride,
-                    const float* q_norm_w, const float* k_norm_w, float eps,
-                    double rope_theta, const int32_t* pos,
-                    uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
-                    int window, float scale, int part_tokens,
-                    void* workspace, size_t workspace_bytes,
-                    void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
-                    int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+int gqa_decode_step_ex(const void* q, const void* k_new, const void* v_new,
+                       gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                       const float* q_norm_w, const float* k_norm_w, float eps,
+                       const double* inv_freq, double rope_mscale, int rope_layout,
+                       const int32_t* pos,
+                       uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                       int window, float scale, int part_tokens,
+                       void* workspace, size_t workspace_bytes,
+                       void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                       int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !lens || !workspace || !out) return GQA_ERR_NULL;
   // the prologue inputs come all together or not at all
   const bool pro = pos != nullptr;
   if ((k_new != nullptr) != pro || (v_new != nullptr) != pro) return GQA_ERR_NULL;
   if ((q_norm_w == nullptr) != (k_norm_w == nullptr)) return GQA_ERR_NULL;
-  if (!pro && (q_norm_w != nullptr || q_out != nullptr)) return GQA_ERR_NULL;
+  if (!pro && (q_norm_w != nullptr || q_out != nullptr || inv_freq != nullptr))
+    return GQA_ERR_NULL;
   int rc = check_shapes(B, Hq, Hkv, D, T);
   if (rc) return rc;
   if ((rc = check_split(B, Hkv, T, window, part_tokens))) return rc;
@@ -218,7 +298,7 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, gqa_dty
   if (q_bstride < (int64_t)Hq * D || kv_bstride < (int64_t)Hkv * D) return GQA_ERR_SHAPE;
   if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
   if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
-  if (isnan(rope_theta) || isinf(rope_theta)) return GQA_ERR_VALUE;
+  if ((rc = check_rope(inv_freq, rope_mscale, rope_layout, D))) return rc;
   if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
   const uintptr_t ea = in_dtype == GQA_BF16 ? 2 : 4;
   // q rows are read as 16-byte vectors: the batch stride must keep that alignment
@@ -246,12 +326,35 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, gqa_dty
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   a.k_new = k_new; a.v_new = v_new; a.kv_bstride = kv_bstride;
   a.wq = q_norm_w; a.wk = k_norm_w; a.eps = eps;
-  a.rope = pro && rope_theta > 0.0;
+  a.rope = pro && inv_freq != nullptr;
+  a.rope_interleaved = rope_layout == GQA_ROPE_INTERLEAVED;
+  a.rope_mscale = (float)rope_mscale;
   a.pos = pos; a.q_out = q_out;
   if (a.rope)
-    for (int i = 0; i < D / 2; ++i)
-      a.inv_freq_rev[i] = pow(rope_theta, -2.0 * i / D) / 6.283185307179586476925;
+    for (int i = 0; i < D / 2; ++i) a.inv_freq_rev[i] = inv_freq[i] / 6.283185307179586476925;
   return gqa::launch_decode_step(a, stream);
+}
+
+int gqa_decode_step(const void* q, const void* k_new, const void* v_new, gqa_dtype_t in_dtype,
+                    int64_t q_bstride, int64_t kv_bstride,
+                    const float* q_norm_w, const float* k_norm_w, float eps,
+                    double rope_theta, const int32_t* pos,
+                    uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                    int window, float scale, int part_tokens,
+                    void* workspace, size_t workspace_bytes,
+                    void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                    int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  if (isnan(rope_theta) || isinf(rope_theta)) return GQA_ERR_VALUE;
+  double table[gqa::kMaxHalfDim];
+  const double* f = nullptr;
+  if (pos != nullptr && rope_theta > 0.0 && (D == 64 || D == 128)) {
+    gqa_rope_table(GQA_ROPE_DEFAULT, D, rope_theta, 1.0, 0, 0.0, 0.0, table, nullptr);
+    f = table;
+  }
+  return gqa_decode_step_ex(q, k_new, v_new, in_dtype, q_bstride, kv_bstride, q_norm_w,
+                            k_norm_w, eps, f, 1.0, GQA_ROPE_NEOX, pos, k_cache, v_cache, lens,
+                            window, scale, part_tokens, workspace, workspace_bytes, out,
+                            out_dtype, lse_out, q_out, B, Hq, Hkv, D, T, stream);
 }
 
 }  // extern "C"

@@ -453,7 +453,9 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     for (int c = 0; c < KC; ++c) {
       if (qnorm) load8f<float>(a.wq + 32 * c + 8 * lg, wq8[c]);
     }
-    const int fi = lane % HALF;               // rotary frequency index of this lane
+    const int fi = lane % HALF;               // rotary pair of this lane
+    const bool il = a.rope_interleaved != 0;  // pairs (2i, 2i+1), else (i, i+D/2)
+    const int e0 = il ? 2 * fi : fi, e1 = il ? 2 * fi + 1 : fi + HALF;
     const double inv_rev = rope ? a.inv_freq_rev[fi] : 0.0;
     // raw values: converted only after the tiles are issued
     IT rx0 = 0, rx1 = 0, rv0 = 0, rv1 = 0;
@@ -463,26 +465,29 @@ attn_decode_mfma_kernel(const KernelArgs a) {
                      (int64_t)g * D;
       const IT* vs = reinterpret_cast<const IT*>(a.v_new) + (int64_t)b * a.kv_bstride +
                      (int64_t)g * D;
-      rx0 = ks[fi];
-      rx1 = ks[fi + HALF];
-      rv0 = vs[fi];
-      rv1 = vs[fi + HALF];
+      rx0 = ks[e0];
+      rx1 = ks[e1];
+      rv0 = vs[e0];
+      rv1 = vs[e1];
       if (a.wk != nullptr) {
-        wk0 = a.wk[fi];
-        wk1 = a.wk[fi + HALF];
+        wk0 = a.wk[e0];
+        wk1 = a.wk[e1];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     prime();
     __builtin_amdgcn_sched_barrier(0);
-    // Rotary angle of frequency index fi: the phase p * theta^(-2fi/D) / (2 pi)
-    // is formed and reduced in float64 from a host-computed table, leaving a
-    // float32 sincos of an angle in [-pi, pi].
+    // Rotary angle of pair fi: the phase p * f_fi / (2 pi) is formed and
+    // reduced in float64 from the host-computed table, leaving a float32
+    // sincos of an angle in [-pi, pi]; cos and sin carry the magnitude
+    // factor, so it reaches both q and k.
     float cs = 1.0f, sn = 0.0f;
     if (rope) {
       const double rev = (double)p * inv_rev;
       const double fr = rev - rint(rev);
       sincosf((float)(fr * 6.283185307179586), &sn, &cs);
+      cs *= a.rope_mscale;
+      sn *= a.rope_mscale;
     }
     // Angles and the new K row cross lanes through this wave's LDS slab (in
     // order within the wave; each asm hides an index from per-lane alias
@@ -506,25 +511,27 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       if (kwrite && lane < HALF) {
         uint16_t* krow = a.k_cache_w + slab_off + (int64_t)p * D;
         uint16_t* vrow = a.v_cache_w + slab_off + (int64_t)p * D;
-        krow[fi] = k0;
-        krow[fi + HALF] = k1;
-        vrow[fi] = v0;
-        vrow[fi + HALF] = v1;
+        krow[e0] = k0;
+        krow[e1] = k1;
+        vrow[e0] = v0;
+        vrow[e1] = v1;
       }
       if (attended && lane < HALF) {
         uint16_t* kh = reinterpret_cast<uint16_t*>(&snew[wave][0][0]);
         int kidx = fi;
         asm volatile("" : "+v"(kidx));
-        kh[kidx] = k0;
-        kh[kidx + HALF] = k1;
-        kh[D + kidx] = v0;
-        kh[D + kidx + HALF] = v1;
+        const int k0i = il ? 2 * kidx : kidx, k1i = il ? 2 * kidx + 1 : kidx + HALF;
+        kh[k0i] = k0;
+        kh[k1i] = k1;
+        kh[D + k0i] = v0;
+        kh[D + k1i] = v1;
       }
       if (attended) psub = p;
     }
     // Query head g*G + hq: RMSNorm over D (the lane's D/4 elements, summed
-    // over the four lane groups of head n), then RoPE: element e < D/2 of
-    // slice c pairs with e + D/2 in slice c + KC/2 of the same lane.
+    // over the four lane groups of head n), then RoPE.  NeoX: element e < D/2
+    // of slice c pairs with e + D/2 in slice c + KC/2 of the same lane.
+    // Interleaved: elements 2i, 2i+1 sit next to each other in one slice.
     if (qnorm) {
       float ss = 0.0f;
 #pragma unroll
@@ -546,17 +553,31 @@ attn_decode_mfma_kernel(const KernelArgs a) {
         af[aidx] = cs;
         af[HALF + aidx] = sn;
       }
-      int ridx = 8 * lg;
-      asm volatile("" : "+v"(ridx));
+      if (il) {
+        int ridx = 4 * lg;                   // pair of element 32c + 8lg + j is 16c + 4lg + j/2
+        asm volatile("" : "+v"(ridx));
 #pragma unroll
-      for (int c = 0; c < KC / 2; ++c)
+        for (int c = 0; c < KC; ++c)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float cc = af[ridx + 32 * c + j], sv = af[HALF + ridx + 32 * c + j];
-          const float y1 = qf[c][j], y2 = qf[c + KC / 2][j];
-          qf[c][j] = y1 * cc - y2 * sv;
-          qf[c + KC / 2][j] = y2 * cc + y1 * sv;
-        }
+          for (int j = 0; j < 8; j += 2) {
+            const float cc = af[ridx + 16 * c + j / 2], sv = af[HALF + ridx + 16 * c + j / 2];
+            const float y1 = qf[c][j], y2 = qf[c][j + 1];
+            qf[c][j] = y1 * cc - y2 * sv;
+            qf[c][j + 1] = y2 * cc + y1 * sv;
+          }
+      } else {
+        int ridx = 8 * lg;
+        asm volatile("" : "+v"(ridx));
+#pragma unroll
+        for (int c = 0; c < KC / 2; ++c)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float cc = af[ridx + 32 * c + j], sv = af[HALF + ridx + 32 * c + j];
+            const float y1 = qf[c][j], y2 = qf[c + KC / 2][j];
+            qf[c][j] = y1 * cc - y2 * sv;
+            qf[c + KC / 2][j] = y2 * cc + y1 * sv;
+          }
+      }
     }
 #pragma unroll
     for (int c = 0; c < KC; ++c)

@@ -8,6 +8,9 @@
 
 namespace gqa {
 
+constexpr int kMaxHalfDim = 64;   // D/2 for the largest supported head dim
+
+// Arguments of the standalone prologue kernel, passed by value.
 struct PrologueArgs {
   const void* q;
   const void* k_new;
@@ -17,15 +20,16 @@ struct PrologueArgs {
   const float* q_norm_w;
   const float* k_norm_w;
   float eps;
-  double theta;
+  int rope;                    // 0: no RoPE
+  int rope_interleaved;        // pairs (2i, 2i+1) instead of (i, i+D/2)
+  float rope_mscale;           // magnitude factor of the rotated vectors
   const int32_t* pos;
   float* q_out;
   uint16_t* k_cache;
   uint16_t* v_cache;
   int B, Hq, Hkv, D, T;
+  double inv_freq[kMaxHalfDim];   // rotary frequency of pair i (radians per position)
 };
-
-constexpr int kMaxHalfDim = 64;   // D/2 for the largest supported head dim
 
 // Arguments of the attention kernel in all three modes, passed by value.
 struct KernelArgs {
@@ -55,11 +59,13 @@ struct KernelArgs {
   const float* wk;
   float eps;
   int rope;                    // 0: no RoPE
+  int rope_interleaved;        // pairs (2i, 2i+1) instead of (i, i+D/2)
+  float rope_mscale;           // magnitude factor of the rotated vectors
   const int32_t* pos;
   float* q_out;                // may be null
   uint16_t* k_cache_w;         // same buffers as k_cache / v_cache
   uint16_t* v_cache_w;
-  double inv_freq_rev[kMaxHalfDim];   // theta^(-2i/D) / (2 pi), float64
+  double inv_freq_rev[kMaxHalfDim];   // frequency of pair i / (2 pi), float64
 };
 
 struct MergeArgs {

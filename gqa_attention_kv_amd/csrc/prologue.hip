@@ -1,17 +1,19 @@
-// Fused decode prologue for gfx950: per-head QK-RMSNorm, NeoX RoPE at the
+// Fused decode prologue for gfx950: per-head QK-RMSNorm, RoPE at the
 // sequence's position, and the append of the new K/V row to the bf16 cache.
 //
 // Follows the cutileGPT README feature "fused QK-Norm + RoPE + KV-cache
 // writes", the RMSNorm formula of its "Why tiles" figure (x * w / sqrt(
 // mean(x^2) + eps)), and the fusedtok 1.0.1 README "Operators" row RoPE
-// (NeoX layout, kv-cache position offset).
+// (interleaved and NeoX layouts, kv-cache position offset).
 //
 // Mapping: one head vector (a query head or a KV head of one sequence) per
-// D/2 consecutive lanes; lane i owns the NeoX pair (i, i + D/2), so the
+// D/2 consecutive lanes; lane i owns rotary pair i -- elements (i, i + D/2)
+// in the NeoX layout, (2i, 2i + 1) in the interleaved one -- so the
 // rotation is lane-local and only the sum of squares crosses lanes.  For
 // D = 128 that is one wave64 per head vector.  The rotary angle
-// pos * theta^(-2i/D) is formed and reduced in float64 (at pos ~ 1e5 a
-// float32 angle would be off by ~1e-2 rad); the rotation itself is float32.
+// pos * inv_freq[i] (the caller's table) is formed in float64 with a
+// float64 sincos (at pos ~ 1e5 a float32 angle would be off by ~1e-2 rad);
+// the rotation itself is float32, scaled by the magnitude factor.
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/gqa_decode.h"
@@ -33,44 +35,44 @@ __device__ __forceinline__ uint16_t to_bf16_bits(const float* p, int64_t i) {
 __device__ __forceinline__ uint16_t to_bf16_bits(const uint16_t* p, int64_t i) { return p[i]; }
 
 template <int D, typename IT>
-__global__ __launch_bounds__(256) void qkv_prologue_kernel(
-    const IT* __restrict__ q, const IT* __restrict__ k_new, const IT* __restrict__ v_new,
-    int64_t q_bstride, int64_t kv_bstride, const float* __restrict__ wq,
-    const float* __restrict__ wk, float eps, double theta, const int32_t* __restrict__ pos,
-    float* __restrict__ q_out, uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
-    int B, int Hq, int Hkv, int T) {
+__global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a) {
   constexpr int HALF = D / 2;        // lanes per head vector
   constexpr int VPB = 256 / HALF;    // head vectors per workgroup
+  const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
   const int H = Hq + Hkv;
   const int vec = blockIdx.x * VPB + threadIdx.x / HALF;
   const int i = threadIdx.x % HALF;
-  const bool live = vec < B * H;     // lanes past the end compute on vector 0, store nothing
+  const bool live = vec < a.B * H;   // lanes past the end compute on vector 0, store nothing
   const int v = live ? vec : 0;
   const int b = v / H;
   const int hh = v % H;
   const bool is_q = hh < Hq;
   const int g = hh - Hq;
+  // elements of rotary pair i
+  const int e0 = a.rope_interleaved ? 2 * i : i;
+  const int e1 = a.rope_interleaved ? 2 * i + 1 : i + HALF;
 
-  const IT* src = is_q ? q + (int64_t)b * q_bstride + (int64_t)hh * D
-                       : k_new + (int64_t)b * kv_bstride + (int64_t)g * D;
-  float x0 = load_elem<IT>(src, i);
-  float x1 = load_elem<IT>(src, i + HALF);
+  const IT* src = is_q ? reinterpret_cast<const IT*>(a.q) + (int64_t)b * a.q_bstride +
+                             (int64_t)hh * D
+                       : reinterpret_cast<const IT*>(a.k_new) + (int64_t)b * a.kv_bstride +
+                             (int64_t)g * D;
+  float x0 = load_elem<IT>(src, e0);
+  float x1 = load_elem<IT>(src, e1);
 
-  const float* w = is_q ? wq : wk;
+  const float* w = is_q ? a.q_norm_w : a.k_norm_w;
   if (w != nullptr) {
     float ss = x0 * x0 + x1 * x1;
     ss = group_sum_shfl<HALF>(ss);
-    const float r = 1.0f / sqrtf(ss / (float)D + eps);
-    x0 = x0 * r * w[i];
-    x1 = x1 * r * w[i + HALF];
+    const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+    x0 = x0 * r * w[e0];
+    x1 = x1 * r * w[e1];
   }
 
-  const int p = pos[b];
-  if (theta > 0.0) {
-    const double inv_freq = pow(theta, -2.0 * (double)i / (double)D);
+  const int p = a.pos[b];
+  if (a.rope) {
     double sn, cs;
-    sincos((double)p * inv_freq, &sn, &cs);
-    const float c = (float)cs, s = (float)sn;
+    sincos((double)p * a.inv_freq[i], &sn, &cs);
+    const float c = (float)cs * a.rope_mscale, s = (float)sn * a.rope_mscale;
     const float y0 = x0 * c - x1 * s;
     const float y1 = x1 * c + x0 * s;
     x0 = y0;
@@ -79,16 +81,17 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(
   if (!live) return;
 
   if (is_q) {
-    float* dst = q_out + ((int64_t)b * Hq + hh) * D;
-    dst[i] = x0;
-    dst[i + HALF] = x1;
+    float* dst = a.q_out + ((int64_t)b * Hq + hh) * D;
+    dst[e0] = x0;
+    dst[e1] = x1;
   } else if (p >= 0 && p < T) {
     const int64_t row = (((int64_t)b * Hkv + g) * T + p) * D;
-    k_cache[row + i] = f32_to_bf16(x0);
-    k_cache[row + i + HALF] = f32_to_bf16(x1);
-    const IT* vs = v_new + (int64_t)b * kv_bstride + (int64_t)g * D;
-    v_cache[row + i] = to_bf16_bits(vs, i);
-    v_cache[row + i + HALF] = to_bf16_bits(vs, i + HALF);
+    a.k_cache[row + e0] = f32_to_bf16(x0);
+    a.k_cache[row + e1] = f32_to_bf16(x1);
+    const IT* vs = reinterpret_cast<const IT*>(a.v_new) + (int64_t)b * a.kv_bstride +
+                   (int64_t)g * D;
+    a.v_cache[row + e0] = to_bf16_bits(vs, e0);
+    a.v_cache[row + e1] = to_bf16_bits(vs, e1);
   }
 }
 
@@ -97,10 +100,7 @@ static int launch_prologue_t(const PrologueArgs& a, hipStream_t s) {
   constexpr int VPB = 256 / (D / 2);
   const int64_t vecs = (int64_t)a.B * (a.Hq + a.Hkv);
   const unsigned blocks = (unsigned)((vecs + VPB - 1) / VPB);
-  hipLaunchKernelGGL((qkv_prologue_kernel<D, IT>), dim3(blocks), dim3(256), 0, s,
-                     (const IT*)a.q, (const IT*)a.k_new, (const IT*)a.v_new, a.q_bstride,
-                     a.kv_bstride, a.q_norm_w, a.k_norm_w, a.eps, a.theta, a.pos, a.q_out,
-                     a.k_cache, a.v_cache, a.B, a.Hq, a.Hkv, a.T);
+  hipLaunchKernelGGL((qkv_prologue_kernel<D, IT>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 

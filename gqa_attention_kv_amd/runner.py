@@ -14,6 +14,7 @@ import numpy as np
 import torch
 
 from . import attn_decode, attn_decode_merge, attn_decode_splitk, decode_step, qkv_prologue
+from . import decode_step_ex, qkv_prologue_ex, rope_table
 from . import decode_step_workspace_bytes, splitk_workspace_bytes
 
 BF16_NAN = 0x7FC0
@@ -79,6 +80,14 @@ class DeviceStep:
             self.w_q = None if w.w_q is None else torch.from_numpy(w.w_q).to(d)
             self.w_k = None if w.w_k is None else torch.from_numpy(w.w_k).to(d)
             self.q = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=d)
+            # A RoPE variant (interleaved pairs or a context-extension table)
+            # goes through the *_ex entry points with the library's own table.
+            sc = getattr(w, "rope_scaling", None)
+            self.rope_layout = getattr(w, "rope_layout", "neox")
+            self.rope_ex = (sc is not None or self.rope_layout != "neox") and w.theta > 0
+            if self.rope_ex:
+                sc = dict(sc or {"kind": "default"})
+                self.inv_freq, self.rope_mscale = rope_table(sc.pop("kind"), w.D, w.theta, **sc)
         else:
             qb = bf16_tensor(w.q, d)
             self.q = qb if q_dtype == "bf16" else qb.float()
@@ -97,6 +106,12 @@ class DeviceStep:
     def prologue(self):
         w = self.w
         if w.pos is None:
+            return
+        if self.rope_ex:
+            qkv_prologue_ex(self.q_in, self.k_new, self.v_new, self.pos, self.k_cache,
+                            self.v_cache, inv_freq=self.inv_freq, rope_mscale=self.rope_mscale,
+                            rope_layout=self.rope_layout, q_norm_w=self.w_q, k_norm_w=self.w_k,
+                            eps=w.eps, q_out=self.q)
             return
         qkv_prologue(self.q_in, self.k_new, self.v_new, self.pos, self.k_cache, self.v_cache,
                      q_norm_w=self.w_q, k_norm_w=self.w_k, eps=w.eps,
@@ -124,6 +139,14 @@ class DeviceStep:
             decode_step(self.q, None, None, None, self.k_cache, self.v_cache, self.lens,
                         self.part_tokens, workspace=self.ws, window=w.window,
                         scale=self.scale, out=self.out, lse_out=self.lse)
+            return
+        if self.rope_ex:
+            decode_step_ex(self.q_in, self.k_new, self.v_new, self.pos, self.k_cache,
+                           self.v_cache, self.lens, self.part_tokens, workspace=self.ws,
+                           inv_freq=self.inv_freq, rope_mscale=self.rope_mscale,
+                           rope_layout=self.rope_layout, q_norm_w=self.w_q, k_norm_w=self.w_k,
+                           eps=w.eps, window=w.window, scale=self.scale, out=self.out,
+                           lse_out=self.lse, q_out=self.q)
             return
         decode_step(self.q_in, self.k_new, self.v_new, self.pos, self.k_cache, self.v_cache,
                     self.lens, self.part_tokens, workspace=self.ws, q_norm_w=self.w_q,

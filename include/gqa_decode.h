@@ -95,6 +95,60 @@ int gqa_qkv_prologue(const void* q, const void* k_new, const void* v_new,
                      uint16_t* k_cache, uint16_t* v_cache,
                      int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
 
+/* RoPE pair layouts (fusedtok 1.0.1 README, Operators row RoPE: interleaved
+ * and NeoX layouts). */
+enum {
+  GQA_ROPE_NEOX = 0,         /* pair i = elements (i, i + D/2), "rotate half" */
+  GQA_ROPE_INTERLEAVED = 1   /* pair i = elements (2i, 2i + 1)                */
+};
+
+/* Rotary frequency schemes (PyGPUkit 0.2.18 page, Positional Encoding
+ * Operations: NTK-aware RoPE, YaRN dimension-wise interpolation, linear
+ * position interpolation; the page names them without formulas). */
+enum {
+  GQA_ROPE_DEFAULT = 0,  /* f_i = theta^(-2i/D)                                */
+  GQA_ROPE_LINEAR = 1,   /* f_i / factor (positions divided by the factor)     */
+  GQA_ROPE_NTK = 2,      /* base theta * factor^(D/(D-2)): f_0 unchanged,      */
+                         /* f_{D/2-1} divided by exactly the factor            */
+  GQA_ROPE_YARN = 3      /* r_i = orig_ctx f_i / (2 pi) rotations over the     */
+                         /* original context; g_i = clamp((r_i - beta_slow) /  */
+                         /* (beta_fast - beta_slow), 0, 1); f_i' = (1 - g_i)   */
+                         /* f_i / factor + g_i f_i; mscale = 1 + 0.1 ln factor */
+};
+
+/*
+ * Host helper (no GPU work): fill inv_freq[D/2] (host memory, radians per
+ * position of rotary pair i) for scheme `kind` and, when `mscale` is not
+ * NULL, the magnitude factor the scheme applies to the rotated q and k (1
+ * except YaRN).  theta > 0; factor >= 1 (ignored by GQA_ROPE_DEFAULT);
+ * orig_ctx >= 1 and beta_fast > beta_slow >= 0 for YaRN (orig_ctx and the
+ * betas are ignored otherwise); D even (>= 4 for NTK).  Returns GQA_OK or
+ * GQA_ERR_NULL / GQA_ERR_SHAPE / GQA_ERR_VALUE; nothing is written on error.
+ */
+int gqa_rope_table(int kind, int D, double theta, double factor, int orig_ctx,
+                   double beta_fast, double beta_slow, double* inv_freq, double* mscale);
+
+/*
+ * gqa_qkv_prologue with an explicit rotary table instead of rope_theta:
+ *   inv_freq     HOST pointer to D/2 float64 frequencies (radians per
+ *                position, finite, >= 0), read during the call; NULL for no
+ *                RoPE.  Pair i of the chosen layout rotates by
+ *                pos * inv_freq[i] (angle and sincos in float64).
+ *   rope_mscale  > 0: both rotated vectors (q and k) are multiplied by it
+ *                (1 for a plain rotation; YaRN's attention temperature).
+ *   rope_layout  GQA_ROPE_NEOX or GQA_ROPE_INTERLEAVED.
+ * Every other argument, and every error, as for gqa_qkv_prologue.
+ * gqa_qkv_prologue(theta) is this call with the GQA_ROPE_DEFAULT table,
+ * mscale 1 and the NeoX layout.
+ */
+int gqa_qkv_prologue_ex(const void* q, const void* k_new, const void* v_new,
+                        gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                        const float* q_norm_w, const float* k_norm_w, float eps,
+                        const double* inv_freq, double rope_mscale, int rope_layout,
+                        const int32_t* pos, float* q_out,
+                        uint16_t* k_cache, uint16_t* v_cache,
+                        int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
 /*
  * Single-token GQA decode attention, one pass over the cache per KV head
  * (fusedtok attention_decode; cutileGPT sliding-window attention).
@@ -202,6 +256,23 @@ int gqa_decode_step(const void* q, const void* k_new, const void* v_new, gqa_dty
                     void* workspace, size_t workspace_bytes,
                     void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
+/*
+ * gqa_decode_step with an explicit rotary table, magnitude factor and pair
+ * layout (arguments and errors as for gqa_qkv_prologue_ex; inv_freq must be
+ * NULL when the prologue is skipped).  gqa_decode_step(theta) is this call
+ * with the GQA_ROPE_DEFAULT table, mscale 1 and the NeoX layout.
+ */
+int gqa_decode_step_ex(const void* q, const void* k_new, const void* v_new,
+                       gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                       const float* q_norm_w, const float* k_norm_w, float eps,
+                       const double* inv_freq, double rope_mscale, int rope_layout,
+                       const int32_t* pos,
+                       uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                       int window, float scale, int part_tokens,
+                       void* workspace, size_t workspace_bytes,
+                       void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                       int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char* gqa_status_string(int status);

@@ -81,3 +81,21 @@ def attend(q, K, V, lens, window=0, scale=0.0):
         out.append(ob)
         lse.append(lb)
     return out, lse
+
+
+def rope_pairs(x, pos, inv_freq, layout="neox", mscale=1.0):
+    """Rotate pair i by pos * inv_freq[i] and scale by mscale, scalar loops.
+
+    Pair i is (i, i + D/2) for "neox" and (2i, 2i + 1) for "interleaved"
+    (the two layouts the fusedtok README's RoPE row names).
+    """
+    D = len(x)
+    h = D // 2
+    y = list(x)
+    for i in range(h):
+        u, v = (i, i + h) if layout == "neox" else (2 * i, 2 * i + 1)
+        a = pos * inv_freq[i]
+        c, s = math.cos(a), math.sin(a)
+        y[u] = mscale * (x[u] * c - x[v] * s)
+        y[v] = mscale * (x[v] * c + x[u] * s)
+    return y

@@ -36,8 +36,8 @@ import math
 import numpy as np
 
 __all__ = [
-    "bf16_to_f64", "f64_to_bf16", "rmsnorm", "rope_inv_freq", "rope_neox",
-    "qkv_prologue", "attend_rows", "attend", "num_partitions",
+    "bf16_to_f64", "f64_to_bf16", "rmsnorm", "rope_inv_freq", "rope_inv_freq_scaled",
+    "rope", "rope_neox", "qkv_prologue", "attend_rows", "attend", "num_partitions",
     "partition_ranges", "attend_partials", "lse_merge", "decode_step",
 ]
 
@@ -109,34 +109,100 @@ def rope_inv_freq(D: int, theta: float) -> np.ndarray:
     return np.power(float(theta), -2.0 * i / D)
 
 
-def rope_neox(x: np.ndarray, pos, theta: float) -> np.ndarray:
-    """Rotate pairs (i, i + D/2) of the last axis by angle pos * f_i.
+def rope_inv_freq_scaled(D: int, theta: float, kind: str = "default", factor: float = 1.0,
+                         orig_ctx: int = 0, beta_fast: float = 32.0,
+                         beta_slow: float = 1.0):
+    """(inv_freq [D/2], mscale) of a RoPE context-extension scheme.
 
-    y_i       = x_i cos a - x_{i+D/2} sin a
-    y_{i+D/2} = x_{i+D/2} cos a + x_i sin a
-    NeoX ("rotate half") pairing is the reading of the README's NeoX
-    (LLaMA-HF) layout; the whole head dimension is rotated (cutileGPT lists
-    partial RoPE as unsupported).  ``pos`` broadcasts against x[..., 0].
+    The PyGPUkit 0.2.18 page ("Positional Encoding Operations") names three
+    table builders -- NTK-aware RoPE, YaRN dimension-wise interpolation and
+    linear position interpolation -- without formulas; each is written here
+    from its published definition (parity unpinned by the pages beyond the
+    limits and closed forms the tests check):
+      linear  positions divided by ``factor`` s: f_i / s.
+      ntk     the base grows to theta * s^(D/(D-2)), so the highest
+              frequency (i = 0) is unchanged and the lowest (i = D/2-1) is
+              divided by exactly s.
+      yarn    (YaRN paper) with wavelength lambda_i = 2 pi / f_i and
+              r_i = orig_ctx / lambda_i rotations over the original context,
+              gamma_i = clip((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1)
+              and f'_i = (1 - gamma_i) f_i / s + gamma_i f_i: dimensions that
+              turn many times keep their frequency, those that turn less
+              than once are interpolated.  The rotated vectors are scaled by
+              mscale = 1 + 0.1 ln s (the paper's attention temperature,
+              applied to both q and k).
+      default the plain table, mscale 1.
+    """
+    f = rope_inv_freq(D, theta)
+    s = float(factor)
+    if kind == "default":
+        return f, 1.0
+    if kind == "linear":
+        return f / s, 1.0
+    if kind == "ntk":
+        i = np.arange(D // 2, dtype=np.float64)
+        return np.power(float(theta) * s ** (D / (D - 2.0)), -2.0 * i / D), 1.0
+    if kind == "yarn":
+        r = float(orig_ctx) * f / (2.0 * math.pi)
+        gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
+        return (1.0 - gamma) * f / s + gamma * f, 1.0 + 0.1 * math.log(s)
+    raise ValueError(kind)
+
+
+def rope(x: np.ndarray, pos, inv_freq: np.ndarray, layout: str = "neox",
+         mscale: float = 1.0) -> np.ndarray:
+    """Rotate pair i of the last axis by angle pos * inv_freq[i], times mscale.
+
+    Pairs (the fusedtok README's RoPE row names both layouts):
+      neox         (i, i + D/2), "rotate half" (its NeoX / LLaMA-HF layout)
+      interleaved  (2i, 2i + 1)
+    For a pair (u, v): u' = m (u cos a - v sin a), v' = m (v cos a + u sin a).
+    The whole head dimension is rotated (cutileGPT lists partial RoPE as
+    unsupported).  ``pos`` broadcasts against x[..., 0].
     """
     x = np.asarray(x, dtype=np.float64)
     D = x.shape[-1]
     h = D // 2
-    a = np.asarray(pos, dtype=np.float64)[..., None] * rope_inv_freq(D, theta)
-    c, s = np.cos(a), np.sin(a)
-    x1, x2 = x[..., :h], x[..., h:]
-    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+    a = np.asarray(pos, dtype=np.float64)[..., None] * np.asarray(inv_freq, np.float64)
+    c, s = mscale * np.cos(a), mscale * np.sin(a)
+    y = np.empty_like(x)
+    if layout == "neox":
+        u, v = x[..., :h], x[..., h:]
+        y[..., :h], y[..., h:] = u * c - v * s, v * c + u * s
+    elif layout == "interleaved":
+        u, v = x[..., 0::2], x[..., 1::2]
+        y[..., 0::2], y[..., 1::2] = u * c - v * s, v * c + u * s
+    else:
+        raise ValueError(layout)
+    return y
+
+
+def rope_neox(x: np.ndarray, pos, theta: float) -> np.ndarray:
+    """NeoX RoPE with the plain table: pairs (i, i + D/2) rotate by
+    pos * theta^(-2i/D).
+
+    y_i       = x_i cos a - x_{i+D/2} sin a
+    y_{i+D/2} = x_{i+D/2} cos a + x_i sin a
+    NeoX ("rotate half") pairing is the reading of the README's NeoX
+    (LLaMA-HF) layout.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return rope(x, pos, rope_inv_freq(x.shape[-1], theta), "neox")
 
 
 # ---------------------------------------------------------------------------
 # Fused prologue (cutileGPT feature list: fused QK-Norm + RoPE + KV-cache writes)
 # ---------------------------------------------------------------------------
-def qkv_prologue(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache):
-    """QK-RMSNorm, then NeoX RoPE at pos[b], then append K and V at row pos[b].
+def qkv_prologue(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache,
+                 inv_freq=None, layout: str = "neox", mscale: float = 1.0):
+    """QK-RMSNorm, then RoPE at pos[b], then append K and V at row pos[b].
 
     q: [B,Hq,D] float64; k_new, v_new: [B,Hkv,D] float64 (exact widenings of
     the bf16 inputs); w_q, w_k: [D] or None (None = no QK-norm; one weight
-    vector per projection shared by all heads); theta <= 0 = no RoPE;
-    pos: int [B]; caches: uint16 [B,Hkv,T,D].
+    vector per projection shared by all heads); pos: int [B]; caches: uint16
+    [B,Hkv,T,D].  RoPE: the table ``inv_freq`` [D/2] with ``layout`` and
+    ``mscale`` (see ``rope``) when given, else the plain NeoX table of
+    ``theta``; no RoPE when neither is given (theta <= 0).
 
     Returns (q_hat float64 [B,Hq,D], k_cache', v_cache') with new arrays for
     the caches.  Order norm -> RoPE -> write follows the feature's name.  V is
@@ -153,21 +219,23 @@ def qkv_prologue(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache):
     kc = np.array(k_cache, copy=True)
     vc = np.array(v_cache, copy=True)
     q_hat = np.empty_like(q)
+    if inv_freq is None and theta > 0:
+        inv_freq = rope_inv_freq(D, theta)
     for b in range(B):
         p = int(pos[b])
         for h in range(Hq):
             x = q[b, h]
             if w_q is not None:
                 x = rmsnorm(x, w_q, eps)
-            if theta > 0:
-                x = rope_neox(x, p, theta)
+            if inv_freq is not None:
+                x = rope(x, p, inv_freq, layout, mscale)
             q_hat[b, h] = x
         for g in range(Hkv):
             x = k[b, g]
             if w_k is not None:
                 x = rmsnorm(x, w_k, eps)
-            if theta > 0:
-                x = rope_neox(x, p, theta)
+            if inv_freq is not None:
+                x = rope(x, p, inv_freq, layout, mscale)
             if 0 <= p < T:
                 kc[b, g, p] = f64_to_bf16(x)
                 vc[b, g, p] = f64_to_bf16(v[b, g])
@@ -323,9 +391,14 @@ def decode_step(w, split: bool = False, scale: float = 0.0):
     """
     q = bf16_to_f64(w.q)
     if w.pos is not None:
+        inv_freq, mscale = None, 1.0
+        scaling = getattr(w, "rope_scaling", None)
+        if scaling is not None and w.theta > 0:
+            inv_freq, mscale = rope_inv_freq_scaled(w.D, w.theta, **scaling)
         q_hat, kc, vc = qkv_prologue(
             q, bf16_to_f64(w.k_new), bf16_to_f64(w.v_new), w.w_q, w.w_k,
-            w.eps, w.theta, w.pos, w.k_cache, w.v_cache)
+            w.eps, w.theta, w.pos, w.k_cache, w.v_cache, inv_freq=inv_freq,
+            layout=getattr(w, "rope_layout", "neox"), mscale=mscale)
     else:
         q_hat, kc, vc = q, w.k_cache, w.v_cache
     res = dict(q_hat=q_hat, k_cache=kc, v_cache=vc)

@@ -184,6 +184,113 @@ def pin_rope_complex_form(O):
     _close(O.rope_neox(x, pos, theta), np.concatenate([z.real, z.imag]), 1e-12, "rope complex")
 
 
+def pin_rope_interleaved_complex_form(O):
+    """Interleaved rotation = multiplying z_i = x_{2i} + j x_{2i+1} by
+    exp(j pos f_i); also the identity at pos 0, norm preservation and the
+    relative-position property for that layout."""
+    rng = _rng(7)
+    x = rng.standard_normal(64)
+    f = O.rope_inv_freq(64, 1e4)
+    for pos in (0, 5, 1234):
+        z = (x[0::2] + 1j * x[1::2]) * np.exp(1j * pos * f)
+        want = np.empty(64)
+        want[0::2], want[1::2] = z.real, z.imag
+        _close(O.rope(x, pos, f, "interleaved"), want, 1e-12, "interleaved complex")
+    assert np.array_equal(O.rope(x, 0, f, "interleaved"), x)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    lhs = O.rope(q, 40, f, "interleaved") @ O.rope(k, 73, f, "interleaved")
+    rhs = q @ O.rope(k, 33, f, "interleaved")
+    assert abs(lhs - rhs) <= 1e-10 * (1 + abs(rhs))
+    assert abs(np.linalg.norm(O.rope(q, 9, f, "interleaved")) - np.linalg.norm(q)) <= 1e-12
+
+
+def pin_rope_layouts_related_by_permutation(O):
+    """Gathering the even elements, then the odd ones, turns interleaved pairs
+    (2i, 2i+1) into NeoX pairs (i, i + D/2): rope_il(x) = P^-1 rope_neox(P x)."""
+    rng = _rng(8)
+    for D in (8, 64, 128):
+        x = rng.standard_normal(D)
+        f = rng.uniform(0.01, 1.0, D // 2)
+        perm = np.concatenate([np.arange(0, D, 2), np.arange(1, D, 2)])
+        y = O.rope(x[perm], 17, f, "neox")
+        back = np.empty(D)
+        back[perm] = y
+        _close(O.rope(x, 17, f, "interleaved"), back, 1e-14, "layout permutation")
+        _close(O.rope(x, 17, f, "neox"), BF.rope_pairs(list(x), 17, list(f), "neox"),
+               1e-14, "neox vs scalar loops")
+
+
+def pin_rope_mscale(O):
+    """The magnitude factor scales the rotated vector and nothing else."""
+    rng = _rng(9)
+    x = rng.standard_normal(16)
+    f = O.rope_inv_freq(16, 1e4)
+    for layout in ("neox", "interleaved"):
+        _close(O.rope(x, 11, f, layout, 1.25), 1.25 * O.rope(x, 11, f, layout), 1e-15,
+               "mscale")
+        assert abs(np.linalg.norm(O.rope(x, 11, f, layout, 1.25))
+                   - 1.25 * np.linalg.norm(x)) <= 1e-12
+
+
+def pin_rope_scaled_tables(O):
+    """Limits and closed forms of the context-extension tables."""
+    D, theta = 128, 5e5
+    f = O.rope_inv_freq(D, theta)
+    for kind in ("default", "linear", "ntk", "yarn"):       # factor 1: the plain table
+        g, m = O.rope_inv_freq_scaled(D, theta, kind, 1.0, 4096)
+        _close(g, f, 1e-15, f"{kind} factor 1")
+        assert m == 1.0
+    s = 4.0
+    g, m = O.rope_inv_freq_scaled(D, theta, "linear", s)
+    _close(g / f, np.full(D // 2, 1 / s), 1e-15, "linear ratio")
+    assert m == 1.0
+    g, m = O.rope_inv_freq_scaled(D, theta, "ntk", s)
+    assert g[0] == 1.0 and m == 1.0                    # highest frequency unchanged
+    assert abs(g[-1] / f[-1] - 1 / s) <= 1e-12        # lowest divided by exactly s
+    # middle index by hand: (theta s^(D/(D-2)))^(-2i/D) = f_i s^(-2i/(D-2))
+    i = 20
+    assert abs(g[i] - f[i] * s ** (-2.0 * i / (D - 2))) <= 1e-15 * f[i]
+    # YaRN: r_i = L f_i / 2 pi; r >= beta_fast keeps f, r <= beta_slow takes f/s
+    L, bf_, bs_ = 4096, 32.0, 1.0
+    g, m = O.rope_inv_freq_scaled(D, theta, "yarn", s, L, bf_, bs_)
+    r = L * f / (2 * math.pi)
+    hi, lo = r >= bf_, r <= bs_
+    assert hi.any() and lo.any() and (~hi & ~lo).any()
+    assert np.array_equal(g[hi], f[hi])
+    _close(g[lo], f[lo] / s, 1e-15, "yarn interpolated dims")
+    assert abs(m - (1 + 0.1 * math.log(s))) <= 1e-15
+    ratio = g / f                                      # 1/s ... 1, monotone in r
+    order = np.argsort(r)
+    assert np.all(np.diff(ratio[order]) >= -1e-15)
+    # a dimension exactly at the middle of the ramp takes the mean of f and f/s
+    D2, th2 = 4, 16.0                                  # f = [1, 1/4]
+    L2 = 2 * math.pi * 16.5 / 1.0                      # r_0 = 16.5 = (1 + 32) / 2
+    g2, _ = O.rope_inv_freq_scaled(D2, th2, "yarn", 2.0, L2, 32.0, 1.0)
+    assert abs(g2[0] - 0.5 * (1.0 + 0.5)) <= 1e-15
+
+
+def pin_prologue_table_and_layout(O):
+    """The prologue with a frequency table, either layout and a magnitude
+    factor matches scalar loops (brute force) on tiny shapes."""
+    for k, layout in enumerate(("interleaved", "neox")):
+        q, kn, vn, wq, wk, pos, kc, vc = _prologue_case(20 + k)
+        D = q.shape[-1]
+        f, m = O.rope_inv_freq_scaled(D, 1e4, "yarn", 3.0, 64)
+        qh, kc2, _ = O.qkv_prologue(q, kn, vn, wq, wk, 1e-6, 0.0, pos, kc, vc,
+                                    inv_freq=f, layout=layout, mscale=m)
+        for b in range(q.shape[0]):
+            for h in range(q.shape[1]):
+                x = BF.rope_pairs(BF.rmsnorm(list(q[b, h]), list(wq), 1e-6), int(pos[b]),
+                                  list(f), layout, m)
+                _close(qh[b, h], x, 1e-12, f"q_hat {layout}")
+            for g in range(kn.shape[1]):
+                x = np.array(BF.rope_pairs(BF.rmsnorm(list(kn[b, g]), list(wk), 1e-6),
+                                           int(pos[b]), list(f), layout, m))
+                row = _torch_bf16_to_f64(kc2[b, g, pos[b]])
+                half_ulp = np.ldexp(1.0, np.frexp(x)[1] - 9)
+                assert np.all(np.abs(row - x) <= half_ulp + 1e-300)
+
+
 # ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------

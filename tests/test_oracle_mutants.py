@@ -92,6 +92,46 @@ def _rope_cos_sin_swapped(x, pos, theta):
     return np.concatenate([x[..., :h] * c - x[..., h:] * s, x[..., h:] * c + x[..., :h] * s], -1)
 
 
+def _rope_general_pairs_swapped(x, pos, inv_freq, layout="neox", mscale=1.0):
+    if layout != "interleaved":
+        return _orig["rope"](x, pos, inv_freq, layout, mscale)
+    x = np.asarray(x, np.float64)
+    sw = x.copy()
+    sw[..., 0::2], sw[..., 1::2] = x[..., 1::2], x[..., 0::2]
+    y = _orig["rope"](sw, pos, inv_freq, layout, mscale)
+    out = y.copy()
+    out[..., 0::2], out[..., 1::2] = y[..., 1::2], y[..., 0::2]
+    return out
+
+
+def _rope_general_mscale_squared(x, pos, inv_freq, layout="neox", mscale=1.0):
+    return _orig["rope"](x, pos, inv_freq, layout, mscale * mscale)
+
+
+def _rope_general_ignores_layout(x, pos, inv_freq, layout="neox", mscale=1.0):
+    return _orig["rope"](x, pos, inv_freq, "neox", mscale)
+
+
+def _table_variant(kind):
+    def f(D, theta, k="default", factor=1.0, orig_ctx=0, beta_fast=32.0, beta_slow=1.0):
+        g, m = _orig["rope_inv_freq_scaled"](D, theta, k, factor, orig_ctx, beta_fast,
+                                              beta_slow)
+        base = _orig["rope_inv_freq"](D, theta)
+        if kind == "yarn_ramp_inverted" and k == "yarn":
+            r = orig_ctx * base / (2 * math.pi)
+            gamma = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0, 1)
+            return gamma * base / factor + (1 - gamma) * base, m
+        if kind == "ntk_base_linear" and k == "ntk":
+            i = np.arange(D // 2)
+            return np.power(theta * factor, -2.0 * i / D), m
+        if kind == "linear_multiplies" and k == "linear":
+            return base * factor, m
+        if kind == "yarn_no_mscale" and k == "yarn":
+            return g, 1.0
+        return g, m
+    return f
+
+
 # --- attention -----------------------------------------------------------------
 def _rows_no_max(q, K, V, scale):
     if K.shape[0] == 0:
@@ -200,7 +240,11 @@ def _merge_no_empty_guard(o_parts, lse_parts):
 
 # --- prologue ----------------------------------------------------------------------
 def _prologue_variant(kind):
-    def f(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache):
+    def f(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache, inv_freq=None,
+          layout="neox", mscale=1.0):
+        if inv_freq is not None:     # these mistakes concern the plain-theta path
+            return _orig["qkv_prologue"](q, k_new, v_new, w_q, w_k, eps, theta, pos,
+                                         k_cache, v_cache, inv_freq, layout, mscale)
         q = np.array(q, np.float64)
         k = np.array(k_new, np.float64)
         v = np.array(v_new, np.float64)
@@ -270,6 +314,13 @@ MUTANTS = {
     "prologue_wk_for_q": {"qkv_prologue": _prologue_variant("wk_for_q")},
     "prologue_rotates_v": {"qkv_prologue": _prologue_variant("rotate_v")},
     "prologue_writes_pos_plus_one": {"qkv_prologue": _prologue_variant("pos_plus_one")},
+    "rope_interleaved_pairs_swapped": {"rope": _rope_general_pairs_swapped},
+    "rope_mscale_squared": {"rope": _rope_general_mscale_squared},
+    "rope_layout_ignored": {"rope": _rope_general_ignores_layout},
+    "yarn_ramp_inverted": {"rope_inv_freq_scaled": _table_variant("yarn_ramp_inverted")},
+    "ntk_base_times_factor": {"rope_inv_freq_scaled": _table_variant("ntk_base_linear")},
+    "linear_multiplies_frequencies": {"rope_inv_freq_scaled": _table_variant("linear_multiplies")},
+    "yarn_without_mscale": {"rope_inv_freq_scaled": _table_variant("yarn_no_mscale")},
 }
 
 

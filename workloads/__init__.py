@@ -118,6 +118,10 @@ class Workload:
     w_q: Optional[np.ndarray]        # float32 [D]
     w_k: Optional[np.ndarray]
     peaky_rows: Optional[np.ndarray] = None  # int64 [B,Hkv,m] rows of K scaled by 4
+    rope_layout: str = "neox"        # RoPE pairs: "neox" (i, i+D/2) | "interleaved" (2i, 2i+1)
+    # RoPE context-extension scheme (None: the plain theta table), e.g.
+    # dict(kind="yarn", factor=4.0, orig_ctx=4096, beta_fast=32.0, beta_slow=1.0)
+    rope_scaling: Optional[dict] = None
 
     @property
     def prologue(self) -> bool:
@@ -169,7 +173,9 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
     """Build workload ``name`` (a key of CONFIGS) with optional overrides.
 
     Overrides accept any base key (B, Hq, Hkv, D, L, window, theta, norm,
-    out_dtype, part_tokens, peaky, lmin) plus ``T`` for ragged layouts.
+    out_dtype, part_tokens, peaky, lmin) plus ``T`` for ragged layouts and
+    ``rope_layout`` / ``rope_scaling`` (the RoPE variant; no effect on the
+    random draws).
     Layouts:
       last       T = L, new token at pos = L-1, lens = L
       append     T = L + 64, new token at pos = L, lens = L + 1
@@ -237,4 +243,5 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
         window=int(p["window"]), theta=float(p["theta"]), eps=1e-6,
         out_dtype=p["out_dtype"], part_tokens=int(p["part_tokens"]),
         q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
-        w_q=w_q, w_k=w_k, peaky_rows=peaky_rows)
+        w_q=w_q, w_k=w_k, peaky_rows=peaky_rows,
+        rope_layout=p.get("rope_layout", "neox"), rope_scaling=p.get("rope_scaling"))
