@@ -48,6 +48,7 @@ WORKLOAD_NAMES = {
     "3": "Llama-3-8B-shaped batched decode, ragged lengths",
     "4": "long-context flash-decoding, L=131072",
     "5": "70B-shaped sliding-window GQA decode (8:1)",
+    "6": "draft-token verification: S=4 causal query tokens per sequence, Llama-3-8B shape",
 }
 
 
@@ -242,6 +243,8 @@ def main():
         w.part_tokens = args.part_tokens
     kvb = workloads.kv_bytes(w)
     mode = args.mode
+    if w.S > 1 and mode == "fused":     # the one-launch step runs one token per sequence
+        mode = "split"
     step = DeviceStep(w, device=dev, mode=mode)
     flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
                                                           device=dev)
@@ -336,6 +339,7 @@ def main():
         "config": {
             "workload": WORKLOAD_NAMES[args.workload],
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D, "T": w.T,
+            "query_tokens": w.S,
             "window": w.window, "part_tokens": w.part_tokens, "out_dtype": w.out_dtype,
             "path": mode,
             "prologue": ("qk_rmsnorm+rope+append" if w.w_q is not None else

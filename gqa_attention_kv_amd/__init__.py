@@ -8,9 +8,11 @@ there is no fallback.  Importing fails loudly when the library is missing.
 
 Functions follow the C entry points' names without the ``gqa_`` prefix:
 ``qkv_prologue``, ``qkv_prologue_ex``, ``attn_decode``,
-``attn_decode_splitk``, ``attn_decode_merge``, ``decode_step``,
+``attn_decode_splitk``, ``attn_decode_merge``, ``attn_decode_multi``,
+``attn_decode_splitk_multi``, ``attn_decode_merge_multi``, ``decode_step``,
 ``decode_step_ex``, ``rope_table``, ``splitk_workspace_bytes``,
-``decode_step_workspace_bytes``, ``num_partitions``.
+``splitk_multi_workspace_bytes``, ``decode_step_workspace_bytes``,
+``num_partitions``.
 """
 from __future__ import annotations
 
@@ -26,6 +28,8 @@ __all__ = [
     "GQAError", "lib", "qkv_prologue", "qkv_prologue_ex", "attn_decode",
     "attn_decode_splitk", "attn_decode_merge", "splitk_workspace_bytes", "num_partitions",
     "decode_step", "decode_step_ex", "decode_step_workspace_bytes", "rope_table",
+    "attn_decode_multi", "attn_decode_splitk_multi", "attn_decode_merge_multi",
+    "splitk_multi_workspace_bytes",
     "F32", "BF16", "SYMBOLS", "ROPE_NEOX", "ROPE_INTERLEAVED", "ROPE_KINDS",
 ]
 
@@ -62,8 +66,14 @@ SYMBOLS = {
                              _i, _f, _i, _p, _sz, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
     "gqa_status_string": (ctypes.c_char_p, [_i]),
     "gqa_rope_table": (_i, [_i, _i, _d, _d, _i, _d, _d, _p, _p]),
-    "gqa_qkv_prologue_ex": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _p,
-                                 _p, _p, _i, _i, _i, _i, _i, _p]),
+    "gqa_qkv_prologue_ex": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _i,
+                                 _p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "gqa_attn_decode_multi": (_i, [_p, _i, _p, _p, _p, _i, _i, _f, _p, _i, _p, _i, _i, _i, _i,
+                                   _i, _p]),
+    "gqa_splitk_multi_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "gqa_attn_decode_splitk_multi": (_i, [_p, _i, _p, _p, _p, _i, _i, _f, _i, _p, _sz,
+                                          _i, _i, _i, _i, _i, _p]),
+    "gqa_attn_decode_merge_multi": (_i, [_p, _sz, _i, _i, _i, _p, _i, _p, _i, _i, _i, _i, _p]),
     "gqa_decode_step_ex": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _p,
                                 _p, _p, _i, _f, _i, _p, _sz, _p, _i, _p, _p, _i, _i, _i, _i,
                                 _i, _p]),
@@ -178,19 +188,43 @@ def qkv_prologue_ex(q, k_new, v_new, pos, k_cache, v_cache, inv_freq=None,
                     k_norm_w=None, eps: float = 1e-6, q_out=None):
     """``qkv_prologue`` with an explicit rotary table (host float64 [D/2] or
     None for no RoPE), magnitude factor and pair layout ("neox" or
-    "interleaved")."""
-    dev, B, Hq, Hkv, D, T, code, q_out = _prologue_checks(
-        q, k_new, v_new, pos, k_cache, v_cache, q_norm_w, k_norm_w, q_out)
+    "interleaved").  q [B,S,Hq,D] and k_new/v_new [B,S,Hkv,D] carry S tokens
+    per sequence (token s at position pos[b] + s); 3-D inputs mean S = 1.
+    Returns q_out float32 of q's shape."""
+    S = 1
+    if q.dim() == 4:
+        S = q.shape[1]
+        if k_new.dim() != 4 or v_new.dim() != 4 or k_new.shape[1] != S or v_new.shape[1] != S:
+            raise ValueError("q, k_new and v_new must have the same token count")
+        for t, w in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+            if t.stride(3) != 1 or t.stride(2) != t.shape[3] or t.stride(1) != t.shape[2] * t.shape[3]:
+                raise ValueError(f"{w}: tokens and heads must be dense inside a batch row")
+        qv = q.select(1, 0)
+        kv_, vv = k_new.select(1, 0), v_new.select(1, 0)
+        dev, B, Hq, Hkv, D, T, code, _ = _prologue_checks(
+            qv, kv_, vv, pos, k_cache, v_cache, q_norm_w, k_norm_w,
+            torch.empty(0, device=k_cache.device))
+        if q_out is None:
+            q_out = torch.empty((B, S, Hq, D), dtype=torch.float32, device=dev)
+        _dev(q_out, "q_out", dev)
+        _contig(q_out, "q_out")
+        if q_out.dtype != torch.float32 or tuple(q_out.shape) != (B, S, Hq, D):
+            raise ValueError("q_out must be float32 [B,S,Hq,D]")
+    else:
+        dev, B, Hq, Hkv, D, T, code, q_out = _prologue_checks(
+            q, k_new, v_new, pos, k_cache, v_cache, q_norm_w, k_norm_w, q_out)
     f = _host_table(inv_freq, D)
     _check(lib.gqa_qkv_prologue_ex(
         _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0), k_new.stride(0),
         _ptr(q_norm_w), _ptr(k_norm_w), float(eps), None if f is None else f.ctypes.data,
-        float(rope_mscale), _layout_code(rope_layout), _ptr(pos), _ptr(q_out),
+        float(rope_mscale), _layout_code(rope_layout), _ptr(pos), int(S), _ptr(q_out),
         _ptr(k_cache), _ptr(v_cache), B, Hq, Hkv, D, T, _stream(dev)))
     return q_out
 
 
 def _prologue_checks(q, k_new, v_new, pos, k_cache, v_cache, q_norm_w, k_norm_w, q_out):
+    """Checks of the single-token layout; q_out may be an empty placeholder
+    (numel 0) that the caller checks itself."""
     dev = k_cache.device
     for t, w in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (pos, "pos"),
                  (k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -220,10 +254,11 @@ def _prologue_checks(q, k_new, v_new, pos, k_cache, v_cache, q_norm_w, k_norm_w,
             _contig(w, nm)
     if q_out is None:
         q_out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    _dev(q_out, "q_out", dev)
-    _contig(q_out, "q_out")
-    if q_out.dtype != torch.float32 or tuple(q_out.shape) != (B, Hq, D):
-        raise ValueError("q_out must be float32 [B,Hq,D]")
+    if q_out.numel():
+        _dev(q_out, "q_out", dev)
+        _contig(q_out, "q_out")
+        if q_out.dtype != torch.float32 or tuple(q_out.shape) != (B, Hq, D):
+            raise ValueError("q_out must be float32 [B,Hq,D]")
     return dev, B, Hq, Hkv, D, T, code, q_out
 
 
@@ -318,6 +353,77 @@ def workspace_views(workspace, B: int, Hq: int, D: int, T: int, window: int,
     lse = flat[: n_lse * 4].view(torch.float32).view(B, Hq, npart)
     o = flat[off: off + n_lse * D * 4].view(torch.float32).view(B, Hq, npart, D)
     return lse, o
+
+
+def _multi_common(q, k_cache, v_cache, lens):
+    if q.dim() != 4:
+        raise ValueError("q must be [B,S,Hq,D]")
+    B, S, Hq, D = q.shape
+    dev, _, _, Hkv, _, T = _attn_common(q.reshape(B, S * Hq, D), k_cache, v_cache, lens)
+    return dev, B, S, Hq, Hkv, D, T
+
+
+def attn_decode_multi(q, k_cache, v_cache, lens, window: int = 0, scale: float = 0.0,
+                      out=None, out_dtype=torch.float32, lse_out=None):
+    """S causal query tokens per sequence (q [B,S,Hq,D]) in one pass per
+    (sequence, KV head); token s attends lens[b] - (S-1-s) rows.  Returns out
+    [B,S,Hq,D]; writes the LSE into ``lse_out`` (float32 [B,S,Hq]) when given."""
+    dev, B, S, Hq, Hkv, D, T = _multi_common(q, k_cache, v_cache, lens)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=dev)
+    _dev(out, "out", dev)
+    _contig(out, "out")
+    if tuple(out.shape) != (B, S, Hq, D):
+        raise ValueError("out must be [B,S,Hq,D]")
+    if lse_out is not None:
+        _lse_check(lse_out.reshape(B, S * Hq), B, S * Hq, dev)
+    _check(lib.gqa_attn_decode_multi(
+        _ptr(q), _dtype_code(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(S),
+        int(window), float(scale), _ptr(out), _dtype_code(out, "out"), _ptr(lse_out),
+        B, Hq, Hkv, D, T, _stream(dev)))
+    return out
+
+
+def splitk_multi_workspace_bytes(B: int, S: int, Hq: int, D: int, T: int, window: int,
+                                 part_tokens: int) -> int:
+    return int(lib.gqa_splitk_multi_workspace_bytes(B, S, Hq, D, T, window, part_tokens))
+
+
+def attn_decode_splitk_multi(q, k_cache, v_cache, lens, part_tokens: int, window: int = 0,
+                             scale: float = 0.0, workspace=None):
+    """Partition pass of the split-K multi-token decode; returns the workspace."""
+    dev, B, S, Hq, Hkv, D, T = _multi_common(q, k_cache, v_cache, lens)
+    need = splitk_multi_workspace_bytes(B, S, Hq, D, T, window, part_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", dev)
+    _contig(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gqa_attn_decode_splitk_multi(
+        _ptr(q), _dtype_code(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(S),
+        int(window), float(scale), int(part_tokens), _ptr(workspace), nbytes,
+        B, Hq, Hkv, D, T, _stream(dev)))
+    return workspace
+
+
+def attn_decode_merge_multi(workspace, B: int, S: int, Hq: int, D: int, T: int,
+                            part_tokens: int, window: int = 0, out=None,
+                            out_dtype=torch.float32, lse_out=None):
+    """Merge of the multi-token partitions; returns out [B,S,Hq,D]."""
+    dev = workspace.device
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=dev)
+    _dev(out, "out", dev)
+    _contig(out, "out")
+    if tuple(out.shape) != (B, S, Hq, D):
+        raise ValueError("out must be [B,S,Hq,D]")
+    if lse_out is not None:
+        _lse_check(lse_out.reshape(B, S * Hq), B, S * Hq, dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gqa_attn_decode_merge_multi(
+        _ptr(workspace), nbytes, int(S), int(window), int(part_tokens), _ptr(out),
+        _dtype_code(out, "out"), _ptr(lse_out), B, Hq, D, T, _stream(dev)))
+    return out
 
 
 def decode_step_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, T: int, window: int,

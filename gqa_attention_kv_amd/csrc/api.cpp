@@ -35,17 +35,29 @@ int check_shapes(int B, int Hq, int Hkv, int D, int T) {
   return GQA_OK;
 }
 
-int num_parts(int T, int window, int part_tokens) {
-  const int64_t span = window > 0 && window < T ? window : T;
+// Rows the S tokens of one sequence attend together span at most T, or
+// window + S - 1 with a window (token s's window ends S-1-s rows earlier).
+int num_parts(int T, int window, int part_tokens, int S = 1) {
+  const int64_t w = window > 0 ? (int64_t)window + S - 1 : (int64_t)T;
+  const int64_t span = w < T ? w : T;
   return (int)((span + part_tokens - 1) / part_tokens);
 }
 
 // Split-K checks; B * Hkv * partitions is the attention pass's grid.
-int check_split(int B, int Hkv, int T, int window, int part_tokens) {
+int check_split(int B, int Hkv, int T, int window, int part_tokens, int S = 1) {
   if (part_tokens < 1) return GQA_ERR_VALUE;
   if ((int64_t)T + part_tokens >= INT32_MAX) return GQA_ERR_SHAPE;
-  if ((int64_t)B * Hkv * num_parts(T, window, part_tokens) > kMaxWorkgroups)
+  if ((int64_t)B * Hkv * num_parts(T, window, part_tokens, S) > kMaxWorkgroups)
     return GQA_ERR_SHAPE;
+  return GQA_OK;
+}
+
+// S query tokens per sequence: all G * S (token, head) rows of a KV head
+// share one 16-column matrix tile.
+int check_tokens(int S, int B, int Hq, int Hkv) {
+  if (S < 1 || S > 16) return S < 1 ? GQA_ERR_SHAPE : GQA_ERR_UNSUPPORTED;
+  if ((Hq / Hkv) * S > 16) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)B * S * Hq > kMaxWorkgroups) return GQA_ERR_SHAPE;
   return GQA_OK;
 }
 
@@ -129,7 +141,7 @@ int gqa_qkv_prologue_ex(const void* q, const void* k_new, const void* v_new,
                         gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
                         const float* q_norm_w, const float* k_norm_w, float eps,
                         const double* inv_freq, double rope_mscale, int rope_layout,
-                        const int32_t* pos, float* q_out,
+                        const int32_t* pos, int S, float* q_out,
                         uint16_t* k_cache, uint16_t* v_cache,
                         int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
   if (!q || !k_new || !v_new || !pos || !q_out || !k_cache || !v_cache) return GQA_ERR_NULL;
@@ -137,7 +149,8 @@ int gqa_qkv_prologue_ex(const void* q, const void* k_new, const void* v_new,
   int rc = check_shapes(B, Hq, Hkv, D, T);
   if (rc) return rc;
   if (!dtype_ok(in_dtype)) return GQA_ERR_UNSUPPORTED;
-  if (q_bstride < (int64_t)Hq * D || kv_bstride < (int64_t)Hkv * D) return GQA_ERR_SHAPE;
+  if (S < 1 || (int64_t)B * S * (Hq + Hkv) > kMaxIndex / D) return GQA_ERR_SHAPE;
+  if (q_bstride < (int64_t)S * Hq * D || kv_bstride < (int64_t)S * Hkv * D) return GQA_ERR_SHAPE;
   if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
   if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
   if ((rc = check_rope(inv_freq, rope_mscale, rope_layout, D))) return rc;
@@ -155,7 +168,7 @@ int gqa_qkv_prologue_ex(const void* q, const void* k_new, const void* v_new,
   a.rope_mscale = (float)rope_mscale;
   if (a.rope)
     for (int i = 0; i < D / 2; ++i) a.inv_freq[i] = inv_freq[i];
-  a.pos = pos; a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.pos = pos; a.S = S; a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   return gqa::launch_prologue(a, stream);
 }
@@ -174,7 +187,7 @@ int gqa_qkv_prologue(const void* q, const void* k_new, const void* v_new,
     f = table;
   }
   return gqa_qkv_prologue_ex(q, k_new, v_new, in_dtype, q_bstride, kv_bstride, q_norm_w,
-                             k_norm_w, eps, f, 1.0, GQA_ROPE_NEOX, pos, q_out, k_cache,
+                             k_norm_w, eps, f, 1.0, GQA_ROPE_NEOX, pos, 1, q_out, k_cache,
                              v_cache, B, Hq, Hkv, D, T, stream);
 }
 
@@ -183,16 +196,27 @@ int gqa_attn_decode(const void* q, gqa_dtype_t q_dtype,
                     const int32_t* lens, int window, float scale,
                     void* out, gqa_dtype_t out_dtype, float* lse_out,
                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  return gqa_attn_decode_multi(q, q_dtype, k_cache, v_cache, lens, 1, window, scale, out,
+                               out_dtype, lse_out, B, Hq, Hkv, D, T, stream);
+}
+
+int gqa_attn_decode_multi(const void* q, gqa_dtype_t q_dtype,
+                          const uint16_t* k_cache, const uint16_t* v_cache,
+                          const int32_t* lens, int S, int window, float scale,
+                          void* out, gqa_dtype_t out_dtype, float* lse_out,
+                          int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !lens || !out) return GQA_ERR_NULL;
   int rc = check_shapes(B, Hq, Hkv, D, T);
   if (rc) return rc;
+  if ((rc = check_tokens(S, B, Hq, Hkv))) return rc;
   if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
   if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(lens, 4) || !aligned(lse_out, 4))
     return GQA_ERR_ALIGN;
   gqa::KernelArgs a{};
-  a.q = q; a.q_bstride = (int64_t)Hq * D; a.in_bf16 = q_dtype == GQA_BF16;
+  a.q = q; a.q_bstride = (int64_t)S * Hq * D; a.q_sstride = (int64_t)Hq * D; a.S = S;
+  a.in_bf16 = q_dtype == GQA_BF16;
   a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens; a.window = window;
   a.qscale = softmax_qscale(scale, D);
   a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
@@ -206,12 +230,18 @@ int gqa_num_partitions(int T, int window, int part_tokens) {
   return num_parts(T, window, part_tokens);
 }
 
-static size_t lse_bytes(int B, int Hq, int np) { return (size_t)B * Hq * np * sizeof(float); }
+static size_t lse_bytes(size_t rows, int np) { return rows * np * sizeof(float); }
 
 size_t gqa_splitk_workspace_bytes(int B, int Hq, int D, int T, int window, int part_tokens) {
-  if (B < 1 || Hq < 1 || D < 1 || T < 1 || part_tokens < 1) return 0;
-  const int np = gqa_num_partitions(T, window, part_tokens);
-  return align256(lse_bytes(B, Hq, np)) + (size_t)B * Hq * np * D * sizeof(float);
+  return gqa_splitk_multi_workspace_bytes(B, 1, Hq, D, T, window, part_tokens);
+}
+
+size_t gqa_splitk_multi_workspace_bytes(int B, int S, int Hq, int D, int T, int window,
+                                        int part_tokens) {
+  if (B < 1 || S < 1 || Hq < 1 || D < 1 || T < 1 || part_tokens < 1) return 0;
+  const int np = num_parts(T, window, part_tokens, S);
+  const size_t rows = (size_t)B * S * Hq;
+  return align256(lse_bytes(rows, np)) + (size_t)rows * np * D * sizeof(float);
 }
 
 int gqa_attn_decode_splitk(const void* q, gqa_dtype_t q_dtype,
@@ -219,26 +249,38 @@ int gqa_attn_decode_splitk(const void* q, gqa_dtype_t q_dtype,
                            const int32_t* lens, int window, float scale,
                            int part_tokens, void* workspace, size_t workspace_bytes,
                            int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  return gqa_attn_decode_splitk_multi(q, q_dtype, k_cache, v_cache, lens, 1, window, scale,
+                                      part_tokens, workspace, workspace_bytes, B, Hq, Hkv, D,
+                                      T, stream);
+}
+
+int gqa_attn_decode_splitk_multi(const void* q, gqa_dtype_t q_dtype,
+                                 const uint16_t* k_cache, const uint16_t* v_cache,
+                                 const int32_t* lens, int S, int window, float scale,
+                                 int part_tokens, void* workspace, size_t workspace_bytes,
+                                 int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !lens || !workspace) return GQA_ERR_NULL;
   int rc = check_shapes(B, Hq, Hkv, D, T);
   if (rc) return rc;
-  if ((rc = check_split(B, Hkv, T, window, part_tokens))) return rc;
+  if ((rc = check_tokens(S, B, Hq, Hkv))) return rc;
+  if ((rc = check_split(B, Hkv, T, window, part_tokens, S))) return rc;
   if (!dtype_ok(q_dtype)) return GQA_ERR_UNSUPPORTED;
   if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(lens, 4) || !aligned(workspace, 256))
     return GQA_ERR_ALIGN;
-  if (workspace_bytes < gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens))
+  if (workspace_bytes < gqa_splitk_multi_workspace_bytes(B, S, Hq, D, T, window, part_tokens))
     return GQA_ERR_WORKSPACE;
-  const int np = gqa_num_partitions(T, window, part_tokens);
+  const int np = num_parts(T, window, part_tokens, S);
   gqa::KernelArgs a{};
-  a.q = q; a.q_bstride = (int64_t)Hq * D; a.in_bf16 = q_dtype == GQA_BF16;
+  a.q = q; a.q_bstride = (int64_t)S * Hq * D; a.q_sstride = (int64_t)Hq * D; a.S = S;
+  a.in_bf16 = q_dtype == GQA_BF16;
   a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens; a.window = window;
   a.qscale = softmax_qscale(scale, D);
   a.part_tokens = part_tokens; a.num_parts = np;
   a.ws_lse = static_cast<float*>(workspace);
   a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    align256(lse_bytes(B, Hq, np)));
+                                    align256(lse_bytes((size_t)B * S * Hq, np)));
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   return gqa::launch_attn_split(a, stream);
 }
@@ -247,23 +289,32 @@ int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
                           int window, int part_tokens,
                           void* out, gqa_dtype_t out_dtype, float* lse_out,
                           int B, int Hq, int D, int T, hipStream_t stream) {
+  return gqa_attn_decode_merge_multi(workspace, workspace_bytes, 1, window, part_tokens, out,
+                                     out_dtype, lse_out, B, Hq, D, T, stream);
+}
+
+int gqa_attn_decode_merge_multi(const void* workspace, size_t workspace_bytes, int S,
+                                int window, int part_tokens,
+                                void* out, gqa_dtype_t out_dtype, float* lse_out,
+                                int B, int Hq, int D, int T, hipStream_t stream) {
   if (!workspace || !out) return GQA_ERR_NULL;
-  if (B < 1 || Hq < 1 || T < 1) return GQA_ERR_SHAPE;
-  if ((int64_t)B * Hq > kMaxWorkgroups) return GQA_ERR_SHAPE;
+  if (B < 1 || Hq < 1 || T < 1 || S < 1) return GQA_ERR_SHAPE;
+  if ((int64_t)B * S * Hq > kMaxWorkgroups) return GQA_ERR_SHAPE;
+  if (S > 16) return GQA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return GQA_ERR_UNSUPPORTED;
-  int rc = check_split(1, 1, T, window, part_tokens);
+  int rc = check_split(1, 1, T, window, part_tokens, S);
   if (rc) return rc;
   if (!dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
   if (!aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse_out, 4)) return GQA_ERR_ALIGN;
-  if (workspace_bytes < gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens))
+  if (workspace_bytes < gqa_splitk_multi_workspace_bytes(B, S, Hq, D, T, window, part_tokens))
     return GQA_ERR_WORKSPACE;
-  const int np = gqa_num_partitions(T, window, part_tokens);
+  const int np = num_parts(T, window, part_tokens, S);
   gqa::MergeArgs a{};
   a.ws_lse = static_cast<const float*>(workspace);
   a.ws_o = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
-                                          align256(lse_bytes(B, Hq, np)));
+                                          align256(lse_bytes((size_t)B * S * Hq, np)));
   a.num_parts = np; a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
-  a.B = B; a.Hq = Hq; a.D = D;
+  a.B = B * S; a.Hq = Hq; a.D = D;       // the merge works on rows of [B*S, Hq]
   return gqa::launch_merge(a, stream);
 }
 
@@ -317,9 +368,10 @@ int gqa_decode_step_ex(const void* q, const void* k_new, const void* v_new,
   a.lens = lens; a.window = window; a.qscale = softmax_qscale(scale, D);
   a.part_tokens = part_tokens; a.num_parts = np;
   char* ws = static_cast<char*>(workspace);
-  const size_t lse_sz = align256(lse_bytes(B, Hq, np));
+  const size_t lse_sz = align256(lse_bytes((size_t)B * Hq, np));
   a.ws_lse = reinterpret_cast<float*>(ws);
   a.ws_o = reinterpret_cast<float*>(ws + lse_sz);
+  a.S = 1; a.q_sstride = (int64_t)Hq * D;
   a.ws_cnt = reinterpret_cast<uint32_t*>(
       ws + align256(gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens)));
   a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;

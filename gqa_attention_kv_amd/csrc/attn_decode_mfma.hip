@@ -290,10 +290,15 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
   }
 }
 
-template <int D, int G, int NW, typename IT, Mode MODE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(G >= 16 ? 2 : GQA_WAVES_PER_EU))) void
+// CT is the column capacity: the NC = G * S query rows of one KV head (G
+// heads of the group times S tokens of the sequence, NC <= CT) are the
+// columns of the 16-column MFMA tile; column c is token c / G, head c % G.
+// MT: several tokens (S > 1), whose columns attend different row ranges;
+// the single-token instances keep the plainer inner loop.
+template <int D, int CT, int NW, typename IT, Mode MODE, bool MT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CT >= 16 ? 2 : GQA_WAVES_PER_EU))) void
 attn_decode_mfma_kernel(const KernelArgs a) {
-  static_assert(G <= 16, "one 16-column MFMA tile holds at most 16 heads");
+  static_assert(CT <= 16, "one 16-column MFMA tile holds at most 16 query rows");
   constexpr int KC = D / 32;          // QK calls per tile (per q part)
   constexpr int VB = D / 16;          // PV column blocks
   constexpr int HALF = D / 2;
@@ -302,7 +307,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   constexpr bool kLo = sizeof(IT) == 4 || MODE == Mode::Step;
   // With at most 8 heads the lo part takes columns 8..15 of the same
   // operand (column n + 8 holds head n's lo part) instead of a second call.
-  constexpr bool kFold = kLo && G <= 8;
+  constexpr bool kFold = kLo && CT <= 8;
   constexpr bool kPartial = MODE != Mode::Final;
 
   // One-dimensional grid.  The hardware hands workgroup i to XCD i % 8.
@@ -337,29 +342,45 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   const int Hq = a.Hq;
   const int Hkv = a.Hkv;
   const int num_parts = a.num_parts;
+  const int S = MT ? a.S : 1;         // tokens per sequence
+  const int G = MT ? Hq / Hkv : CT;   // heads per KV head (CT itself with one token)
+  const int NC = MT ? G * S : CT;     // columns in use
 
-  const int nrow = min(max(a.lens[b], 0), T);
-  const int lo = a.window > 0 ? max(0, nrow - a.window) : 0;
+  // Token s of sequence b attends rows [lo_s, n_s): n_s = lens[b] - (S-1-s)
+  // clamped to [0, T], lo_s = n_s - window (or 0).  The workgroup streams
+  // the union [lo_0, n_{S-1}), or its partition of that range.
+  auto tok_end = [&](int st) {
+    return (int)min(max((int64_t)a.lens[b] - (S - 1 - st), (int64_t)0), (int64_t)T);
+  };
+  auto tok_lo = [&](int st) { return a.window > 0 ? max(0, tok_end(st) - a.window) : 0; };
+  const int nrow = MT ? tok_end(S - 1) : min(max(a.lens[b], 0), T);
+  const int lo = MT ? tok_lo(0) : (a.window > 0 ? max(0, nrow - a.window) : 0);
   // Rows this workgroup attends: the whole range, or its partition.
   int t0 = lo, t1 = nrow;
   if (kPartial) {
     t0 = min(lo + part * a.part_tokens, nrow);
     t1 = min(t0 + a.part_tokens, nrow);
   }
-  const int64_t head0 = (int64_t)b * Hq + (int64_t)g * G;
+  // output row (of [B, S, Hq]) of column c
+  const int64_t head0 = ((int64_t)b * S) * Hq + (int64_t)g * G;
+  auto orow = [&](int c) -> int64_t {
+    if constexpr (MT) return ((int64_t)b * S + c / G) * Hq + (int64_t)g * G + c % G;
+    return head0 + c;
+  };
 
   if constexpr (MODE != Mode::Step) {
     if (t0 >= t1) {   // nothing to attend in this range (uniform over the workgroup)
       if (MODE == Mode::Split) {
-        for (int h = threadIdx.x; h < G; h += NW * 64)
-          a.ws_lse[(head0 + h) * num_parts + part] = -INFINITY;
+        for (int c = threadIdx.x; c < NC; c += NW * 64)
+          a.ws_lse[orow(c) * num_parts + part] = -INFINITY;
       } else {
-        for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-          if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[head0 * D + e] = 0;
-          else reinterpret_cast<float*>(a.out)[head0 * D + e] = 0.0f;
+        for (int e = threadIdx.x; e < NC * D; e += NW * 64) {
+          const int64_t oi = orow(e / D) * D + e % D;
+          if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = 0;
+          else reinterpret_cast<float*>(a.out)[oi] = 0.0f;
         }
         if (a.lse_out != nullptr)
-          for (int h = threadIdx.x; h < G; h += NW * 64) a.lse_out[head0 + h] = -INFINITY;
+          for (int c = threadIdx.x; c < NC; c += NW * 64) a.lse_out[orow(c)] = -INFINITY;
       }
       return;
     }
@@ -415,12 +436,19 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     issue(bf[1], rcur + 16);
   };
 
-  // q for head hn = n (n % 8 when folded; padding columns hn >= G load head
-  // G-1 -- no branch around the loads -- and are zeroed): lane holds
-  // elements 32c + 8lg + j.
+  // q of column hn = n (n % 8 when folded; padding columns hn >= NC load
+  // column NC-1 -- no branch around the loads -- and are zeroed): lane
+  // holds elements 32c + 8lg + j of token hq / G, head hq % G.
   const int hn = kFold ? (n & 7) : n;
-  const float keep = hn < G ? 1.0f : 0.0f;
-  const int hq = min(hn, G - 1);
+  const float keep = hn < NC ? 1.0f : 0.0f;
+  const int hq = min(hn, NC - 1);
+  const int tq = MT ? hq / G : 0;     // token and head of column hq
+  const int hh = MT ? hq % G : hq;
+  const int64_t qoff = (int64_t)b * a.q_bstride + (int64_t)tq * a.q_sstride +
+                       (int64_t)(g * G + hh) * D;
+  // Rows column hn may attend, within this workgroup's range.
+  const int clo = MT ? max(t0, tok_lo(tq)) : t0;
+  const int chi = MT ? min(t1, tok_end(tq)) : t1;
   float qf[KC][8];
   // Step: the appended row (bf16 K row, then V row, per wave), substituted
   // into the one tile that holds row psub.
@@ -442,8 +470,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     const bool need_k = attended || kwrite;
     // Every global load of the prologue is issued before the first tiles:
     // loads complete in order, so waiting for these never waits for a tile.
-    const IT* qs = reinterpret_cast<const IT*>(a.q) + (int64_t)b * a.q_bstride +
-                   (int64_t)(g * G + hq) * D;
+    const IT* qs = reinterpret_cast<const IT*>(a.q) + qoff;
 #pragma unroll
     for (int c = 0; c < KC; ++c) load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
     const bool qnorm = has_pro && a.wq != nullptr;
@@ -583,8 +610,8 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     for (int c = 0; c < KC; ++c)
 #pragma unroll
       for (int j = 0; j < 8; ++j) qf[c][j] *= keep;
-    if (has_pro && a.q_out != nullptr && part == 0 && wave == 0 && n < G) {
-      float* qo = a.q_out + (head0 + n) * D;
+    if (has_pro && a.q_out != nullptr && part == 0 && wave == 0 && n < NC) {
+      float* qo = a.q_out + orow(n) * D;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         *reinterpret_cast<float4*>(qo + 32 * c + 8 * lg) =
@@ -596,7 +623,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   } else {
     // The q loads go out first and the first tiles right behind them, so
     // waiting for q never waits for a tile (loads complete in order).
-    const IT* qs = reinterpret_cast<const IT*>(a.q) + (head0 + hq) * D;
+    const IT* qs = reinterpret_cast<const IT*>(a.q) + qoff;
 #pragma unroll
     for (int c = 0; c < KC; ++c) load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
     __builtin_amdgcn_sched_barrier(0);
@@ -690,20 +717,25 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = base + 4 * r + lg < t1;
+      const int row = base + 4 * r + lg;
+      const bool ok = MT ? (row >= clo && row < chi) : row < t1;
       p[r] = ok ? s[r] * qscale : -INFINITY;
       tmax = fmaxf(tmax, p[r]);
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // finite: the unit's first tile always holds a valid row
+    // With several tokens a column may have seen no valid row yet (m = mnew
+    // = -inf): exponents are then taken against 0, which keeps alpha and p
+    // at 0 instead of NaN.  With one token the unit's first tile always
+    // holds a valid row, so mnew is finite.
     const float mnew = fmaxf(m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    const float mref = MT && mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - mref);
     m = mnew;
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(p[r] - mnew);
+      p[r] = __builtin_amdgcn_exp2f(p[r] - mref);
       psum += p[r];
     }
     l = l * alpha + psum;
@@ -761,17 +793,17 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
 
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_o[NW][G][D];
-  if (lg == 0 && n < G) {
+  __shared__ float sm_m[NW][CT];
+  __shared__ float sm_l[NW][CT];
+  __shared__ float sm_o[NW][CT][D];
+  if (lg == 0 && n < NC) {
     sm_m[wave][n] = m;
     sm_l[wave][n] = l;
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 4 * lg + r;
-    if (h < G) {
+    if (h < NC) {
 #pragma unroll
       for (int blk = 0; blk < VB; ++blk) sm_o[wave][h][VB * n + blk] = o[blk][r];
     }
@@ -780,9 +812,11 @@ attn_decode_mfma_kernel(const KernelArgs a) {
 
   // Step with a single partition writes the final output like Final.
   const bool write_final = MODE == Mode::Final || (MODE == Mode::Step && num_parts == 1);
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int h = idx / D;
+  for (int idx = threadIdx.x; idx < CT * D; idx += NW * 64) {
+    const int h = idx / D;          // column
     const int d = idx % D;
+    if (h >= NC) break;             // columns only grow with idx
+    const int64_t oh = orow(h);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
@@ -798,21 +832,21 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     const float ov = any ? A / L : 0.0f;
     const float lse = any ? (M + log2f(L)) * kLn2 : -INFINITY;
     if (write_final) {
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[(head0 + h) * D + d] = f32_to_bf16(ov);
-      else reinterpret_cast<float*>(a.out)[(head0 + h) * D + d] = ov;
-      if (d == 0 && a.lse_out != nullptr) a.lse_out[head0 + h] = lse;
+      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oh * D + d] = f32_to_bf16(ov);
+      else reinterpret_cast<float*>(a.out)[oh * D + d] = ov;
+      if (d == 0 && a.lse_out != nullptr) a.lse_out[oh] = lse;
     } else if (MODE == Mode::Split) {
-      if (any) a.ws_o[((head0 + h) * num_parts + part) * D + d] = ov;
-      if (d == 0) a.ws_lse[(head0 + h) * num_parts + part] = lse;
+      if (any) a.ws_o[(oh * num_parts + part) * D + d] = ov;
+      if (d == 0) a.ws_lse[oh * num_parts + part] = lse;
     } else {
       // Agent-scope stores write through to the coherence point, so the
       // merging workgroup (possibly on another XCD) can read them without
       // any L2 writeback.
       if (any)
-        __hip_atomic_store(a.ws_o + ((head0 + h) * num_parts + part) * D + d, ov,
+        __hip_atomic_store(a.ws_o + (oh * num_parts + part) * D + d, ov,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0)
-        __hip_atomic_store(a.ws_lse + (head0 + h) * num_parts + part, lse, __ATOMIC_RELAXED,
+        __hip_atomic_store(a.ws_lse + oh * num_parts + part, lse, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -837,7 +871,8 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    merge_partials<D, G, NW>(a, head0);
+    // Step runs one token (S = 1, NC = G = CT): column c is row head0 + c.
+    merge_partials<D, CT, NW>(a, (int64_t)b * Hq + (int64_t)g * G);
     if (threadIdx.x == 0)
       __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -847,17 +882,24 @@ attn_decode_mfma_kernel(const KernelArgs a) {
 #define GQA_MFMA_NW 4
 #endif
 
-template <int D, int G, typename IT, Mode MODE>
+template <int D, int CT, typename IT, Mode MODE>
 static int launch_mode(const KernelArgs& a, hipStream_t s) {
   constexpr int NW = GQA_MFMA_NW;
   const dim3 grid((MODE == Mode::Final ? 1 : a.num_parts) * a.B * a.Hkv);
-  hipLaunchKernelGGL((attn_decode_mfma_kernel<D, G, NW, IT, MODE>), grid, dim3(NW * 64), 0, s, a);
+  if (MODE != Mode::Step && a.S > 1)
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, IT, MODE, MODE != Mode::Step>), grid,
+                       dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, IT, MODE, false>), grid,
+                       dim3(NW * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
+// Column capacity: the smallest power of two holding G * S query rows.
 template <int D, typename IT, Mode MODE>
 static int dispatch_g(const KernelArgs& a, hipStream_t s) {
-  switch (a.Hq / a.Hkv) {
+  const int nc = (a.Hq / a.Hkv) * a.S;
+  switch (nc <= 1 ? 1 : nc <= 2 ? 2 : nc <= 4 ? 4 : nc <= 8 ? 8 : nc <= 16 ? 16 : 0) {
     case 1: return launch_mode<D, 1, IT, MODE>(a, s);
     case 2: return launch_mode<D, 2, IT, MODE>(a, s);
     case 4: return launch_mode<D, 4, IT, MODE>(a, s);

@@ -23,7 +23,8 @@ struct PrologueArgs {
   int rope;                    // 0: no RoPE
   int rope_interleaved;        // pairs (2i, 2i+1) instead of (i, i+D/2)
   float rope_mscale;           // magnitude factor of the rotated vectors
-  const int32_t* pos;
+  const int32_t* pos;          // token s of sequence b sits at pos[b] + s
+  int S;                       // tokens per sequence
   float* q_out;
   uint16_t* k_cache;
   uint16_t* v_cache;
@@ -33,9 +34,12 @@ struct PrologueArgs {
 
 // Arguments of the attention kernel in all three modes, passed by value.
 struct KernelArgs {
-  // query: dense [B,Hq,D] (Final, Split) or rows q_bstride apart (Step)
+  // query [B,S,Hq,D]: sequences q_bstride elements apart, tokens q_sstride
+  // apart, heads dense (Step: S = 1)
   const void* q;
   int64_t q_bstride;
+  int64_t q_sstride;
+  int S;                       // query tokens per sequence (causal among themselves)
   int in_bf16;                 // q (and, in Step, k_new / v_new) are bf16
   const uint16_t* k_cache;
   const uint16_t* v_cache;

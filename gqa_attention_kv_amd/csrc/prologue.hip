@@ -6,8 +6,9 @@
 // mean(x^2) + eps)), and the fusedtok 1.0.1 README "Operators" row RoPE
 // (interleaved and NeoX layouts, kv-cache position offset).
 //
-// Mapping: one head vector (a query head or a KV head of one sequence) per
-// D/2 consecutive lanes; lane i owns rotary pair i -- elements (i, i + D/2)
+// Mapping: one head vector (a query head or a KV head of one token of one
+// sequence; token s of sequence b sits at position pos[b] + s) per D/2
+// consecutive lanes; lane i owns rotary pair i -- elements (i, i + D/2)
 // in the NeoX layout, (2i, 2i + 1) in the interleaved one -- so the
 // rotation is lane-local and only the sum of squares crosses lanes.  For
 // D = 128 that is one wave64 per head vector.  The rotary angle
@@ -38,14 +39,15 @@ template <int D, typename IT>
 __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a) {
   constexpr int HALF = D / 2;        // lanes per head vector
   constexpr int VPB = 256 / HALF;    // head vectors per workgroup
-  const int Hq = a.Hq, Hkv = a.Hkv, T = a.T;
+  const int Hq = a.Hq, Hkv = a.Hkv, T = a.T, S = a.S;
   const int H = Hq + Hkv;
-  const int vec = blockIdx.x * VPB + threadIdx.x / HALF;
+  const int64_t vec = (int64_t)blockIdx.x * VPB + threadIdx.x / HALF;
   const int i = threadIdx.x % HALF;
-  const bool live = vec < a.B * H;   // lanes past the end compute on vector 0, store nothing
-  const int v = live ? vec : 0;
-  const int b = v / H;
-  const int hh = v % H;
+  const bool live = vec < (int64_t)a.B * S * H;   // lanes past the end: vector 0, no stores
+  const int64_t v = live ? vec : 0;
+  const int b = (int)(v / ((int64_t)S * H));
+  const int st = (int)(v / H % S);  // token
+  const int hh = (int)(v % H);
   const bool is_q = hh < Hq;
   const int g = hh - Hq;
   // elements of rotary pair i
@@ -53,9 +55,9 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
   const int e1 = a.rope_interleaved ? 2 * i + 1 : i + HALF;
 
   const IT* src = is_q ? reinterpret_cast<const IT*>(a.q) + (int64_t)b * a.q_bstride +
-                             (int64_t)hh * D
+                             ((int64_t)st * Hq + hh) * D
                        : reinterpret_cast<const IT*>(a.k_new) + (int64_t)b * a.kv_bstride +
-                             (int64_t)g * D;
+                             ((int64_t)st * Hkv + g) * D;
   float x0 = load_elem<IT>(src, e0);
   float x1 = load_elem<IT>(src, e1);
 
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
     x1 = x1 * r * w[e1];
   }
 
-  const int p = a.pos[b];
+  const int64_t p = (int64_t)a.pos[b] + st;
   if (a.rope) {
     double sn, cs;
     sincos((double)p * a.inv_freq[i], &sn, &cs);
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
   if (!live) return;
 
   if (is_q) {
-    float* dst = a.q_out + ((int64_t)b * Hq + hh) * D;
+    float* dst = a.q_out + (((int64_t)b * S + st) * Hq + hh) * D;
     dst[e0] = x0;
     dst[e1] = x1;
   } else if (p >= 0 && p < T) {
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
     a.k_cache[row + e0] = f32_to_bf16(x0);
     a.k_cache[row + e1] = f32_to_bf16(x1);
     const IT* vs = reinterpret_cast<const IT*>(a.v_new) + (int64_t)b * a.kv_bstride +
-                   (int64_t)g * D;
+                   ((int64_t)st * Hkv + g) * D;
     a.v_cache[row + e0] = to_bf16_bits(vs, e0);
     a.v_cache[row + e1] = to_bf16_bits(vs, e1);
   }
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
 template <int D, typename IT>
 static int launch_prologue_t(const PrologueArgs& a, hipStream_t s) {
   constexpr int VPB = 256 / (D / 2);
-  const int64_t vecs = (int64_t)a.B * (a.Hq + a.Hkv);
+  const int64_t vecs = (int64_t)a.B * a.S * (a.Hq + a.Hkv);
   const unsigned blocks = (unsigned)((vecs + VPB - 1) / VPB);
   hipLaunchKernelGGL((qkv_prologue_kernel<D, IT>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;

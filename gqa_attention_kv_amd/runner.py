@@ -15,7 +15,8 @@ import torch
 
 from . import attn_decode, attn_decode_merge, attn_decode_splitk, decode_step, qkv_prologue
 from . import decode_step_ex, qkv_prologue_ex, rope_table
-from . import decode_step_workspace_bytes, splitk_workspace_bytes
+from . import attn_decode_merge_multi, attn_decode_multi, attn_decode_splitk_multi
+from . import decode_step_workspace_bytes, splitk_multi_workspace_bytes, splitk_workspace_bytes
 
 BF16_NAN = 0x7FC0
 
@@ -50,7 +51,10 @@ class DeviceStep:
                  mode: Optional[str] = None):
         self.w = w
         self.dev = torch.device(device)
+        self.S = int(getattr(w, "S", 1))     # query tokens per sequence
         self.mode = mode or ("split" if split else "unsplit")
+        if self.S > 1 and self.mode == "fused":
+            raise NotImplementedError("the one-launch step runs one token per sequence")
         self.split = self.mode == "split"
         self.part_tokens = int(part_tokens or w.part_tokens)
         self.scale = float(scale)
@@ -61,17 +65,21 @@ class DeviceStep:
             kc, vc = kc.copy(), vc.copy()
             n = np.clip(w.lens.astype(np.int64), 0, w.T)
             for b in range(w.B):
-                lo = max(0, int(n[b]) - w.window) if w.window > 0 else 0
+                n0 = max(0, min(int(w.lens[b]) - (self.S - 1), w.T))   # first token's end
+                lo = max(0, n0 - w.window) if w.window > 0 else 0
                 keep = np.zeros(w.T, bool)
                 keep[lo:int(n[b])] = True
-                if w.pos is not None and 0 <= int(w.pos[b]) < w.T:
-                    keep[int(w.pos[b])] = True
+                if w.pos is not None:
+                    for st in range(self.S):
+                        if 0 <= int(w.pos[b]) + st < w.T:
+                            keep[int(w.pos[b]) + st] = True
                 kc[b][:, ~keep] = BF16_NAN
                 vc[b][:, ~keep] = BF16_NAN
         d = self.dev
         self.k_cache = bf16_tensor(kc, d)
         self.v_cache = bf16_tensor(vc, d)
         self.lens = torch.from_numpy(w.lens.astype(np.int32)).to(d)
+        self.rope_ex, self.inv_freq, self.rope_mscale, self.rope_layout = False, None, 1.0, "neox"
         if w.pos is not None:
             self.q_in = bf16_tensor(w.q, d)
             self.k_new = bf16_tensor(w.k_new, d)
@@ -79,23 +87,27 @@ class DeviceStep:
             self.pos = torch.from_numpy(w.pos.astype(np.int32)).to(d)
             self.w_q = None if w.w_q is None else torch.from_numpy(w.w_q).to(d)
             self.w_k = None if w.w_k is None else torch.from_numpy(w.w_k).to(d)
-            self.q = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=d)
+            self.q = torch.empty(tuple(w.q.shape), dtype=torch.float32, device=d)
             # A RoPE variant (interleaved pairs or a context-extension table)
-            # goes through the *_ex entry points with the library's own table.
+            # or several tokens go through the *_ex entry points with the
+            # library's own table.
             sc = getattr(w, "rope_scaling", None)
             self.rope_layout = getattr(w, "rope_layout", "neox")
-            self.rope_ex = (sc is not None or self.rope_layout != "neox") and w.theta > 0
-            if self.rope_ex:
+            self.rope_ex = (sc is not None or self.rope_layout != "neox" or self.S > 1)
+            self.inv_freq, self.rope_mscale = None, 1.0
+            if self.rope_ex and w.theta > 0:
                 sc = dict(sc or {"kind": "default"})
                 self.inv_freq, self.rope_mscale = rope_table(sc.pop("kind"), w.D, w.theta, **sc)
         else:
             qb = bf16_tensor(w.q, d)
             self.q = qb if q_dtype == "bf16" else qb.float()
-        self.out = torch.empty((w.B, w.Hq, w.D), dtype=self.out_dtype, device=d)
-        self.lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=d)
+        tok = (self.S,) if self.S > 1 else ()
+        self.out = torch.empty((w.B,) + tok + (w.Hq, w.D), dtype=self.out_dtype, device=d)
+        self.lse = torch.empty((w.B,) + tok + (w.Hq,), dtype=torch.float32, device=d)
         self.ws = None
         if self.mode == "split":
-            nb = splitk_workspace_bytes(w.B, w.Hq, w.D, w.T, w.window, self.part_tokens)
+            nb = splitk_multi_workspace_bytes(w.B, self.S, w.Hq, w.D, w.T, w.window,
+                                              self.part_tokens)
             self.ws = torch.empty(nb, dtype=torch.uint8, device=d)
         elif self.mode == "fused":
             nb = decode_step_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.T, w.window,
@@ -119,6 +131,16 @@ class DeviceStep:
 
     def attention(self):
         w = self.w
+        if self.S > 1:
+            if self.split:
+                attn_decode_splitk_multi(self.q, self.k_cache, self.v_cache, self.lens,
+                                         self.part_tokens, window=w.window, scale=self.scale,
+                                         workspace=self.ws)
+            else:
+                attn_decode_multi(self.q, self.k_cache, self.v_cache, self.lens,
+                                  window=w.window, scale=self.scale, out=self.out,
+                                  lse_out=self.lse)
+            return
         if self.split:
             attn_decode_splitk(self.q, self.k_cache, self.v_cache, self.lens, self.part_tokens,
                                window=w.window, scale=self.scale, workspace=self.ws)
@@ -130,6 +152,10 @@ class DeviceStep:
         if not self.split:
             return
         w = self.w
+        if self.S > 1:
+            attn_decode_merge_multi(self.ws, w.B, self.S, w.Hq, w.D, w.T, self.part_tokens,
+                                    window=w.window, out=self.out, lse_out=self.lse)
+            return
         attn_decode_merge(self.ws, w.B, w.Hq, w.D, w.T, self.part_tokens, window=w.window,
                           out=self.out, lse_out=self.lse)
 

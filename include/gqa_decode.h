@@ -129,23 +129,29 @@ int gqa_rope_table(int kind, int D, double theta, double factor, int orig_ctx,
                    double beta_fast, double beta_slow, double* inv_freq, double* mscale);
 
 /*
- * gqa_qkv_prologue with an explicit rotary table instead of rope_theta:
+ * gqa_qkv_prologue with an explicit rotary table instead of rope_theta, and
+ * S >= 1 new tokens per sequence:
  *   inv_freq     HOST pointer to D/2 float64 frequencies (radians per
  *                position, finite, >= 0), read during the call; NULL for no
  *                RoPE.  Pair i of the chosen layout rotates by
- *                pos * inv_freq[i] (angle and sincos in float64).
+ *                position * inv_freq[i] (angle and sincos in float64).
  *   rope_mscale  > 0: both rotated vectors (q and k) are multiplied by it
  *                (1 for a plain rotation; YaRN's attention temperature).
  *   rope_layout  GQA_ROPE_NEOX or GQA_ROPE_INTERLEAVED.
+ *   S            tokens per sequence: q is [B,S,Hq,D] and k_new, v_new are
+ *                [B,S,Hkv,D] (batch rows q_bstride >= S*Hq*D and kv_bstride
+ *                >= S*Hkv*D elements apart, tokens dense inside a row);
+ *                token s of sequence b sits at position pos[b] + s and is
+ *                written to cache row pos[b] + s; q_out is [B,S,Hq,D].
  * Every other argument, and every error, as for gqa_qkv_prologue.
  * gqa_qkv_prologue(theta) is this call with the GQA_ROPE_DEFAULT table,
- * mscale 1 and the NeoX layout.
+ * mscale 1, the NeoX layout and S = 1.
  */
 int gqa_qkv_prologue_ex(const void* q, const void* k_new, const void* v_new,
                         gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
                         const float* q_norm_w, const float* k_norm_w, float eps,
                         const double* inv_freq, double rope_mscale, int rope_layout,
-                        const int32_t* pos, float* q_out,
+                        const int32_t* pos, int S, float* q_out,
                         uint16_t* k_cache, uint16_t* v_cache,
                         int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
 
@@ -273,6 +279,39 @@ int gqa_decode_step_ex(const void* q, const void* k_new, const void* v_new,
                        void* workspace, size_t workspace_bytes,
                        void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
                        int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
+/*
+ * Multi-token decode: S >= 1 query tokens per sequence (e.g. draft tokens
+ * being verified), causal among themselves, over the same cache.  The
+ * fusedtok README's attention_prefill attends S query rows causally; here
+ * the rows sit at the end of a cache that already holds them:
+ *   token s of sequence b attends rows [lo_s, n_s) with
+ *   n_s = clamp(lens[b] - (S-1-s), 0, T) and lo_s = max(0, n_s - window)
+ *   (or 0 without a window), so the last token sees lens[b] rows.
+ * q, out [B,S,Hq,D] dense, lse_out [B,S,Hq]; every other argument as for
+ * the single-token call (which is this call with S = 1).  G = Hq/Hkv times
+ * S must be at most 16 (all (token, head) rows of a KV head share each
+ * cache row read), else GQA_ERR_UNSUPPORTED.
+ * The split-K variant partitions the union of the tokens' rows (at most T,
+ * or window + S - 1 rows) and its workspace holds [B,S,Hq] rows of
+ * partials; gqa_attn_decode_merge_multi merges them.
+ */
+int gqa_attn_decode_multi(const void* q, gqa_dtype_t q_dtype,
+                          const uint16_t* k_cache, const uint16_t* v_cache,
+                          const int32_t* lens, int S, int window, float scale,
+                          void* out, gqa_dtype_t out_dtype, float* lse_out,
+                          int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+size_t gqa_splitk_multi_workspace_bytes(int B, int S, int Hq, int D, int T, int window,
+                                        int part_tokens);
+int gqa_attn_decode_splitk_multi(const void* q, gqa_dtype_t q_dtype,
+                                 const uint16_t* k_cache, const uint16_t* v_cache,
+                                 const int32_t* lens, int S, int window, float scale,
+                                 int part_tokens, void* workspace, size_t workspace_bytes,
+                                 int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+int gqa_attn_decode_merge_multi(const void* workspace, size_t workspace_bytes, int S,
+                                int window, int part_tokens,
+                                void* out, gqa_dtype_t out_dtype, float* lse_out,
+                                int B, int Hq, int D, int T, hipStream_t stream);
 
 /* Static text for a status code (never NULL). */
 const char* gqa_status_string(int status);

@@ -39,6 +39,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "rmsnorm", "rope_inv_freq", "rope_inv_freq_scaled",
     "rope", "rope_neox", "qkv_prologue", "attend_rows", "attend", "num_partitions",
     "partition_ranges", "attend_partials", "lse_merge", "decode_step",
+    "qkv_prologue_multi", "attend_multi",
 ]
 
 
@@ -301,6 +302,48 @@ def attend(q, k_cache, v_cache, lens, window: int = 0, scale: float = 0.0):
 
 
 # ---------------------------------------------------------------------------
+# Several query tokens per sequence (fusedtok Operators row attention_prefill:
+# S query rows, causal; here they sit at the end of the cache)
+# ---------------------------------------------------------------------------
+def qkv_prologue_multi(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache,
+                       inv_freq=None, layout: str = "neox", mscale: float = 1.0):
+    """The single-token prologue applied to token s = 0, 1, ..., S-1 in turn,
+    token s at position pos[b] + s (and cache row pos[b] + s).
+
+    q: [B,S,Hq,D]; k_new, v_new: [B,S,Hkv,D].  Returns (q_hat [B,S,Hq,D],
+    k_cache', v_cache').
+    """
+    q = np.asarray(q, dtype=np.float64)
+    S = q.shape[1]
+    q_hat = np.empty_like(q)
+    kc, vc = k_cache, v_cache
+    for s in range(S):
+        q_hat[:, s], kc, vc = qkv_prologue(
+            q[:, s], np.asarray(k_new)[:, s], np.asarray(v_new)[:, s], w_q, w_k, eps, theta,
+            np.asarray(pos, np.int64) + s, kc, vc, inv_freq=inv_freq, layout=layout,
+            mscale=mscale)
+    return q_hat, kc, vc
+
+
+def attend_multi(q, k_cache, v_cache, lens, window: int = 0, scale: float = 0.0):
+    """Causal attention of S query tokens per sequence over the cache.
+
+    q: [B,S,Hq,D].  Token s of sequence b is single-token attention with
+    lens[b] - (S-1-s) rows (the last token sees lens[b] rows; each earlier
+    token one row fewer), with the window applied per token.
+    Returns (out [B,S,Hq,D], lse [B,S,Hq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, S, Hq, D = q.shape
+    out = np.zeros((B, S, Hq, v_cache.shape[3]))
+    lse = np.full((B, S, Hq), -math.inf)
+    for s in range(S):
+        lens_s = np.asarray(lens, np.int64) - (S - 1 - s)
+        out[:, s], lse[:, s] = attend(q[:, s], k_cache, v_cache, lens_s, window, scale)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
 # Flash-decoding split (fusedtok attention_decode row: "flash-decoding split
 # over long caches") and the log-sum-exp merge
 # ---------------------------------------------------------------------------
@@ -390,11 +433,23 @@ def decode_step(w, split: bool = False, scale: float = 0.0):
     result in out / lse.
     """
     q = bf16_to_f64(w.q)
+    S = getattr(w, "S", 1)
+    inv_freq, mscale = None, 1.0
+    scaling = getattr(w, "rope_scaling", None)
+    if scaling is not None and w.theta > 0:
+        inv_freq, mscale = rope_inv_freq_scaled(w.D, w.theta, **scaling)
+    if S > 1:                 # several tokens per sequence: q is [B,S,Hq,D]
+        if w.pos is not None:
+            q_hat, kc, vc = qkv_prologue_multi(
+                q, bf16_to_f64(w.k_new), bf16_to_f64(w.v_new), w.w_q, w.w_k, w.eps,
+                w.theta, w.pos, w.k_cache, w.v_cache, inv_freq=inv_freq,
+                layout=getattr(w, "rope_layout", "neox"), mscale=mscale)
+        else:
+            q_hat, kc, vc = q, w.k_cache, w.v_cache
+        res = dict(q_hat=q_hat, k_cache=kc, v_cache=vc)
+        res["out"], res["lse"] = attend_multi(q_hat, kc, vc, w.lens, w.window, scale)
+        return res
     if w.pos is not None:
-        inv_freq, mscale = None, 1.0
-        scaling = getattr(w, "rope_scaling", None)
-        if scaling is not None and w.theta > 0:
-            inv_freq, mscale = rope_inv_freq_scaled(w.D, w.theta, **scaling)
         q_hat, kc, vc = qkv_prologue(
             q, bf16_to_f64(w.k_new), bf16_to_f64(w.v_new), w.w_q, w.w_k,
             w.eps, w.theta, w.pos, w.k_cache, w.v_cache, inv_freq=inv_freq,

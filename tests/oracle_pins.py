@@ -572,4 +572,75 @@ def pin_prologue_writes_only_pos_rows(O):
         _close(qh[1, 0], x, 1e-12, "q_hat out of range pos")
 
 
+# ---------------------------------------------------------------------------
+# Several query tokens per sequence
+# ---------------------------------------------------------------------------
+def pin_attend_multi_matches_bruteforce(O):
+    """Token s of S attends lens - (S-1-s) rows (causal among the new
+    tokens), with the window counted back from each token's own end."""
+    rng = _rng(70)
+    B, S, Hq, Hkv, D, T = 2, 3, 4, 2, 6, 9
+    q = rng.standard_normal((B, S, Hq, D))
+    kc, vc = _bits(rng, (B, Hkv, T, D)), _bits(rng, (B, Hkv, T, D))
+    K, V = _torch_bf16_to_f64(kc), _torch_bf16_to_f64(vc)
+    for lens, window in (((9, 5), 0), ((7, 3), 4), ((2, 9), 2), ((1, 0), 0)):
+        out, lse = O.attend_multi(q, kc, vc, np.array(lens, np.int32), window, 0.0)
+        for s in range(S):
+            lens_s = [l - (S - 1 - s) for l in lens]
+            bo, bl = BF.attend(q[:, s].tolist(), K.tolist(), V.tolist(), lens_s, window, 0.0)
+            _close(out[:, s], np.array(bo), 1e-12, "multi out")
+            assert np.allclose(lse[:, s], np.array(bl), atol=1e-12, rtol=0) or \
+                np.array_equal(np.isinf(lse[:, s]), np.isinf(np.array(bl)))
+
+
+def pin_attend_multi_causal(O):
+    """A token's output does not depend on rows after its own end."""
+    rng = _rng(71)
+    B, S, Hq, Hkv, D, T = 1, 4, 2, 1, 8, 12
+    q = rng.standard_normal((B, S, Hq, D))
+    kc, vc = _bits(rng, (B, Hkv, T, D)), _bits(rng, (B, Hkv, T, D))
+    lens = np.array([10], np.int32)
+    out, _ = O.attend_multi(q, kc, vc, lens)
+    for s in range(S):
+        end = 10 - (S - 1 - s)
+        kc2, vc2 = kc.copy(), vc.copy()
+        kc2[:, :, end:] = _bits(rng, (B, Hkv, T - end, D))
+        vc2[:, :, end:] = _bits(rng, (B, Hkv, T - end, D))
+        out2, _ = O.attend_multi(q, kc2, vc2, lens)
+        assert np.array_equal(out2[:, s], out[:, s]), s
+        if end < T and s < S - 1:
+            assert not np.array_equal(out2[:, S - 1], out[:, S - 1])
+
+
+def pin_prologue_multi_matches_bruteforce(O):
+    """S new tokens: token s normalised and rotated at pos + s, its K/V row
+    appended at row pos + s, every other row untouched."""
+    rng = _rng(72)
+    B, S, Hq, Hkv, D, T = 2, 3, 4, 2, 8, 10
+    q = _torch_bf16_to_f64(_bits(rng, (B, S, Hq, D)))
+    kn = _torch_bf16_to_f64(_bits(rng, (B, S, Hkv, D)))
+    vn = _torch_bf16_to_f64(_bits(rng, (B, S, Hkv, D)))
+    kc, vc = _bits(rng, (B, Hkv, T, D)), _bits(rng, (B, Hkv, T, D))
+    wq, wk = 1 + 0.1 * rng.standard_normal(D), 1 + 0.1 * rng.standard_normal(D)
+    pos = np.array([2, 7], np.int32)                 # 7, 8, 9: the last row is T-1
+    qh, kc2, vc2 = O.qkv_prologue_multi(q, kn, vn, wq, wk, 1e-6, 1e4, pos, kc, vc)
+    for b in range(B):
+        for s in range(S):
+            p = int(pos[b]) + s
+            for h in range(Hq):
+                x = BF.rope_neox(BF.rmsnorm(list(q[b, s, h]), list(wq), 1e-6), p, 1e4)
+                _close(qh[b, s, h], x, 1e-12, "multi q_hat")
+            for g in range(Hkv):
+                x = np.array(BF.rope_neox(BF.rmsnorm(list(kn[b, s, g]), list(wk), 1e-6), p, 1e4))
+                row = _torch_bf16_to_f64(kc2[b, g, p])
+                half_ulp = np.ldexp(1.0, np.frexp(x)[1] - 9)
+                assert np.all(np.abs(row - x) <= half_ulp + 1e-300)
+                assert np.array_equal(_torch_bf16_to_f64(vc2[b, g, p]), vn[b, s, g])
+        written = {int(pos[b]) + s for s in range(S)}
+        for t in range(T):
+            if t not in written:
+                assert np.array_equal(kc2[b, :, t], kc[b, :, t])
+                assert np.array_equal(vc2[b, :, t], vc[b, :, t])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -132,6 +132,49 @@ def _table_variant(kind):
     return f
 
 
+def _multi_off_by_one(q, k_cache, v_cache, lens, window=0, scale=0.0):
+    q = np.asarray(q, np.float64)
+    B, S = q.shape[:2]
+    out = np.zeros(q.shape)
+    lse = np.full(q.shape[:3], -math.inf)
+    for s in range(S):
+        out[:, s], lse[:, s] = R.attend(q[:, s], k_cache, v_cache,
+                                        np.asarray(lens, np.int64) - (S - s), window, scale)
+    return out, lse
+
+
+def _multi_window_from_last(q, k_cache, v_cache, lens, window=0, scale=0.0):
+    q = np.asarray(q, np.float64)
+    B, S = q.shape[:2]
+    out = np.zeros(q.shape)
+    lse = np.full(q.shape[:3], -math.inf)
+    T = k_cache.shape[2]
+    for s in range(S):
+        for b in range(B):
+            n = min(max(int(lens[b]) - (S - 1 - s), 0), T)
+            lo = max(0, int(lens[b]) - window) if window > 0 else 0
+            for h in range(q.shape[2]):
+                g = h // (q.shape[2] // k_cache.shape[1])
+                K = R.bf16_to_f64(k_cache[b, g, lo:n])
+                V = R.bf16_to_f64(v_cache[b, g, lo:n])
+                sc = scale if scale > 0 else 1.0 / math.sqrt(q.shape[3])
+                out[b, s, h], lse[b, s, h] = R.attend_rows(q[b, s, h], K, V, sc)
+    return out, lse
+
+
+def _prologue_multi_same_pos(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_cache,
+                             inv_freq=None, layout="neox", mscale=1.0):
+    q = np.asarray(q, np.float64)
+    qh = np.empty_like(q)
+    kc, vc = k_cache, v_cache
+    for s in range(q.shape[1]):
+        qh[:, s], kc, vc = R.qkv_prologue(q[:, s], np.asarray(k_new)[:, s],
+                                          np.asarray(v_new)[:, s], w_q, w_k, eps, theta,
+                                          np.asarray(pos) + (s if s < q.shape[1] - 1 else 0),
+                                          kc, vc)
+    return qh, kc, vc
+
+
 # --- attention -----------------------------------------------------------------
 def _rows_no_max(q, K, V, scale):
     if K.shape[0] == 0:
@@ -321,6 +364,9 @@ MUTANTS = {
     "ntk_base_times_factor": {"rope_inv_freq_scaled": _table_variant("ntk_base_linear")},
     "linear_multiplies_frequencies": {"rope_inv_freq_scaled": _table_variant("linear_multiplies")},
     "yarn_without_mscale": {"rope_inv_freq_scaled": _table_variant("yarn_no_mscale")},
+    "multi_token_off_by_one": {"attend_multi": _multi_off_by_one},
+    "multi_window_from_last_token": {"attend_multi": _multi_window_from_last},
+    "multi_prologue_last_token_position": {"qkv_prologue_multi": _prologue_multi_same_pos},
 }
 
 

@@ -58,10 +58,10 @@ A16 = 0x100000       # stand-in device addresses: every call below fails on the 
 
 def test_prologue_ex_validation(G):
     good = np.full(64, 0.01)
-    def call(f=good, m=1.0, lay=0, D=128, pos=A16):
+    def call(f=good, m=1.0, lay=0, D=128, pos=A16, S=1):
         return G.lib.gqa_qkv_prologue_ex(
-            A16, A16, A16, 1, 8 * D, 2 * D, None, None, 1e-6,
-            None if f is None else f.ctypes.data, m, lay, pos, A16, A16, A16,
+            A16, A16, A16, 1, S * 8 * D, S * 2 * D, None, None, 1e-6,
+            None if f is None else f.ctypes.data, m, lay, pos, S, A16, A16, A16,
             1, 8, 2, D, 16, None)
     bad = good.copy(); bad[5] = float("nan")
     neg = good.copy(); neg[0] = -1.0
@@ -70,6 +70,7 @@ def test_prologue_ex_validation(G):
     assert call(lay=2) == -7
     assert call(D=96) == -3
     assert call(f=bad, pos=None) == -1                # null checks come first
+    assert call(f=bad, S=0) == -2                     # S >= 1
 
 
 def test_decode_step_ex_validation(G):

@@ -122,6 +122,9 @@ class Workload:
     # RoPE context-extension scheme (None: the plain theta table), e.g.
     # dict(kind="yarn", factor=4.0, orig_ctx=4096, beta_fast=32.0, beta_slow=1.0)
     rope_scaling: Optional[dict] = None
+    # query tokens per sequence (causal among themselves); with S > 1, q is
+    # [B,S,Hq,D], k_new/v_new [B,S,Hkv,D], token s at position pos[b] + s
+    S: int = 1
 
     @property
     def prologue(self) -> bool:
@@ -132,10 +135,13 @@ class Workload:
         return self.Hq // self.Hkv
 
     def attended(self) -> np.ndarray:
-        """Rows attended per sequence, n_b - lo_b (after clamping lens to [0,T])."""
+        """Rows read per sequence: the union of the tokens' ranges, n_b - lo_b
+        with n_b = lens_b (clamped to [0,T]) and lo_b the first token's window
+        start (the window counts back from each token's own end)."""
         n = np.clip(self.lens.astype(np.int64), 0, self.T)
         if self.window > 0:
-            return n - np.maximum(0, n - self.window)
+            n0 = np.clip(self.lens.astype(np.int64) - (self.S - 1), 0, self.T)
+            return n - np.maximum(0, n0 - self.window)
         return n
 
 
@@ -166,6 +172,11 @@ CONFIGS: Dict[str, dict] = {
     # 70B-shaped sliding window: B8 Hq64 Hkv8 L32768, W=4096
     "5": dict(seed=5, B=8, Hq=64, Hkv=8, D=128, L=32768, layout="last",
               window=4096, theta=5e5, norm=True, out_dtype="f32", part_tokens=1024),
+    # several query tokens per sequence (draft-token verification): the
+    # Llama-3-8B shape with S=4 new tokens appended at L=8192, so the 4 x 4
+    # (token, head) rows of each KV head share every cache row read
+    "6": dict(seed=6, B=8, Hq=32, Hkv=8, D=128, L=8192, layout="append", S=4,
+              window=0, theta=5e5, norm=False, out_dtype="bf16", part_tokens=1024),
 }
 
 
@@ -177,30 +188,32 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
     ``rope_layout`` / ``rope_scaling`` (the RoPE variant; no effect on the
     random draws).
     Layouts:
-      last       T = L, new token at pos = L-1, lens = L
-      append     T = L + 64, new token at pos = L, lens = L + 1
-      ragged     T = L, lens ~ U{lmin..L}, pos = lens - 1
+      last       T = L, new tokens at pos = L-S .. L-1, lens = L
+      append     T = L + 64, new tokens at pos = L .. L+S-1, lens = L + S
+      ragged     T = L, lens ~ U{lmin..L}, pos = lens - S
       noprologue T = L, lens = L, q given directly
+    (S = 1 unless overridden: the query tokens per sequence.)
     """
     p = dict(CONFIGS[name])
     p.update(over)
     seed = p["seed"] if seed is None else seed
     B, Hq, Hkv, D, L = p["B"], p["Hq"], p["Hkv"], p["D"], p["L"]
+    S = int(p.get("S", 1))
     layout = p["layout"]
     rng = np.random.default_rng(seed)
 
     if layout == "last":
         T = L
         lens = np.full(B, L, np.int32)
-        pos = np.full(B, L - 1, np.int32)
+        pos = np.full(B, L - S, np.int32)
     elif layout == "append":
         T = p.get("T", L + 64)
-        lens = np.full(B, L + 1, np.int32)
+        lens = np.full(B, L + S, np.int32)
         pos = np.full(B, L, np.int32)
     elif layout == "ragged":
         T = p.get("T", L)
-        lens = rng.integers(p["lmin"], L, size=B, endpoint=True).astype(np.int32)
-        pos = (lens - 1).astype(np.int32)
+        lens = rng.integers(max(p["lmin"], S), L, size=B, endpoint=True).astype(np.int32)
+        pos = (lens - S).astype(np.int32)
     elif layout == "noprologue":
         T = L
         lens = np.full(B, L, np.int32)
@@ -208,10 +221,11 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
     else:
         raise ValueError(layout)
 
-    q = _normal_bf16(rng, (B, Hq, D))
+    tok = (S,) if S > 1 else ()
+    q = _normal_bf16(rng, (B,) + tok + (Hq, D))
     if pos is not None:
-        k_new = _normal_bf16(rng, (B, Hkv, D))
-        v_new = _normal_bf16(rng, (B, Hkv, D))
+        k_new = _normal_bf16(rng, (B,) + tok + (Hkv, D))
+        v_new = _normal_bf16(rng, (B,) + tok + (Hkv, D))
     else:
         k_new = v_new = None
     k_cache = _cache_bf16(seed, 1, (B, Hkv, T, D))
@@ -244,4 +258,4 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
         out_dtype=p["out_dtype"], part_tokens=int(p["part_tokens"]),
         q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
         w_q=w_q, w_k=w_k, peaky_rows=peaky_rows,
-        rope_layout=p.get("rope_layout", "neox"), rope_scaling=p.get("rope_scaling"))
+        rope_layout=p.get("rope_layout", "neox"), rope_scaling=p.get("rope_scaling"), S=S)
