@@ -362,6 +362,8 @@ int gqa_decode_step_ex(const void* q, const void* k_new, const void* v_new,
   if (workspace_bytes < gqa_decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens))
     return GQA_ERR_WORKSPACE;
   const int np = gqa_num_partitions(T, window, part_tokens);
+  // the merge reads one (sequence, KV head)'s partials with 32-bit offsets
+  if ((int64_t)(Hq / Hkv) * np * D * 4 >= (INT64_C(1) << 31)) return GQA_ERR_SHAPE;
   gqa::KernelArgs a{};
   a.q = q; a.q_bstride = q_bstride; a.in_bf16 = in_dtype == GQA_BF16;
   a.k_cache = k_cache; a.v_cache = v_cache; a.k_cache_w = k_cache; a.v_cache_w = v_cache;

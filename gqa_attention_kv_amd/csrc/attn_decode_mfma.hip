@@ -169,9 +169,11 @@ struct TileBuf {
 // float4 group(s) of the G*D outputs; when there are fewer groups than
 // threads, KS subsets of threads take partitions s, s + KS, ... and are
 // combined through LDS at the end.  Every order is fixed, so the result is
-// bit-identical from run to run.  Partials are read with agent-scope loads
-// (8 bytes each), which do not hit stale L2 lines; a batch of up to MB
-// partitions is one memory round trip.
+// bit-identical from run to run.  Partials are read with device-coherent
+// loads (the sc1 policy of agent-scope atomics; 16-byte buffer loads for o),
+// which do not hit stale L2 lines; a batch of up to MB partitions is one
+// memory round trip.  The team's slice of o is below 2 GiB (checked on the
+// host), so 32-bit buffer offsets reach all of it.
 template <int D, int G, int NW>
 __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head0) {
   constexpr int NTH = NW * 64;
@@ -179,10 +181,13 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
   constexpr int GPT = NG > NTH ? NG / NTH : 1;  // groups per thread
   constexpr int TPS = NG < NTH ? NG : NTH;      // threads per partition subset
   constexpr int KS = NTH / TPS;                 // partition subsets
-  constexpr int MB = 16 / GPT;                  // partitions per batch
+  constexpr int MB = 16 / GPT;                  // partitions per batch (no spills)
+  constexpr int kCoherent = 0x10;               // sc1: read through to the coherence point
   const int num_parts = a.num_parts;
   const int t = threadIdx.x;
   const int s = t / TPS;
+  const __amdgpu_buffer_rsrc_t Ors =
+      make_rsrc(a.ws_o + head0 * num_parts * D, (uint32_t)((size_t)G * num_parts * D * 4));
   float Mx[GPT], Wx[GPT];
   float Ax[GPT][4];
 #pragma unroll
@@ -194,24 +199,22 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
   }
   for (int k0 = s; k0 < num_parts; k0 += KS * MB) {
     float lk[GPT][MB];
-    uint64_t ov[GPT][MB][2];
+    f32x4_t ov[GPT][MB];
 #pragma unroll
     for (int j = 0; j < GPT; ++j) {
       const int gi = t % TPS + j * TPS;
       const int h = gi / (D / 4);
       const int d4 = gi % (D / 4);
       const float* Lh = a.ws_lse + (head0 + h) * num_parts;
-      const float* Oh = a.ws_o + (head0 + h) * num_parts * D + 4 * d4;
 #pragma unroll
       for (int k = 0; k < MB; ++k) {
         const int kk = k0 + k * KS;
         lk[j][k] = -INFINITY;
-        ov[j][k][0] = ov[j][k][1] = 0;
+        ov[j][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (kk < num_parts) {
           lk[j][k] = __hip_atomic_load(Lh + kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint64_t* op = reinterpret_cast<const uint64_t*>(Oh + (int64_t)kk * D);
-          ov[j][k][0] = __hip_atomic_load(op, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ov[j][k][1] = __hip_atomic_load(op + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint32_t off = (uint32_t)((((int64_t)h * num_parts + kk) * D + 4 * d4) * 4);
+          ov[j][k] = __builtin_amdgcn_raw_buffer_load_b128(Ors, off, 0, kCoherent);
         }
       }
     }
@@ -232,10 +235,7 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
         // an empty partition (lse = -inf) has weight 0 and an undefined o_k
         const bool ok = lk[j][k] != -INFINITY;
         const float w = ok ? __expf(lk[j][k] - Mn) : 0.0f;
-        const float o4[4] = {__uint_as_float((uint32_t)ov[j][k][0]),
-                             __uint_as_float((uint32_t)(ov[j][k][0] >> 32)),
-                             __uint_as_float((uint32_t)ov[j][k][1]),
-                             __uint_as_float((uint32_t)(ov[j][k][1] >> 32))};
+        const float o4[4] = {ov[j][k][0], ov[j][k][1], ov[j][k][2], ov[j][k][3]};
         W += w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) A[e] = fmaf(w, ok ? o4[e] : 0.0f, A[e]);

@@ -247,6 +247,9 @@ int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
  *              share a workspace must not overlap in time.
  *   q          16-byte aligned and q_bstride * element size a multiple of 16.
  *   q_out      float32 [B,Hq,D] rotated queries, or NULL.
+ * One (sequence, KV head)'s partials, (Hq/Hkv) * partitions * D * 4 bytes,
+ * must stay below 2 GiB (else GQA_ERR_SHAPE; only reached with very small
+ * part_tokens).
  * With pos, k_new and v_new all NULL (and no norm weights, no q_out) the
  * prologue is skipped: q [B,Hq,D] in in_dtype is attended as given and the
  * cache is only read -- the split-K pass and the merge in one launch.
