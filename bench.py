@@ -31,6 +31,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -49,7 +51,13 @@ WORKLOAD_NAMES = {
     "4": "long-context flash-decoding, L=131072",
     "5": "70B-shaped sliding-window GQA decode (8:1)",
     "6": "draft-token verification: S=4 causal query tokens per sequence, Llama-3-8B shape",
+    "7": "chunked prefill: the last 1024 tokens of four 8192-row sequences as causal "
+         "queries, Llama-3-8B shape",
+    "7f": "fresh-sequence causal prefill, S=1024, D=128, Llama-3-8B heads",
 }
+PREFILL_WORKLOADS = ("7", "7f")
+PREFILL_KERNEL = "attn_prefill_kernel"
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def _parse():
@@ -68,9 +76,11 @@ def _parse():
                     help="also time a plain device copy of this many MiB")
     ap.add_argument("--part-tokens", type=int, default=0,
                     help="override the workload's split-K partition size")
-    ap.add_argument("--mode", default="fused", choices=["fused", "split"],
+    ap.add_argument("--mode", default="fused", choices=["fused", "split", "prefill"],
                     help="fused: the whole step as one launch (default); split: "
-                         "prologue, split-K pass and merge as three launches")
+                         "prologue, split-K pass and merge as three launches; prefill: "
+                         "prologue and the matrix-core prefill kernel (the default "
+                         "for the prefill workloads)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn two rocprofv3 --pmc output directories "
                          "(FETCH_SIZE, WRITE_SIZE; each from a bench run with "
@@ -217,6 +227,45 @@ def _cpu_baseline(w, min_seconds: float):
     }
 
 
+def _cpu_baseline_prefill(w, min_seconds: float):
+    """Time the fp64 oracle on a bounded sample of a prefill step's tokens:
+    each sampled token is single-token attention over its own rows (what the
+    oracle's multi-token attention does per token), scaled to the whole step
+    by its share of the step's attended rows."""
+    import threadpoolctl
+    import workloads
+    from oracle import reference as oracle
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    q = oracle.bf16_to_f64(w.q)
+    rows = w.token_rows()                       # [B,S]
+    order = np.random.default_rng(0).permutation(w.S)
+    back = np.arange(w.S - 1, -1, -1) if w.causal else np.zeros(w.S, np.int64)
+    done, toks, t0 = 0, 0, time.perf_counter()
+    while True:
+        s = int(order[toks % w.S])
+        lens_s = w.lens.astype(np.int64) - back[s]
+        oracle.attend(q[:, s], w.k_cache, w.v_cache, lens_s, w.window, 0.0)
+        done += int(rows[:, s].sum())
+        toks += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    est_step = el * float(rows.sum()) / max(done, 1)
+    kvb = workloads.kv_bytes(w)
+    return {
+        "value": round(kvb / est_step / 1e9, 6),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{toks} of the step's {w.S} query tokens (all {w.B} sequences and "
+                   f"{w.Hq} heads each; float64 numpy attention), {el:.1f} s wall, "
+                   f"scaled by attended rows to {est_step:.1f} s per step; the prologue "
+                   f"is not timed"),
+    }
+
+
 def main():
     args = _parse()
     if args.record_traffic:
@@ -243,7 +292,9 @@ def main():
         w.part_tokens = args.part_tokens
     kvb = workloads.kv_bytes(w)
     mode = args.mode
-    if w.S > 1 and mode == "fused":     # the one-launch step runs one token per sequence
+    if args.workload in PREFILL_WORKLOADS:
+        mode = "prefill"
+    elif w.S > 1 and mode == "fused":     # the one-launch step runs one token per sequence
         mode = "split"
     step = DeviceStep(w, device=dev, mode=mode)
     flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
@@ -319,9 +370,38 @@ def main():
         copy_probe = {"bytes": 2 * n * 4, "ms": round(t, 4),
                       "GBps": round(2 * n * 4 / (t * 1e-3) / 1e9, 1)}
 
-    cpu = None if args.no_cpu_baseline else _cpu_baseline(w, args.cpu_seconds)
+    if args.no_cpu_baseline:
+        cpu = None
+    elif mode == "prefill":
+        cpu = _cpu_baseline_prefill(w, args.cpu_seconds)
+    else:
+        cpu = _cpu_baseline(w, args.cpu_seconds)
 
     traffic = _traffic(args.workload)
+    if mode == "prefill":
+        flops = workloads.attention_flops(w)
+        tflops = flops / (mean_attn * 1e-3) / 1e12
+        roofline = {
+            "bound": "mfma",
+            "kernel": PREFILL_KERNEL,
+            "achieved": round(tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": flops,
+        }
+    else:
+        roofline = {
+            "bound": "hbm",
+            "kernel": ATTN_KERNEL + (" (whole fused step)" if mode == "fused"
+                                     else " (split-K partition pass)"),
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        }
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -334,7 +414,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if mode == "prefill" else "f32",
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_NAMES[args.workload],
@@ -348,16 +428,7 @@ def main():
             "cache_sweep_between_steps": args.flush,
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": ATTN_KERNEL + (" (whole fused step)" if mode == "fused"
-                                     else " (split-K partition pass)"),
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-        },
+        "roofline": roofline,
         "kernels_us": {
             "mode": mode,
             "prologue": round(1e3 * statistics.fmean(pro_ms), 2),

@@ -77,6 +77,8 @@ SYMBOLS = {
     "gqa_decode_step_ex": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _p,
                                 _p, _p, _i, _f, _i, _p, _sz, _p, _i, _p, _p, _i, _i, _i, _i,
                                 _i, _p]),
+    "gqa_attn_prefill": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _f, _p, _i, _p, _i, _i, _i, _i,
+                              _i, _p]),
 }
 for _name, (_res, _args) in SYMBOLS.items():
     _fn = getattr(lib, _name)
@@ -381,6 +383,28 @@ def attn_decode_multi(q, k_cache, v_cache, lens, window: int = 0, scale: float =
         _ptr(q), _dtype_code(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(S),
         int(window), float(scale), _ptr(out), _dtype_code(out, "out"), _ptr(lse_out),
         B, Hq, Hkv, D, T, _stream(dev)))
+    return out
+
+
+def attn_prefill(q, k_cache, v_cache, lens, causal: bool = True, window: int = 0,
+                 scale: float = 0.0, out=None, out_dtype=torch.float32, lse_out=None):
+    """S query tokens per sequence (q [B,S,Hq,D]) over the cache on the matrix
+    cores, any S.  causal: token s attends lens[b] - (S-1-s) rows (as
+    attn_decode_multi); otherwise every token attends lens[b] rows.  Returns
+    out [B,S,Hq,D]; writes the LSE into ``lse_out`` (float32 [B,S,Hq])."""
+    dev, B, S, Hq, Hkv, D, T = _multi_common(q, k_cache, v_cache, lens)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=dev)
+    _dev(out, "out", dev)
+    _contig(out, "out")
+    if tuple(out.shape) != (B, S, Hq, D):
+        raise ValueError("out must be [B,S,Hq,D]")
+    if lse_out is not None:
+        _lse_check(lse_out.reshape(B, S * Hq), B, S * Hq, dev)
+    _check(lib.gqa_attn_prefill(
+        _ptr(q), _dtype_code(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(S),
+        1 if causal else 0, int(window), float(scale), _ptr(out), _dtype_code(out, "out"),
+        _ptr(lse_out), B, Hq, Hkv, D, T, _stream(dev)))
     return out
 
 

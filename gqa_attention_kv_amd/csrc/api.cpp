@@ -225,6 +225,37 @@ int gqa_attn_decode_multi(const void* q, gqa_dtype_t q_dtype,
   return gqa::launch_attn_final(a, stream);
 }
 
+int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
+                     const uint16_t* k_cache, const uint16_t* v_cache,
+                     const int32_t* lens, int S, int causal, int window, float scale,
+                     void* out, gqa_dtype_t out_dtype, float* lse_out,
+                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !lens || !out) return GQA_ERR_NULL;
+  int rc = check_shapes(B, Hq, Hkv, D, T);
+  if (rc) return rc;
+  if (S < 1) return GQA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return GQA_ERR_VALUE;
+  if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(lens, 4) || !aligned(lse_out, 4))
+    return GQA_ERR_ALIGN;
+  const int64_t rows = (int64_t)S * (Hq / Hkv);   // (token, head) rows per KV head
+  if (rows > INT32_MAX / 2 || (int64_t)B * S * Hq > kMaxIndex / D) return GQA_ERR_SHAPE;
+  const int per = gqa::prefill_rows_per_block();
+  const int64_t row_blocks = (rows + per - 1) / per;
+  if ((int64_t)B * Hkv * row_blocks > kMaxWorkgroups) return GQA_ERR_SHAPE;
+  gqa::PrefillArgs a{};
+  a.q = q; a.in_bf16 = q_dtype == GQA_BF16;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens;
+  a.S = S; a.causal = causal; a.window = window;
+  a.qscale = softmax_qscale(scale, D);
+  a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
+  a.row_blocks = (int)row_blocks;
+  return gqa::launch_attn_prefill(a, stream);
+}
+
 int gqa_num_partitions(int T, int window, int part_tokens) {
   if (T < 1 || part_tokens < 1) return 0;
   return num_parts(T, window, part_tokens);

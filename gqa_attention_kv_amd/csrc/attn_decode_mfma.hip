@@ -117,6 +117,40 @@ __device__ __forceinline__ uint32_t split_bf16(float x) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// sin and cos of |x| <= pi in float64, with few registers: x = k pi/2 + r
+// (k = rint(2x/pi), pi/2 in two parts, |r| <= pi/4), then the Taylor series
+// of sin r through r^17 and of cos r through r^16 (truncation below 1e-16
+// on |r| <= pi/4, Horner form), and the quadrant k mod 4 swaps and signs.
+__device__ __forceinline__ void sincos_pi_f64(double x, double* s, double* c) {
+  constexpr double kHalfPi1 = 1.5707963267948966;      // fp64 nearest pi/2
+  constexpr double kHalfPi2 = 6.123233995736766e-17;   // pi/2 - kHalfPi1
+  const double k = rint(x * 0.6366197723675814);
+  const double r = (x - k * kHalfPi1) - k * kHalfPi2;
+  const double z = r * r;
+  double ps = 1.0 / 355687428096000.0;                 // 1/17!
+  ps = fma(ps, -z, 1.0 / 1307674368000.0);             // 1/15!
+  ps = fma(ps, -z, 1.0 / 6227020800.0);                // 1/13!
+  ps = fma(ps, -z, 1.0 / 39916800.0);                  // 1/11!
+  ps = fma(ps, -z, 1.0 / 362880.0);                    // 1/9!
+  ps = fma(ps, -z, 1.0 / 5040.0);                      // 1/7!
+  ps = fma(ps, -z, 1.0 / 120.0);                       // 1/5!
+  ps = fma(ps, -z, 1.0 / 6.0);                         // 1/3!
+  const double sr = fma(-z * r, ps, r);
+  double pc = 1.0 / 20922789888000.0;                  // 1/16!
+  pc = fma(pc, -z, 1.0 / 87178291200.0);               // 1/14!
+  pc = fma(pc, -z, 1.0 / 479001600.0);                 // 1/12!
+  pc = fma(pc, -z, 1.0 / 3628800.0);                   // 1/10!
+  pc = fma(pc, -z, 1.0 / 40320.0);                     // 1/8!
+  pc = fma(pc, -z, 1.0 / 720.0);                       // 1/6!
+  pc = fma(pc, -z, 1.0 / 24.0);                        // 1/4!
+  pc = fma(pc, -z, 0.5);                               // 1/2!
+  const double cr = fma(-z, pc, 1.0);
+  const int q = (int)k & 3;
+  const double sv = (q & 1) ? cr : sr, cv = (q & 1) ? sr : cr;
+  *s = (q & 2) ? -sv : sv;
+  *c = (q == 1 || q == 2) ? -cv : cv;
+}
+
 template <typename T>
 __device__ __forceinline__ void load8f(const T* p, float f[8]);
 template <>
@@ -529,9 +563,10 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     // sincos of an angle in [-pi, pi]; cos and sin carry the magnitude
     // factor, so it reaches both q and k.
     float cs = 1.0f, sn = 0.0f;
+    double fr = 0.0;
     if (rope) {
       const double rev = (double)p * inv_rev;
-      const double fr = rev - rint(rev);
+      fr = rev - rint(rev);
       sincosf((float)(fr * 6.283185307179586), &sn, &cs);
       cs *= a.rope_mscale;
       sn *= a.rope_mscale;
@@ -541,19 +576,28 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     // analysis, so the compiler keeps program order).
     float* af = reinterpret_cast<float*>(slab);
     if (need_k) {
-      float x0 = to_f32(rx0), x1 = to_f32(rx1);
+      // The appended K row in float64 (weights, a float64 sin/cos and the
+      // rotation on the exact inputs, the RMS factor last), rounded once:
+      // an element much smaller than its inputs keeps ~1e-7 relative
+      // accuracy, so it lands within one bf16 ulp of the exact value.
+      const float xf0 = to_f32(rx0), xf1 = to_f32(rx1);
+      double x0 = xf0, x1 = xf1, r = 1.0;
       if (a.wk != nullptr) {
-        const float ss = group_sum_shfl<HALF>(x0 * x0 + x1 * x1);
-        const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
-        x0 = x0 * r * wk0;
-        x1 = x1 * r * wk1;
+        const float ss = group_sum_shfl<HALF>(xf0 * xf0 + xf1 * xf1);
+        r = 1.0 / sqrt((double)ss / D + (double)a.eps);
+        x0 *= (double)wk0;
+        x1 *= (double)wk1;
       }
-      if (a.rope) {
-        const float y0 = x0 * cs - x1 * sn, y1 = x1 * cs + x0 * sn;
+      if (rope) {
+        double sd, cd;
+        sincos_pi_f64(fr * 6.283185307179586, &sd, &cd);
+        cd *= (double)a.rope_mscale;
+        sd *= (double)a.rope_mscale;
+        const double y0 = x0 * cd - x1 * sd, y1 = x1 * cd + x0 * sd;
         x0 = y0;
         x1 = y1;
       }
-      const uint16_t k0 = f32_to_bf16(x0), k1 = f32_to_bf16(x1);
+      const uint16_t k0 = f32_to_bf16((float)(x0 * r)), k1 = f32_to_bf16((float)(x1 * r));
       const uint16_t v0 = bits_bf16(&rv0, 0), v1 = bits_bf16(&rv1, 0);
       if (kwrite && lane < HALF) {
         uint16_t* krow = a.k_cache_w + slab_off + (int64_t)p * D;

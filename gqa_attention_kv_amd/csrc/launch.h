@@ -82,10 +82,31 @@ struct MergeArgs {
   int B, Hq, D;
 };
 
+// Arguments of the prefill kernel (S query tokens per sequence over the
+// cache, causal or bidirectional), passed by value.
+struct PrefillArgs {
+  const void* q;               // [B,S,Hq,D] dense
+  int in_bf16;
+  const uint16_t* k_cache;     // [B,Hkv,T,D]
+  const uint16_t* v_cache;
+  const int32_t* lens;
+  int S;
+  int causal;
+  int window;
+  float qscale;                // softmax scale * log2(e)
+  void* out;                   // [B,S,Hq,D]
+  int out_bf16;
+  float* lse_out;              // [B,S,Hq] or null
+  int B, Hq, Hkv, D, T;
+  int row_blocks;              // ceil(S * G / prefill_rows_per_block())
+};
+
 int launch_prologue(const PrologueArgs& a, hipStream_t s);
 int launch_attn_final(const KernelArgs& a, hipStream_t s);   // one pass per (seq, KV head)
 int launch_attn_split(const KernelArgs& a, hipStream_t s);   // partition pass
 int launch_decode_step(const KernelArgs& a, hipStream_t s);  // fused whole step
 int launch_merge(const MergeArgs& a, hipStream_t s);
+int prefill_rows_per_block();                                 // (token, head) rows per workgroup
+int launch_attn_prefill(const PrefillArgs& a, hipStream_t s);
 
 }  // namespace gqa

@@ -14,7 +14,8 @@
 // D = 128 that is one wave64 per head vector.  The rotary angle
 // pos * inv_freq[i] (the caller's table) is formed in float64 with a
 // float64 sincos (at pos ~ 1e5 a float32 angle would be off by ~1e-2 rad);
-// the rotation itself is float32, scaled by the magnitude factor.
+// the norm weights, the rotation and the magnitude factor are applied in
+// float64 too, and the result is rounded once.
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/gqa_decode.h"
@@ -61,25 +62,33 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
   float x0 = load_elem<IT>(src, e0);
   float x1 = load_elem<IT>(src, e1);
 
+  // Weights and rotation act on the exact inputs in float64 and the RMS
+  // factor r multiplies the result, so a rotated element much smaller than
+  // its inputs (x0 c ~ x1 s) keeps the accuracy of r (~1e-7 relative)
+  // instead of the ~1e-7 absolute error an fp32 rotation leaves.
   const float* w = is_q ? a.q_norm_w : a.k_norm_w;
+  double y0 = x0, y1 = x1, r = 1.0;
   if (w != nullptr) {
     float ss = x0 * x0 + x1 * x1;
     ss = group_sum_shfl<HALF>(ss);
-    const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
-    x0 = x0 * r * w[e0];
-    x1 = x1 * r * w[e1];
+    r = 1.0 / sqrt((double)ss / D + (double)a.eps);
+    y0 *= (double)w[e0];
+    y1 *= (double)w[e1];
   }
 
   const int64_t p = (int64_t)a.pos[b] + st;
   if (a.rope) {
     double sn, cs;
     sincos((double)p * a.inv_freq[i], &sn, &cs);
-    const float c = (float)cs * a.rope_mscale, s = (float)sn * a.rope_mscale;
-    const float y0 = x0 * c - x1 * s;
-    const float y1 = x1 * c + x0 * s;
-    x0 = y0;
-    x1 = y1;
+    cs *= (double)a.rope_mscale;
+    sn *= (double)a.rope_mscale;
+    const double t0 = y0 * cs - y1 * sn;
+    const double t1 = y1 * cs + y0 * sn;
+    y0 = t0;
+    y1 = t1;
   }
+  x0 = (float)(y0 * r);
+  x1 = (float)(y1 * r);
   if (!live) return;
 
   if (is_q) {

@@ -15,7 +15,7 @@ import torch
 
 from . import attn_decode, attn_decode_merge, attn_decode_splitk, decode_step, qkv_prologue
 from . import decode_step_ex, qkv_prologue_ex, rope_table
-from . import attn_decode_merge_multi, attn_decode_multi, attn_decode_splitk_multi
+from . import attn_decode_merge_multi, attn_decode_multi, attn_decode_splitk_multi, attn_prefill
 from . import decode_step_workspace_bytes, splitk_multi_workspace_bytes, splitk_workspace_bytes
 
 BF16_NAN = 0x7FC0
@@ -39,7 +39,8 @@ class DeviceStep:
     "split" runs the prologue, the split-K partition pass over
     ``part_tokens``-row partitions (default: the workload's own size) and the
     merge as three launches; "unsplit" runs the prologue and the unsplit
-    kernel.  ``split`` (bool) is the older spelling of split/unsplit.  ``q_dtype`` selects the dtype attention reads q in when the
+    kernel; "prefill" runs the prologue and the matrix-core prefill kernel
+    (any number of tokens, causal or bidirectional as the workload says).  ``split`` (bool) is the older spelling of split/unsplit.  ``q_dtype`` selects the dtype attention reads q in when the
     workload has no prologue.  ``poison`` writes bf16 NaN into every cache
     row outside each sequence's attended range [lo, n) (rows the step must
     never read); rows written by the prologue are left alone.
@@ -55,6 +56,9 @@ class DeviceStep:
         self.mode = mode or ("split" if split else "unsplit")
         if self.S > 1 and self.mode == "fused":
             raise NotImplementedError("the one-launch step runs one token per sequence")
+        self.causal = bool(getattr(w, "causal", True))
+        if not self.causal and self.mode != "prefill":
+            raise NotImplementedError("bidirectional attention runs on the prefill kernel")
         self.split = self.mode == "split"
         self.part_tokens = int(part_tokens or w.part_tokens)
         self.scale = float(scale)
@@ -64,8 +68,9 @@ class DeviceStep:
         if poison:
             kc, vc = kc.copy(), vc.copy()
             n = np.clip(w.lens.astype(np.int64), 0, w.T)
+            back = (self.S - 1) if self.causal else 0
             for b in range(w.B):
-                n0 = max(0, min(int(w.lens[b]) - (self.S - 1), w.T))   # first token's end
+                n0 = max(0, min(int(w.lens[b]) - back, w.T))   # first token's end
                 lo = max(0, n0 - w.window) if w.window > 0 else 0
                 keep = np.zeros(w.T, bool)
                 keep[lo:int(n[b])] = True
@@ -131,6 +136,13 @@ class DeviceStep:
 
     def attention(self):
         w = self.w
+        if self.mode == "prefill":
+            q = self.q if self.q.dim() == 4 else self.q.unsqueeze(1)
+            out = self.out if self.out.dim() == 4 else self.out.unsqueeze(1)
+            attn_prefill(q, self.k_cache, self.v_cache, self.lens, causal=self.causal,
+                         window=w.window, scale=self.scale, out=out,
+                         lse_out=self.lse.reshape(w.B, self.S, w.Hq))
+            return
         if self.S > 1:
             if self.split:
                 attn_decode_splitk_multi(self.q, self.k_cache, self.v_cache, self.lens,

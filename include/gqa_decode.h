@@ -316,6 +316,33 @@ int gqa_attn_decode_merge_multi(const void* workspace, size_t workspace_bytes, i
                                 void* out, gqa_dtype_t out_dtype, float* lse_out,
                                 int B, int Hq, int D, int T, hipStream_t stream);
 
+/*
+ * Prefill: attention of S query tokens per sequence over the cache, causal
+ * or bidirectional (fusedtok README, "Operators" row attention_prefill),
+ * with the GQA head mapping, lengths and window of attention_decode.  The S
+ * tokens are the last rows of each sequence's cache (a fresh sequence:
+ * lens[b] = S, T >= S):
+ *   causal = 1: token s attends rows [lo_s, n_s), n_s = clamp(lens[b] -
+ *               (S-1-s), 0, T) -- the same rows as gqa_attn_decode_multi;
+ *   causal = 0: every token attends [lo, n), n = clamp(lens[b], 0, T);
+ *   lo = max(0, n - window) with window > 0, else 0.
+ * q [B,S,Hq,D] fp32 or bf16, dense; out [B,S,Hq,D] fp32 or bf16;
+ * lse_out [B,S,Hq] fp32 (natural log) or NULL.  Any S >= 1 and any G =
+ * Hq/Hkv in {1,2,4,8,16}; D in {64,128}.  A row with no key gets out = 0 and
+ * lse = -inf.  Runs on the matrix cores: K and V tiles are shared through
+ * LDS by 128 (token, head) rows of one KV head; P keeps ~16 mantissa bits
+ * (bf16 hi + lo) and an fp32 q is split the same way.  Errors:
+ * GQA_ERR_NULL, GQA_ERR_SHAPE (S < 1, sizes), GQA_ERR_VALUE (causal not 0 or
+ * 1, non-finite scale), GQA_ERR_UNSUPPORTED (D, G, dtypes), GQA_ERR_ALIGN
+ * (q, caches, out 16-byte aligned; lens, lse_out 4-byte aligned).  Nothing
+ * is allocated; outputs must not alias inputs.
+ */
+int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
+                     const uint16_t* k_cache, const uint16_t* v_cache,
+                     const int32_t* lens, int S, int causal, int window, float scale,
+                     void* out, gqa_dtype_t out_dtype, float* lse_out,
+                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char* gqa_status_string(int status);
 

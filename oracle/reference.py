@@ -325,12 +325,15 @@ def qkv_prologue_multi(q, k_new, v_new, w_q, w_k, eps, theta, pos, k_cache, v_ca
     return q_hat, kc, vc
 
 
-def attend_multi(q, k_cache, v_cache, lens, window: int = 0, scale: float = 0.0):
-    """Causal attention of S query tokens per sequence over the cache.
+def attend_multi(q, k_cache, v_cache, lens, window: int = 0, scale: float = 0.0,
+                 causal: bool = True):
+    """Attention of S query tokens per sequence over the cache.
 
-    q: [B,S,Hq,D].  Token s of sequence b is single-token attention with
-    lens[b] - (S-1-s) rows (the last token sees lens[b] rows; each earlier
-    token one row fewer), with the window applied per token.
+    q: [B,S,Hq,D].  Causal (the default): token s of sequence b is
+    single-token attention with lens[b] - (S-1-s) rows (the last token sees
+    lens[b] rows; each earlier token one row fewer), with the window applied
+    per token.  Bidirectional (fusedtok README, attention_prefill row,
+    "causal / bidirectional"): every token sees the same lens[b] rows.
     Returns (out [B,S,Hq,D], lse [B,S,Hq]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -338,7 +341,7 @@ def attend_multi(q, k_cache, v_cache, lens, window: int = 0, scale: float = 0.0)
     out = np.zeros((B, S, Hq, v_cache.shape[3]))
     lse = np.full((B, S, Hq), -math.inf)
     for s in range(S):
-        lens_s = np.asarray(lens, np.int64) - (S - 1 - s)
+        lens_s = np.asarray(lens, np.int64) - ((S - 1 - s) if causal else 0)
         out[:, s], lse[:, s] = attend(q[:, s], k_cache, v_cache, lens_s, window, scale)
     return out, lse
 
@@ -447,7 +450,8 @@ def decode_step(w, split: bool = False, scale: float = 0.0):
         else:
             q_hat, kc, vc = q, w.k_cache, w.v_cache
         res = dict(q_hat=q_hat, k_cache=kc, v_cache=vc)
-        res["out"], res["lse"] = attend_multi(q_hat, kc, vc, w.lens, w.window, scale)
+        res["out"], res["lse"] = attend_multi(q_hat, kc, vc, w.lens, w.window, scale,
+                                              causal=getattr(w, "causal", True))
         return res
     if w.pos is not None:
         q_hat, kc, vc = qkv_prologue(

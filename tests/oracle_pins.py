@@ -612,6 +612,49 @@ def pin_attend_multi_causal(O):
             assert not np.array_equal(out2[:, S - 1], out[:, S - 1])
 
 
+def pin_attend_multi_bidirectional_matches_bruteforce(O):
+    """Bidirectional (attention_prefill row, "causal / bidirectional"):
+    every token attends the same lens[b] rows, window counted from there."""
+    rng = _rng(73)
+    B, S, Hq, Hkv, D, T = 2, 3, 4, 2, 6, 9
+    q = rng.standard_normal((B, S, Hq, D))
+    kc, vc = _bits(rng, (B, Hkv, T, D)), _bits(rng, (B, Hkv, T, D))
+    K, V = _torch_bf16_to_f64(kc), _torch_bf16_to_f64(vc)
+    for lens, window in (((9, 5), 0), ((7, 3), 4), ((0, 2), 0)):
+        out, lse = O.attend_multi(q, kc, vc, np.array(lens, np.int32), window, 0.0,
+                                  causal=False)
+        for s in range(S):
+            bo, bl = BF.attend(q[:, s].tolist(), K.tolist(), V.tolist(), list(lens), window, 0.0)
+            _close(out[:, s], np.array(bo), 1e-12, "bidirectional out")
+            assert np.allclose(lse[:, s], np.array(bl), atol=1e-12, rtol=0) or \
+                np.array_equal(np.isinf(lse[:, s]), np.isinf(np.array(bl)))
+
+
+def pin_prefill_equal_keys_closed_form(O):
+    """Fresh sequence of S tokens whose K rows are all equal: every score of a
+    row is the same, so causal token s averages V rows 0..s and its LSE is
+    scale * q.k + ln(s + 1); bidirectional tokens all average the S rows."""
+    rng = _rng(74)
+    B, S, Hq, Hkv, D = 1, 5, 2, 1, 8
+    T = S + 3
+    q = rng.standard_normal((B, S, Hq, D))
+    krow = _bits(rng, (D,))
+    kc = np.broadcast_to(krow, (B, Hkv, T, D)).copy()
+    vc = _bits(rng, (B, Hkv, T, D))
+    V = _torch_bf16_to_f64(vc)[0, 0]
+    k = _torch_bf16_to_f64(krow)
+    lens = np.array([S], np.int32)
+    out, lse = O.attend_multi(q, kc, vc, lens)
+    outb, lseb = O.attend_multi(q, kc, vc, lens, causal=False)
+    for s in range(S):
+        for h in range(Hq):
+            sc = float(q[0, s, h] @ k) / math.sqrt(D)
+            _close(out[0, s, h], V[:s + 1].mean(axis=0), 1e-12, "causal mean")
+            assert abs(lse[0, s, h] - (sc + math.log(s + 1))) < 1e-12
+            _close(outb[0, s, h], V[:S].mean(axis=0), 1e-12, "bidirectional mean")
+            assert abs(lseb[0, s, h] - (sc + math.log(S))) < 1e-12
+
+
 def pin_prologue_multi_matches_bruteforce(O):
     """S new tokens: token s normalised and rotated at pos + s, its K/V row
     appended at row pos + s, every other row untouched."""

@@ -132,18 +132,19 @@ def _table_variant(kind):
     return f
 
 
-def _multi_off_by_one(q, k_cache, v_cache, lens, window=0, scale=0.0):
+def _multi_off_by_one(q, k_cache, v_cache, lens, window=0, scale=0.0, causal=True):
     q = np.asarray(q, np.float64)
     B, S = q.shape[:2]
     out = np.zeros(q.shape)
     lse = np.full(q.shape[:3], -math.inf)
     for s in range(S):
         out[:, s], lse[:, s] = R.attend(q[:, s], k_cache, v_cache,
-                                        np.asarray(lens, np.int64) - (S - s), window, scale)
+                                        np.asarray(lens, np.int64) - (S - s if causal else 1),
+                                        window, scale)
     return out, lse
 
 
-def _multi_window_from_last(q, k_cache, v_cache, lens, window=0, scale=0.0):
+def _multi_window_from_last(q, k_cache, v_cache, lens, window=0, scale=0.0, causal=True):
     q = np.asarray(q, np.float64)
     B, S = q.shape[:2]
     out = np.zeros(q.shape)
@@ -325,6 +326,19 @@ def _prologue_variant(kind):
     return f
 
 
+def _multi_causal_flag_ignored(q, k_cache, v_cache, lens, window=0, scale=0.0, causal=True):
+    return _orig["attend_multi"](q, k_cache, v_cache, lens, window, scale)
+
+
+def _multi_bidirectional_first_token_rows(q, k_cache, v_cache, lens, window=0, scale=0.0,
+                                          causal=True):
+    if causal:
+        return _orig["attend_multi"](q, k_cache, v_cache, lens, window, scale)
+    S = np.asarray(q).shape[1]
+    return _orig["attend_multi"](q, k_cache, v_cache, np.asarray(lens, np.int64) - (S - 1),
+                                 window, scale, causal=False)
+
+
 MUTANTS = {
     "bf16_truncate": {"f64_to_bf16": _bf16_truncate},
     "bf16_double_round": {"f64_to_bf16": _bf16_double_round},
@@ -367,6 +381,8 @@ MUTANTS = {
     "multi_token_off_by_one": {"attend_multi": _multi_off_by_one},
     "multi_window_from_last_token": {"attend_multi": _multi_window_from_last},
     "multi_prologue_last_token_position": {"qkv_prologue_multi": _prologue_multi_same_pos},
+    "prefill_causal_flag_ignored": {"attend_multi": _multi_causal_flag_ignored},
+    "prefill_bidirectional_first_token_rows": {"attend_multi": _multi_bidirectional_first_token_rows},
 }
 
 

@@ -1,0 +1,179 @@
+"""Prefill on the matrix cores (gqa_attn_prefill): S query tokens per
+sequence over the cache, causal or bidirectional (the fusedtok README's
+attention_prefill row), any S and any group size.  CPU: host-side validation
+of the C ABI.  GPU: against the fp64 oracle on seeded workloads -- fresh
+sequences and chunks at the end of a longer cache, fp32 q from the prologue
+and bf16 q given directly, ragged row blocks, every group size, D = 64,
+windows, ragged lengths, rows with no key, NaN outside the attended rows --
+and the full-size chunked-prefill config on sampled tokens."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import reference as O
+
+A16 = 0x100000        # stand-in device addresses: every call below fails on the host
+
+
+@pytest.fixture(scope="module")
+def G():
+    import gqa_attention_kv_amd
+    return gqa_attention_kv_amd
+
+
+def test_prefill_validation(G):
+    def call(q=A16, S=64, causal=1, Hq=32, Hkv=8, D=128, qd=1, od=0, scale=0.0, out=A16,
+             lse=None):
+        return G.lib.gqa_attn_prefill(q, qd, A16, A16, A16, S, causal, 0, scale, out, od, lse,
+                                      1, Hq, Hkv, D, 4096, None)
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(S=0) == -2
+    assert call(causal=2) == -7
+    assert call(scale=math.inf) == -7
+    assert call(Hq=24, Hkv=8) == -3          # G = 3
+    assert call(D=96) == -3
+    assert call(qd=5) == -3
+    assert call(q=A16 + 8) == -6
+    assert call(lse=A16 + 2) == -6
+    assert call(Hq=30, Hkv=8) == -2          # Hq not a multiple of Hkv
+
+
+def _step(w, **kw):
+    from gqa_attention_kv_amd import runner
+    step = runner.DeviceStep(w, mode="prefill", **kw)
+    step.run()
+    return step.results()
+
+
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# (config, overrides, what the case covers)
+CASES = [
+    ("7f", dict(S=256, L=256), "fresh causal, prologue fp32 q, 8 row blocks"),
+    ("7f", dict(S=200, L=300), "fresh, T > S, ragged last row block"),
+    ("7f", dict(S=150, L=160, causal=False), "fresh bidirectional"),
+    ("6", dict(B=2, L=300, S=64), "chunk after 300 rows, prologue"),
+    ("6", dict(B=2, L=500, S=100, Hq=16, Hkv=2), "G=8, ragged row block"),
+    ("6", dict(B=2, L=200, S=130, Hq=8, Hkv=8), "G=1"),
+    ("6", dict(B=1, L=100, S=20, Hq=16, Hkv=1), "G=16"),
+    ("6", dict(B=1, L=64, S=9, Hq=4, Hkv=2), "G=2, fewer rows than one block"),
+    ("1", dict(S=50), "D=64, last 50 rows of 128"),
+    ("1", dict(S=40, causal=False, layout="noprologue"), "D=64 bidirectional, bf16 q"),
+    ("5", dict(B=2, L=2000, window=300, S=200), "window per token, QK-norm, G=8"),
+    ("5", dict(B=2, L=800, window=64, S=100, causal=False), "window, bidirectional"),
+    ("3", dict(B=4, L=1200, S=96, lmin=96), "ragged lengths, bf16 out"),
+    ("7", dict(B=2, L=1000, S=128), "chunk with bf16 q (no prologue)"),
+    ("7", dict(B=2, L=700, S=70, out_dtype="f32"), "bf16 q, fp32 out"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over,what", CASES,
+                         ids=[f"cfg{c[0]}_{i}" for i, c in enumerate(CASES)])
+def test_gpu_prefill(name, over, what):
+    _gpu()
+    from test_gpu_parity import check_attention
+    from test_multi_token import check_prologue_multi
+    w = W.make(name, **over)
+    print(f"\n[case] prefill cfg={name} {over} ({what})", flush=True)
+    ref = O.decode_step(w)
+    got = _step(w)
+    check_attention(got, ref, w.out_dtype, f"prefill {name} {over}")
+    if w.pos is not None:
+        check_prologue_multi(w, got, ref, f"prefill {name} {over}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("causal", [True, False])
+def test_gpu_prefill_poisoned_rows(causal):
+    """Rows outside every token's range hold bf16 NaN and must not be read
+    into the result (they may be loaded only as masked keys of rows the
+    workgroup attends, which hold finite values)."""
+    _gpu()
+    from test_gpu_parity import check_attention
+    w = W.make("3", B=3, L=900, S=80, lmin=80, window=150, causal=causal)
+    print(f"\n[case] prefill poisoned rows causal={causal}", flush=True)
+    ref = O.decode_step(w)
+    got = _step(w, poison=True)
+    check_attention(got, ref, w.out_dtype, "prefill poisoned")
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_rows_without_keys():
+    """lens smaller than S: the first tokens of a causal chunk see no row
+    (out = 0, lse = -inf); a zero length empties the whole sequence."""
+    _gpu()
+    from test_gpu_parity import check_attention
+    w = W.make("7", B=3, L=400, S=64)
+    w.lens[:] = np.array([30, 0, 400], np.int32)
+    print("\n[case] prefill rows without keys", flush=True)
+    ref = O.decode_step(w)
+    got = _step(w)
+    check_attention(got, ref, w.out_dtype, "prefill empty rows")
+    assert np.all(got["out"][0, :33] == 0) and np.all(got["lse"][0, :33] == -math.inf)
+    assert np.all(got["out"][1] == 0)
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_matches_decode_paths():
+    """S = 1 is single-token decode; small G*S is the multi-token decode:
+    the prefill kernel agrees with both within the parity bar."""
+    _gpu()
+    import torch
+    from gqa_attention_kv_amd import runner
+    w1 = W.make("2a")
+    a = runner.DeviceStep(w1, mode="unsplit")
+    a.run()
+    b = _step(w1)
+    ra = a.results()
+    assert float(np.max(np.abs(ra["out"] - b["out"]))) <= 1e-3
+    w4 = W.make("6", B=2, L=600, S=4)
+    c = runner.DeviceStep(w4, mode="unsplit")
+    c.run()
+    rc = c.results()
+    d = _step(w4)
+    assert float(np.max(np.abs(rc["out"] - d["out"]))) <= 1.5e-2
+    torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_bit_identical_reruns():
+    _gpu()
+    from gqa_attention_kv_amd import runner
+    w = W.make("7", B=2, L=900, S=200)
+    step = runner.DeviceStep(w, mode="prefill")
+    step.run()
+    r1 = step.results()
+    step.run()
+    r2 = step.results()
+    assert np.array_equal(r1["out"], r2["out"]) and np.array_equal(r1["lse"], r2["lse"])
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_full_size_sampled():
+    """The chunked-prefill config at full size (4 x 1024 tokens over 8192
+    rows, the launch the benchmark times), checked on sampled tokens: the
+    first and last of the chunk, the edges of 128-row blocks, and a few
+    seeded others, each against single-token attention over its own rows."""
+    _gpu()
+    from test_gpu_parity import OUT_TOL, LSE_TOL
+    w = W.make("7")
+    print("\n[case] prefill full size cfg 7", flush=True)
+    got = _step(w)
+    q = O.bf16_to_f64(w.q)
+    rng = np.random.default_rng(77)
+    toks = sorted({0, 1, 31, 32, w.S // 2, w.S - 2, w.S - 1,
+                   *rng.integers(0, w.S, size=3).tolist()})
+    for s in toks:
+        lens_s = w.lens.astype(np.int64) - (w.S - 1 - s)
+        ro, rl = O.attend(q[:, s], w.k_cache, w.v_cache, lens_s, w.window, 0.0)
+        err = float(np.max(np.abs(got["out"][:, s] - ro)))
+        assert err <= OUT_TOL[w.out_dtype], (s, err)
+        assert float(np.max(np.abs(got["lse"][:, s] - rl))) <= LSE_TOL, s

@@ -125,6 +125,8 @@ class Workload:
     # query tokens per sequence (causal among themselves); with S > 1, q is
     # [B,S,Hq,D], k_new/v_new [B,S,Hkv,D], token s at position pos[b] + s
     S: int = 1
+    # False: every token attends all lens[b] rows (bidirectional prefill)
+    causal: bool = True
 
     @property
     def prologue(self) -> bool:
@@ -140,15 +142,29 @@ class Workload:
         start (the window counts back from each token's own end)."""
         n = np.clip(self.lens.astype(np.int64), 0, self.T)
         if self.window > 0:
-            n0 = np.clip(self.lens.astype(np.int64) - (self.S - 1), 0, self.T)
+            back = (self.S - 1) if self.causal else 0
+            n0 = np.clip(self.lens.astype(np.int64) - back, 0, self.T)
             return n - np.maximum(0, n0 - self.window)
         return n
+
+    def token_rows(self) -> np.ndarray:
+        """Rows each (sequence, token) attends, int64 [B,S]: n_s - lo_s."""
+        back = np.arange(self.S - 1, -1, -1) if self.causal else np.zeros(self.S, np.int64)
+        n = np.clip(self.lens.astype(np.int64)[:, None] - back[None, :], 0, self.T)
+        lo = np.maximum(0, n - self.window) if self.window > 0 else np.zeros_like(n)
+        return n - lo
 
 
 def kv_bytes(w: Workload) -> int:
     """Algorithmic KV-cache bytes one decode step reads: K and V rows of the
     attended window, bf16, every KV head of every sequence."""
     return int(w.attended().sum()) * w.Hkv * w.D * 2 * 2
+
+
+def attention_flops(w: Workload) -> int:
+    """Algorithmic FLOPs of the attention contractions: 2 D for q.k plus 2 D
+    for p v per (query head, attended row) pair."""
+    return int(w.token_rows().sum()) * w.Hq * 4 * w.D
 
 
 # name -> (base parameters).  Sizes may be overridden for reduced test cases.
@@ -177,6 +193,15 @@ CONFIGS: Dict[str, dict] = {
     # (token, head) rows of each KV head share every cache row read
     "6": dict(seed=6, B=8, Hq=32, Hkv=8, D=128, L=8192, layout="append", S=4,
               window=0, theta=5e5, norm=False, out_dtype="bf16", part_tokens=1024),
+    # chunked prefill: the Llama-3-8B shape with the last S=1024 tokens of an
+    # 8192-row cache as causal queries, q given in bf16 (the matrix-core path)
+    "7": dict(seed=7, B=4, Hq=32, Hkv=8, D=128, L=8192, layout="noprologue", S=1024,
+              window=0, theta=0.0, norm=False, out_dtype="bf16", part_tokens=1024),
+    # fresh-sequence causal prefill of S=1024 tokens at D=128 (the shape of the
+    # fusedtok attention_prefill benchmark row), Llama-3-8B heads, prologue
+    # on every token
+    "7f": dict(seed=8, B=1, Hq=32, Hkv=8, D=128, L=1024, layout="fresh", S=1024,
+               window=0, theta=5e5, norm=False, out_dtype="bf16", part_tokens=1024),
 }
 
 
@@ -192,6 +217,8 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
       append     T = L + 64, new tokens at pos = L .. L+S-1, lens = L + S
       ragged     T = L, lens ~ U{lmin..L}, pos = lens - S
       noprologue T = L, lens = L, q given directly
+      fresh      T = L (>= S), the S tokens of a new sequence at pos = 0 .. S-1,
+                 lens = S
     (S = 1 unless overridden: the query tokens per sequence.)
     """
     p = dict(CONFIGS[name])
@@ -218,6 +245,12 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
         T = L
         lens = np.full(B, L, np.int32)
         pos = None
+    elif layout == "fresh":
+        T = p.get("T", L)
+        if T < S:
+            raise ValueError("a fresh sequence needs T >= S")
+        lens = np.full(B, S, np.int32)
+        pos = np.zeros(B, np.int32)
     else:
         raise ValueError(layout)
 
@@ -258,4 +291,5 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
         out_dtype=p["out_dtype"], part_tokens=int(p["part_tokens"]),
         q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
         w_q=w_q, w_k=w_k, peaky_rows=peaky_rows,
-        rope_layout=p.get("rope_layout", "neox"), rope_scaling=p.get("rope_scaling"), S=S)
+        rope_layout=p.get("rope_layout", "neox"), rope_scaling=p.get("rope_scaling"), S=S,
+        causal=bool(p.get("causal", True)))
