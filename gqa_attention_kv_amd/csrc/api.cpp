@@ -150,6 +150,8 @@ int gqa_qkv_prologue_ex(const void* q, const void* k_new, const void* v_new,
   if (rc) return rc;
   if (!dtype_ok(in_dtype)) return GQA_ERR_UNSUPPORTED;
   if (S < 1 || (int64_t)B * S * (Hq + Hkv) > kMaxIndex / D) return GQA_ERR_SHAPE;
+  // the prologue's grid: one row of workgroups per (sequence, token)
+  if ((int64_t)B * S > kMaxWorkgroups || Hq + Hkv > 65535) return GQA_ERR_SHAPE;
   if (q_bstride < (int64_t)S * Hq * D || kv_bstride < (int64_t)S * Hkv * D) return GQA_ERR_SHAPE;
   if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
   if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
@@ -167,7 +169,7 @@ int gqa_qkv_prologue_ex(const void* q, const void* k_new, const void* v_new,
   a.rope_interleaved = rope_layout == GQA_ROPE_INTERLEAVED;
   a.rope_mscale = (float)rope_mscale;
   if (a.rope)
-    for (int i = 0; i < D / 2; ++i) a.inv_freq[i] = inv_freq[i];
+    for (int i = 0; i < D / 2; ++i) a.inv_freq_rev[i] = inv_freq[i] / 6.283185307179586476925;
   a.pos = pos; a.S = S; a.q_out = q_out; a.k_cache = k_cache; a.v_cache = v_cache;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   return gqa::launch_prologue(a, stream);

@@ -21,21 +21,25 @@
 // Lane l, with n = l % 16 and k4 = l / 16, per 16-row block (columns = query
 // rows, so a row's softmax state stays in its own lanes):
 //   QK: S^T[16 keys x 16 rows] += K[16 x 32] * q^T[32 x 16] per 32-wide slice
-//       of D (v_mfma_f32_16x16x32_bf16).  The result leaves lane l holding
-//       keys 4 k4 + i (i < 4) of query row n.  An fp32 q is split into bf16
-//       hi + lo and takes two calls per slice; a bf16 q takes one.
-//   PV: O^T[16 cols x 16 rows] += V^T[16 x 32] * P^T[32 x 16] per D/16 column
-//       block, with the 16 keys as 32 k-indices k = 8 k4 + 2 i + x: x = 0 is
-//       the bf16 hi part of P, x = 1 its lo part (P keeps ~16 mantissa bits),
-//       and V appears at both k of its key.  Lane l's P operand is exactly
-//       the four scores the QK step left in it.  Output column n of block b
-//       stands for d = (D/16) n + b, so a lane reads one contiguous D/8-byte
-//       piece of each V row from LDS for all blocks.
-// Online softmax per row with a lazy rescale: the reference maximum only
-// moves when a tile's maximum exceeds it by more than 2^8 (in exp2 units),
-// so P stays below 256 and O is rarely rescaled.  Keys outside a row's
-// range are masked only in tiles that are not wholly inside every range of
-// the wave's rows.
+//       of D (v_mfma_f32_16x16x32_bf16), for both 16-key halves of the tile.
+//       The results leave lane l holding keys 4 k4 + i and 16 + 4 k4 + i
+//       (i < 4) of query row n.  An fp32 q is split into bf16 hi + lo and
+//       takes two calls per slice; a bf16 q takes one.
+//   PV: O^T[16 cols x 16 rows] += V^T[16 x 32] * P^T[32 x 16] per 16-column
+//       block, the 32 keys of the tile as the k index in the order lane l's
+//       P operand already holds them: k = 8 k4 + e is key 4 k4 + e (e < 4)
+//       or 16 + 4 k4 + e - 4.  V is stored transposed in LDS with its keys
+//       in that order, so lane l's V operand is one 16-byte read.  P is
+//       rounded once to bf16 when the output is bf16 (an error of at most
+//       2^-9 sum p|V|, the order of the output's own rounding); for an fp32
+//       output P is carried as bf16 hi + lo (~16 mantissa bits) in two calls
+//       on the same V operand.
+// The tiles pass through two LDS stages: the next tile is stashed while the
+// current one is computed, with one barrier per tile.  Online softmax per
+// row with a lazy rescale: the reference maximum only moves when a tile's
+// maximum exceeds it by more than 2^8 (in exp2 units), so P stays below 256
+// and O is rarely rescaled.  Keys outside a row's range are masked only in
+// tiles that are not wholly inside every range of the wave's rows.
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/gqa_decode.h"
@@ -51,7 +55,12 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;                  // two 16-row blocks
 constexpr int kRows = kWaves * kRowsPerWave;      // query rows per workgroup
-constexpr int kKeys = 32;                         // cache rows per LDS tile
+#ifndef GQA_PREFILL_KEYS
+#define GQA_PREFILL_KEYS 64
+#endif
+constexpr int kKeys = GQA_PREFILL_KEYS;           // cache rows per LDS tile (32 or 64)
+constexpr int kKB = kKeys / 16;                   // 16-key blocks per tile
+static_assert(kKeys == 32 || kKeys == 64, "tile of 32 or 64 keys");
 constexpr float kRescaleLog2 = 8.0f;              // lazy-rescale threshold
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, uint32_t bytes) {
@@ -59,35 +68,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-// x as a bf16 pair: hi = bf16(x) in the low half, lo = bf16(x - hi) above.
-__device__ __forceinline__ uint32_t hi_lo_bf16(float x) {
-  const __bf16 h = (__bf16)x;
-  const bf16x2_t v = {h, (__bf16)(x - (float)h)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// bf16 element e of a packed slice, copied into both halves of a dword.
-__device__ __forceinline__ uint32_t dup_half(uint32_t w, int e) {
-  return __builtin_amdgcn_perm(w, w, (e & 1) ? 0x03020302u : 0x01000100u);
-}
-
 __device__ __forceinline__ int clampi(int64_t v, int lo, int hi) {
   return (int)(v < lo ? lo : v > hi ? hi : v);
 }
 
-template <int D, bool QF32>
+// Position of key k of a tile in the transposed V rows: the order of the
+// PV k index within each 32-key half, 8 k4 + 4 kb + i for key 16 kb + 4 k4
+// + i of the half.
+__device__ __forceinline__ int vpos(int key) {
+  const int k = key & 31;
+  return (key & ~31) + 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+}
+
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 of a wave, in every lane:
+// v_permlane32_swap exchanges the wave's halves and v_permlane16_swap the
+// odd and even 16-lane rows (VALU ops, no LDS round trip).
+__device__ __forceinline__ float max_over_rows(float t) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
+                                                  false, false);
+  t = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t),
+                                                  false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Two floats as packed bf16 (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int D, bool QF32, bool PLO>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void
 attn_prefill_kernel(const PrefillArgs a) {
   constexpr int KC = D / 32;            // QK slices
   constexpr int VB = D / 16;            // PV column blocks
-  constexpr int VW = D / 32;            // dwords of a lane's V piece (D/8 bytes)
-  constexpr int ROW = D * 2 + 16;       // LDS row pitch in bytes (conflict-free reads)
+  constexpr int KROW = D * 2 + 16;      // K row pitch in LDS (conflict-free operand reads)
+  constexpr int VROW = kKeys * 2 + 16;  // pitch of a transposed V row (one column of V)
   constexpr int CPR = D / 8;            // 16-byte chunks per cache row
-  constexpr int FILL = kKeys * CPR / (kWaves * 64);   // chunks per thread per tile
-  static_assert(FILL >= 1, "tile fill");
+  constexpr int KFILL = kKeys * CPR / (kWaves * 64);   // K chunks per thread per tile
+  constexpr int VITEMS = (kKeys / 2) * CPR;            // (key pair, chunk) items per tile
+  constexpr int VFILL = (VITEMS + kWaves * 64 - 1) / (kWaves * 64);
+  constexpr int KBYTES = kKeys * KROW;
+  constexpr int STAGE = KBYTES + D * VROW;
+  static_assert(KFILL >= 1 && VITEMS % (kWaves * 64) == 0 || VITEMS < kWaves * 64,
+                "tile fill");
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k[kKeys * ROW];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v[kKeys * ROW];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
 
   const int Hq = a.Hq, Hkv = a.Hkv, S = a.S, T = a.T;
   const int G = Hq / Hkv;
@@ -112,7 +139,8 @@ attn_prefill_kernel(const PrefillArgs a) {
   const int rb = nrb - 1 - rbi;
   const int b = pair / Hkv, g = pair % Hkv;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, k4 = lane >> 4;
 
   const int len = a.lens[b];
@@ -203,150 +231,206 @@ attn_prefill_kernel(const PrefillArgs a) {
 
   const int ntiles = kend > kbeg ? (kend - kbeg + kKeys - 1) / kKeys : 0;
 
-  // Tile fill: thread t moves chunks t + 256 f of the tile (row-major, CPR
-  // chunks per row).  Rows past the range are clamped into it (they are
+  // Tile fill.  K: thread t moves chunks t + 256 f (row-major, CPR chunks a
+  // row).  V: item t + 256 f (< VITEMS) is chunk it / (kKeys/2) of keys
+  // 2 (it % (kKeys/2)) and the next, which land side by side in the
+  // transposed rows.  Keys past the range are clamped into it (they are
   // masked below, and a row the workgroup attends holds finite values).
-  u32x4_t fk[FILL], fv[FILL];
+  constexpr int PAIRS = kKeys / 2;
+  const bool vthread = VITEMS >= kWaves * 64 || tid < VITEMS;
+  u32x4_t fk[KFILL], fv0[VFILL], fv1[VFILL];
+  auto clamp_key = [&](int key) { return key < kend ? key : kend - 1; };
   auto fetch = [&](int tile) {
+    const int base = kbeg + kKeys * tile;
 #pragma unroll
-    for (int f = 0; f < FILL; ++f) {
-      const int ci = threadIdx.x + kWaves * 64 * f;
-      const int rr = ci / CPR, cc = ci % CPR;
-      int key = kbeg + kKeys * tile + rr;
-      key = key < kend ? key : kend - 1;
-      const uint32_t off = (uint32_t)key * (uint32_t)(D * 2) + 16u * cc;
+    for (int f = 0; f < KFILL; ++f) {
+      const int ci = tid + kWaves * 64 * f;
+      const uint32_t off = (uint32_t)clamp_key(base + ci / CPR) * (uint32_t)(D * 2) +
+                           16u * (ci % CPR);
       fk[f] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      fv[f] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+    if (vthread) {
+#pragma unroll
+      for (int f = 0; f < VFILL; ++f) {
+        const int it = tid + kWaves * 64 * f;
+        const int vp = it % PAIRS, vm = it / PAIRS;
+        const uint32_t off0 =
+            (uint32_t)clamp_key(base + 2 * vp) * (uint32_t)(D * 2) + 16u * vm;
+        const uint32_t off1 =
+            (uint32_t)clamp_key(base + 2 * vp + 1) * (uint32_t)(D * 2) + 16u * vm;
+        fv0[f] = __builtin_bit_cast(u32x4_t,
+                                    __builtin_amdgcn_raw_buffer_load_b128(rv, off0, 0, 0));
+        fv1[f] = __builtin_bit_cast(u32x4_t,
+                                    __builtin_amdgcn_raw_buffer_load_b128(rv, off1, 0, 0));
+      }
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int stage) {
+    unsigned char* st = lds + stage * STAGE;
 #pragma unroll
-    for (int f = 0; f < FILL; ++f) {
-      const int ci = threadIdx.x + kWaves * 64 * f;
-      const int rr = ci / CPR, cc = ci % CPR;
-      *reinterpret_cast<u32x4_t*>(lds_k + rr * ROW + 16 * cc) = fk[f];
-      *reinterpret_cast<u32x4_t*>(lds_v + rr * ROW + 16 * cc) = fv[f];
+    for (int f = 0; f < KFILL; ++f) {
+      const int ci = tid + kWaves * 64 * f;
+      *reinterpret_cast<u32x4_t*>(st + (ci / CPR) * KROW + 16 * (ci % CPR)) = fk[f];
     }
-  };
-
-  if (ntiles > 0) fetch(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();              // every wave is done with the previous tile
-    stash();
-    __syncthreads();
-    if (tile + 1 < ntiles) fetch(tile + 1);   // in flight during the compute
-    __builtin_amdgcn_sched_barrier(0);
-
-    const int k0 = kbeg + kKeys * tile;
-    if (!wave_live || k0 >= need_hi || k0 + kKeys <= need_lo) continue;   // wave-uniform
-    const bool full = k0 >= free_lo && k0 + kKeys <= free_hi;
-
-    // QK for both 16-key blocks and both row blocks.
-    f32x4_t s[2][2];
+    if (vthread) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < VFILL; ++f) {
+        const int it = tid + kWaves * 64 * f;
+        const int vp = it % PAIRS, vm = it / PAIRS;
+        // element e of the chunk is column 8 vm + e; keys 2 vp and 2 vp + 1
+        // pair up in one dword of that column's row
+        unsigned char* vt = st + KBYTES + 2 * vpos(2 * vp);
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const u32x4_t ka =
-            *reinterpret_cast<const u32x4_t*>(lds_k + (16 * kb + n) * ROW + 64 * c + 16 * k4);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          s[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qh[j][c]), s[kb][j],
-              0, 0, 0);
-          if constexpr (QF32)
-            s[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, ql[j][c]),
-                s[kb][j], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t w = __builtin_amdgcn_perm(fv1[f][e >> 1], fv0[f][e >> 1],
+                                                   (e & 1) ? 0x07060302u : 0x05040100u);
+          *reinterpret_cast<uint32_t*>(vt + (8 * vm + e) * VROW) = w;
         }
       }
     }
+  };
 
-    // Masks and the tile maximum of each row (raw scores; qscale > 0).
-    float mnew[2];
-    bool need[2];
+  if (ntiles > 0) {
+    fetch(0);
+    stash(0);
+    if (ntiles > 1) fetch(1);
+  }
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const unsigned char* cur = lds + (tile & 1) * STAGE;
+    const int k0 = kbeg + kKeys * tile;
+    const bool work = wave_live && k0 < need_hi && k0 + kKeys > need_lo;   // wave-uniform
+    f32x4_t s[kKB][2];
+    if (work) {
+      // QK for every 16-key block and both row blocks.
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (!full) {
+      for (int kb = 0; kb < kKB; ++kb) {
+        s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int c = 0; c < KC; ++c) {
+          const u32x4_t ka =
+              *reinterpret_cast<const u32x4_t*>(cur + (16 * kb + n) * KROW + 64 * c + 16 * k4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 16 * kb + 4 * k4 + i;
-            if (key < rlo[j] || key >= rhi[j]) s[kb][j][i] = -INFINITY;
+          for (int j = 0; j < 2; ++j) {
+            s[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qh[j][c]),
+                s[kb][j], 0, 0, 0);
+            if constexpr (QF32)
+              s[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, ql[j][c]),
+                  s[kb][j], 0, 0, 0);
           }
+        }
       }
-      float t = fmaxf(fmaxf(fmaxf(s[0][j][0], s[0][j][1]), fmaxf(s[0][j][2], s[0][j][3])),
-                      fmaxf(fmaxf(s[1][j][0], s[1][j][1]), fmaxf(s[1][j][2], s[1][j][3])));
-      t = fmaxf(t, __shfl_xor(t, 16, 64));
-      t = fmaxf(t, __shfl_xor(t, 32, 64));
-      mnew[j] = fmaxf(m[j], t);
-      // m = -inf with a finite maximum gives +inf (rescale); both -inf give
-      // NaN (no rescale: the row has seen no key yet).
-      need[j] = (mnew[j] - m[j]) * qscale > kRescaleLog2;
     }
-    if (__any(need[0] || need[1])) {
+    // Stash the next tile into the other stage (every wave finished reading
+    // that stage before the barrier that ended the previous trip), then
+    // fetch the one after: while the QK calls run, or -- with an fp32 q,
+    // whose hi and lo parts leave no registers for it -- after the PV calls.
+    constexpr bool kEarlyStash = !QF32;
+    if (kEarlyStash) {
+      if (tile + 1 < ntiles) stash((tile + 1) & 1);
+      if (tile + 2 < ntiles) fetch(tile + 2);
+    }
+    if (work) {
+      const bool full = k0 >= free_lo && k0 + kKeys <= free_hi;
+      // Masks and the tile maximum of each row (raw scores; qscale > 0).
+      float mnew[2];
+      bool need[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float alpha = need[j] ? __builtin_amdgcn_exp2f((m[j] - mnew[j]) * qscale) : 1.0f;
-        if (need[j]) m[j] = mnew[j];
-        l[j] *= alpha;
+        if (!full) {
 #pragma unroll
-        for (int v = 0; v < VB; ++v) o[j][v] *= alpha;
-      }
-    }
-
-    // P = exp2(s * qscale - m * qscale) as bf16 hi/lo pairs (the B operand).
-    u32x4_t pb[2][2];
+          for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float mref = m[j] == -INFINITY ? 0.0f : m[j] * qscale;
-      float ps = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j][i], qscale, -mref));
-          ps += p;
-          pb[j][kb][i] = hi_lo_bf16(p);
+            for (int i = 0; i < 4; ++i) {
+              const int key = k0 + 16 * kb + 4 * k4 + i;
+              if (key < rlo[j] || key >= rhi[j]) s[kb][j][i] = -INFINITY;
+            }
         }
-      l[j] += ps;
-    }
-
-    // PV: V rows 16 kb + 4 k4 + i at columns (D/16) n .. + D/16.
+        float t = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      uint32_t vw[4][VW];
+        for (int kb = 0; kb < kKB; ++kb)
+          t = fmaxf(t, fmaxf(fmaxf(s[kb][j][0], s[kb][j][1]), fmaxf(s[kb][j][2], s[kb][j][3])));
+        t = max_over_rows(t);
+        mnew[j] = fmaxf(m[j], t);
+        // m = -inf with a finite maximum gives +inf (rescale); both -inf give
+        // NaN (no rescale: the row has seen no key yet).
+        need[j] = (mnew[j] - m[j]) * qscale > kRescaleLog2;
+      }
+      if (__any(need[0] || need[1])) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const unsigned char* src = lds_v + (16 * kb + 4 * k4 + i) * ROW + (D / 8) * n;
-        if constexpr (VW == 4) {
-          const u32x4_t t = *reinterpret_cast<const u32x4_t*>(src);
-          vw[i][0] = t[0]; vw[i][1] = t[1]; vw[i][2] = t[2]; vw[i][3] = t[3];
-        } else {
-          const uint2 t = *reinterpret_cast<const uint2*>(src);
-          vw[i][0] = t.x; vw[i][1] = t.y;
+        for (int j = 0; j < 2; ++j) {
+          const float alpha = need[j] ? __builtin_amdgcn_exp2f((m[j] - mnew[j]) * qscale) : 1.0f;
+          if (need[j]) m[j] = mnew[j];
+          l[j] *= alpha;
+#pragma unroll
+          for (int v = 0; v < VB; ++v) o[j][v] *= alpha;
         }
       }
+
+      // P = exp2(s * qscale - m * qscale) as the B operands, one per 32-key
+      // half h: bf16 (hi) and, for an fp32 output, the bf16 remainder (lo).
+      // Word w of half h holds k = 2w, 2w + 1: keys 32h + (4 k4 + 2w, + 1)
+      // for w < 2, 32h + (16 + 4 k4 + 2w - 4, + 1) for w >= 2.
+      constexpr int NH = kKB / 2;
+      u32x4_t ph[NH][2], pl[NH][2];
 #pragma unroll
-      for (int v = 0; v < VB; ++v) {
-        u32x4_t va;
+      for (int j = 0; j < 2; ++j) {
+        const float mref = m[j] == -INFINITY ? 0.0f : m[j] * qscale;
+        float p[kKB][4];
+        float ps = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) va[i] = dup_half(vw[i][v >> 1], v);
+        for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pb[j][kb]), o[j][v],
-              0, 0, 0);
+          for (int i = 0; i < 4; ++i) {
+            p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j][i], qscale, -mref));
+            ps += p[kb][i];
+          }
+        l[j] += ps;
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float pa = p[2 * hh + (w >> 1)][2 * (w & 1)];
+            const float pb = p[2 * hh + (w >> 1)][2 * (w & 1) + 1];
+            const uint32_t hw = pack_bf16(pa, pb);
+            ph[hh][j][w] = hw;
+            if constexpr (PLO)
+              pl[hh][j][w] = pack_bf16(pa - __uint_as_float(hw << 16),
+                                       pb - __uint_as_float(hw & 0xffff0000u));
+          }
       }
+
+      // PV: column block v, lane row n is column 16 v + n of V.
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int v = 0; v < VB; ++v) {
+          const u32x4_t va = *reinterpret_cast<const u32x4_t*>(
+              cur + KBYTES + (16 * v + n) * VROW + 64 * hh + 16 * k4);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, ph[hh][j]),
+                o[j][v], 0, 0, 0);
+            if constexpr (PLO)
+              o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pl[hh][j]),
+                  o[j][v], 0, 0, 0);
+          }
+        }
     }
+    if (!kEarlyStash) {
+      if (tile + 1 < ntiles) stash((tile + 1) & 1);
+      if (tile + 2 < ntiles) fetch(tile + 2);
+    }
+    __syncthreads();
   }
 
-  // Normalise and store.  Lane (n, k4) holds, for row n of block j,
-  // columns d = (D/16)(4 k4 + i) + v of block v, i < 4: for each i the VB
-  // columns from (D/16)(4 k4 + i) on are consecutive.
+  // Normalise and store.  Lane (n, k4) holds, for row n of block j, columns
+  // 16 v + 4 k4 + i (i < 4) of block v.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float lt = l[j];
@@ -358,26 +442,18 @@ attn_prefill_kernel(const PrefillArgs a) {
     const int64_t orow = ((int64_t)b * S + t) * Hq + (int64_t)g * G + h;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = VB * (4 * k4 + i);
-      float y[VB];
-#pragma unroll
-      for (int v = 0; v < VB; ++v) y[v] = o[j][v][i] * inv;
+    for (int v = 0; v < VB; ++v) {
+      const int d0 = 16 * v + 4 * k4;
+      const float y0 = o[j][v][0] * inv, y1 = o[j][v][1] * inv;
+      const float y2 = o[j][v][2] * inv, y3 = o[j][v][3] * inv;
       if (a.out_bf16) {
         uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + orow * D + d0;
-        uint32_t w[VB / 2];
-#pragma unroll
-        for (int v = 0; v < VB / 2; ++v)
-          w[v] = (uint32_t)f32_to_bf16(y[2 * v]) | ((uint32_t)f32_to_bf16(y[2 * v + 1]) << 16);
-        if constexpr (VB == 8)
-          *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
-        else
-          *reinterpret_cast<uint2*>(dst) = uint2{w[0], w[1]};
+        *reinterpret_cast<uint2*>(dst) =
+            uint2{(uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16),
+                  (uint32_t)f32_to_bf16(y2) | ((uint32_t)f32_to_bf16(y3) << 16)};
       } else {
         float* dst = reinterpret_cast<float*>(a.out) + orow * D + d0;
-#pragma unroll
-        for (int v = 0; v < VB; v += 4)
-          *reinterpret_cast<float4*>(dst + v) = float4{y[v], y[v + 1], y[v + 2], y[v + 3]};
+        *reinterpret_cast<float4*>(dst) = float4{y0, y1, y2, y3};
       }
     }
     if (a.lse_out != nullptr && k4 == 0)
@@ -388,7 +464,12 @@ attn_prefill_kernel(const PrefillArgs a) {
 template <int D, bool QF32>
 int launch_t(const PrefillArgs& a, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)a.B * a.Hkv * a.row_blocks);
-  hipLaunchKernelGGL((attn_prefill_kernel<D, QF32>), dim3(blocks), dim3(kWaves * 64), 0, s, a);
+  if (a.out_bf16)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QF32, false>), dim3(blocks), dim3(kWaves * 64),
+                       0, s, a);
+  else
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QF32, true>), dim3(blocks), dim3(kWaves * 64),
+                       0, s, a);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 

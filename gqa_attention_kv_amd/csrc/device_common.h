@@ -1,5 +1,6 @@
 // Device helpers shared by the gfx950 kernels: bf16 packing, DPP lane
-// exchange, and wave-level reductions.  Internal header.
+// exchange, wave-level reductions and a float64 sin/cos of a reduced angle.
+// Internal header.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -68,6 +69,40 @@ __device__ __forceinline__ float group_sum_shfl(float v) {
 #pragma unroll
   for (int m = 1; m < N; m <<= 1) v += __shfl_xor(v, m, 64);
   return v;
+}
+
+// sin and cos of |x| <= pi in float64, with few registers: x = k pi/2 + r
+// (k = rint(2x/pi), pi/2 in two parts, |r| <= pi/4), then the Taylor series
+// of sin r through r^17 and of cos r through r^16 (truncation below 1e-16
+// on |r| <= pi/4, Horner form), and the quadrant k mod 4 swaps and signs.
+__device__ __forceinline__ void sincos_pi_f64(double x, double* s, double* c) {
+  constexpr double kHalfPi1 = 1.5707963267948966;      // fp64 nearest pi/2
+  constexpr double kHalfPi2 = 6.123233995736766e-17;   // pi/2 - kHalfPi1
+  const double k = rint(x * 0.6366197723675814);
+  const double r = (x - k * kHalfPi1) - k * kHalfPi2;
+  const double z = r * r;
+  double ps = 1.0 / 355687428096000.0;                 // 1/17!
+  ps = fma(ps, -z, 1.0 / 1307674368000.0);             // 1/15!
+  ps = fma(ps, -z, 1.0 / 6227020800.0);                // 1/13!
+  ps = fma(ps, -z, 1.0 / 39916800.0);                  // 1/11!
+  ps = fma(ps, -z, 1.0 / 362880.0);                    // 1/9!
+  ps = fma(ps, -z, 1.0 / 5040.0);                      // 1/7!
+  ps = fma(ps, -z, 1.0 / 120.0);                       // 1/5!
+  ps = fma(ps, -z, 1.0 / 6.0);                         // 1/3!
+  const double sr = fma(-z * r, ps, r);
+  double pc = 1.0 / 20922789888000.0;                  // 1/16!
+  pc = fma(pc, -z, 1.0 / 87178291200.0);               // 1/14!
+  pc = fma(pc, -z, 1.0 / 479001600.0);                 // 1/12!
+  pc = fma(pc, -z, 1.0 / 3628800.0);                   // 1/10!
+  pc = fma(pc, -z, 1.0 / 40320.0);                     // 1/8!
+  pc = fma(pc, -z, 1.0 / 720.0);                       // 1/6!
+  pc = fma(pc, -z, 1.0 / 24.0);                        // 1/4!
+  pc = fma(pc, -z, 0.5);                               // 1/2!
+  const double cr = fma(-z, pc, 1.0);
+  const int q = (int)k & 3;
+  const double sv = (q & 1) ? cr : sr, cv = (q & 1) ? sr : cr;
+  *s = (q & 2) ? -sv : sv;
+  *c = (q == 1 || q == 2) ? -cv : cv;
 }
 
 }  // namespace gqa

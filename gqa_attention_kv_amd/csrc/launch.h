@@ -29,7 +29,7 @@ struct PrologueArgs {
   uint16_t* k_cache;
   uint16_t* v_cache;
   int B, Hq, Hkv, D, T;
-  double inv_freq[kMaxHalfDim];   // rotary frequency of pair i (radians per position)
+  double inv_freq_rev[kMaxHalfDim];   // rotary frequency of pair i / (2 pi), float64
 };
 
 // Arguments of the attention kernel in all three modes, passed by value.
