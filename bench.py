@@ -57,6 +57,7 @@ WORKLOAD_NAMES = {
 }
 PREFILL_WORKLOADS = ("7", "7f")
 PREFILL_KERNEL = "attn_prefill_kernel"
+PREFILL_SRC = os.path.join(ROOT, "gqa_attention_kv_amd", "csrc", "attn_prefill_mfma.hip")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -84,7 +85,8 @@ def _parse():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn two rocprofv3 --pmc output directories "
                          "(FETCH_SIZE, WRITE_SIZE; each from a bench run with "
-                         "--copy-probe-mib) into profiles/attn_traffic_workload<W>.json")
+                         "--copy-probe-mib) into profiles/attn_traffic_workload<W>.json "
+                         "(the attention kernel of the workload: decode or prefill)")
     return ap.parse_args()
 
 
@@ -93,15 +95,23 @@ def _src_sha(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def _kernel_of(workload: str):
+    """(kernel name, kernel source) of the workload's dominant launch."""
+    if workload in PREFILL_WORKLOADS:
+        return PREFILL_KERNEL, PREFILL_SRC
+    return ATTN_KERNEL, ATTN_SRC
+
+
 def _traffic(workload: str):
     """HBM bytes per attention launch from committed rocprofv3 counters, if
-    they were taken on the current attention kernel source."""
+    they were taken on the current source of that kernel."""
     path = os.path.join(ROOT, "profiles", f"attn_traffic_workload{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("attn_src_sha") != _src_sha(ATTN_SRC):
+    kernel, src = _kernel_of(workload)
+    if rec.get("kernel") != kernel or rec.get("attn_src_sha") != _src_sha(src):
         return None
     return rec.get("bytes_per_launch")
 
@@ -116,12 +126,14 @@ def _pmc_rows(d: str):
         return list(csv.DictReader(f))
 
 
-def _per_launch(rows, counter):
+def _per_launch(rows, counter, kernel):
     """(mean KiB per attention dispatch, calibration factor from the copy
     probe: true bytes / counted bytes for a 256 MiB device copy)."""
     rows = [r for r in rows if r["Counter_Name"] == counter]
-    attn = [float(r["Counter_Value"]) for r in rows if ATTN_KERNEL in r["Kernel_Name"]]
-    last_attn = max(int(r["Dispatch_Id"]) for r in rows if ATTN_KERNEL in r["Kernel_Name"])
+    attn = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
+    if not attn:
+        raise SystemExit(f"{counter}: no {kernel} dispatches")
+    last_attn = max(int(r["Dispatch_Id"]) for r in rows if kernel in r["Kernel_Name"])
     copies = [float(r["Counter_Value"]) for r in rows
               if "copyBuffer" in r["Kernel_Name"] and int(r["Dispatch_Id"]) > last_attn]
     # the probe's 256 MiB copies are the largest copy dispatches after the timed loop
@@ -134,12 +146,13 @@ def _per_launch(rows, counter):
 
 
 def _record_traffic(workload: str, fetch_dir: str, write_dir: str):
-    f_kib, f_fac = _per_launch(_pmc_rows(fetch_dir), "FETCH_SIZE")
-    w_kib, w_fac = _per_launch(_pmc_rows(write_dir), "WRITE_SIZE")
+    kernel, src = _kernel_of(workload)
+    f_kib, f_fac = _per_launch(_pmc_rows(fetch_dir), "FETCH_SIZE", kernel)
+    w_kib, w_fac = _per_launch(_pmc_rows(write_dir), "WRITE_SIZE", kernel)
     rec = {
         "workload": workload,
-        "kernel": ATTN_KERNEL,
-        "attn_src_sha": _src_sha(ATTN_SRC),
+        "kernel": kernel,
+        "attn_src_sha": _src_sha(src),
         "fetch_kib_counted": round(f_kib, 1), "fetch_calibration": round(f_fac, 4),
         "write_kib_counted": round(w_kib, 1), "write_calibration": round(w_fac, 4),
         "bytes_per_launch": int(round((f_kib * f_fac + w_kib * w_fac) * 1024)),
@@ -388,7 +401,7 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "flops_per_launch": flops,
         }
     else:
