@@ -54,10 +54,16 @@ WORKLOAD_NAMES = {
     "7": "chunked prefill: the last 1024 tokens of four 8192-row sequences as causal "
          "queries, Llama-3-8B shape",
     "7f": "fresh-sequence causal prefill, S=1024, D=128, Llama-3-8B heads",
+    "8": "packed QKV projection of the 70B-shaped decode batch (M=8, K=8192, N=10240)",
+    "8a": "bf16 GEMV, one row, K=2048, N=8192",
+    "8b": "bf16 GEMV, one row, K=4096, N=14336",
 }
+GEMV_WORKLOADS = ("8", "8a", "8b")
+GEMV_KERNEL = "qkv_gemv_kernel"
 PREFILL_WORKLOADS = ("7", "7f")
 PREFILL_KERNEL = "attn_prefill_kernel"
 PREFILL_SRC = os.path.join(ROOT, "gqa_attention_kv_amd", "csrc", "attn_prefill_mfma.hip")
+GEMV_SRC = os.path.join(ROOT, "gqa_attention_kv_amd", "csrc", "qkv_gemv.hip")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -99,6 +105,8 @@ def _kernel_of(workload: str):
     """(kernel name, kernel source) of the workload's dominant launch."""
     if workload in PREFILL_WORKLOADS:
         return PREFILL_KERNEL, PREFILL_SRC
+    if workload in GEMV_WORKLOADS:
+        return GEMV_KERNEL, GEMV_SRC
     return ATTN_KERNEL, ATTN_SRC
 
 
@@ -279,6 +287,131 @@ def _cpu_baseline_prefill(w, min_seconds: float):
     }
 
 
+def _copy_probe(mib: int, dev, sweep):
+    """Time a plain device copy of ``mib`` MiB (five runs, median) after the
+    timed loop: its dispatches calibrate the FETCH_SIZE / WRITE_SIZE
+    counters (--record-traffic)."""
+    if not mib:
+        return None
+    import torch
+    n = mib << 18
+    src = torch.ones(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    ts = []
+    for _ in range(5):
+        sweep()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    t = statistics.median(ts)
+    return {"bytes": 2 * n * 4, "ms": round(t, 4), "GBps": round(2 * n * 4 / (t * 1e-3) / 1e9, 1)}
+
+
+def _bench_gemv(args, dev):
+    """The packed QKV projection: one launch per step, weights read once."""
+    import torch
+
+    import workloads
+    from gqa_attention_kv_amd.runner import DeviceGemv
+
+    g = workloads.make_gemv(args.workload)
+    nbytes = workloads.gemv_bytes(g)
+    run = DeviceGemv(g, device=dev)
+    flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
+                                                          device=dev)
+    flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def sweep():
+        if args.flush == "read":
+            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink)
+        elif args.flush == "rmw":
+            flush.add_(1)
+
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    timer = _HipEvents(2 * args.steps)
+    for _ in range(args.warmup):
+        sweep()
+        run.run()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        sweep()
+        timer.record(2 * i, stream)
+        run.run()
+        timer.record(2 * i + 1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = [timer.ms(2 * i, 2 * i + 1) for i in range(args.steps)]
+    timer.close()
+    mean = statistics.fmean(ms)
+    gbps = nbytes / (mean * 1e-3) / 1e9
+    copy_probe = _copy_probe(args.copy_probe_mib, dev, sweep)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+        from oracle import reference as oracle
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.linear(g.x, g.w)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        cpu = {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": (f"{reps} full projection(s) of the same workload (bf16 widened to "
+                          f"float64, numpy matrix product), {el:.1f} s wall, "
+                          f"{1e6 * el / reps:.0f} us each")}
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean, 5),
+        "us_per_step": round(1e3 * mean, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[args.workload],
+            "M": g.M, "N": g.N, "K": g.K, "out_dtype": g.out_dtype, "path": "gemv",
+            "bytes_per_step": nbytes,
+            "cache_sweep_between_steps": args.flush,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": GEMV_KERNEL,
+            "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBS, 4),
+            "traffic": _traffic(args.workload),
+        },
+        "kernels_us": {
+            "mode": "gemv",
+            "gemv": round(1e3 * mean, 2),
+            "step_p10": round(1e3 * sorted(ms)[len(ms) // 10], 2),
+            "step_p90": round(1e3 * sorted(ms)[(9 * len(ms)) // 10], 2),
+        },
+        "wall_s_timed_loop": round(wall, 4),
+        "output_finite": bool(torch.isfinite(run.y.float()).all().item()),
+        "cpu_baseline": cpu,
+    }
+    if copy_probe:
+        line["copy_probe"] = copy_probe
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = _parse()
     if args.record_traffic:
@@ -299,6 +432,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in GEMV_WORKLOADS:
+        _bench_gemv(args, dev)
+        return
 
     w = workloads.make(args.workload)
     if args.part_tokens:
@@ -365,23 +501,7 @@ def main():
 
     finite = bool(torch.isfinite(step.out.float()).all().item())
 
-    copy_probe = None
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib << 18
-        src = torch.ones(n, dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        ts = []
-        for _ in range(5):
-            sweep()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            dst.copy_(src)
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b))
-        t = statistics.median(ts)
-        copy_probe = {"bytes": 2 * n * 4, "ms": round(t, 4),
-                      "GBps": round(2 * n * 4 / (t * 1e-3) / 1e9, 1)}
+    copy_probe = _copy_probe(args.copy_probe_mib, dev, sweep)
 
     if args.no_cpu_baseline:
         cpu = None

@@ -79,6 +79,7 @@ SYMBOLS = {
                                 _i, _p]),
     "gqa_attn_prefill": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _f, _p, _i, _p, _i, _i, _i, _i,
                               _i, _p]),
+    "gqa_qkv_gemv": (_i, [_p, _i64, _p, _i64, _p, _i, _i64, _i, _i, _i, _p]),
 }
 for _name, (_res, _args) in SYMBOLS.items():
     _fn = getattr(lib, _name)
@@ -405,6 +406,33 @@ def attn_prefill(q, k_cache, v_cache, lens, causal: bool = True, window: int = 0
         _ptr(q), _dtype_code(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(S),
         1 if causal else 0, int(window), float(scale), _ptr(out), _dtype_code(out, "out"),
         _ptr(lse_out), B, Hq, Hkv, D, T, _stream(dev)))
+    return out
+
+
+def qkv_gemv(x, w, out=None, out_dtype=torch.bfloat16):
+    """Packed QKV projection y = x W^T for the decode batch: x [M,K] bf16
+    (M <= 16), w [N,K] bf16 (rows of the projection, K a multiple of 128).
+    Returns y [M,N] (or writes ``out``, which may be a row-strided view)."""
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError("x must be [M,K] and w [N,K]")
+    dev = x.device
+    _dev(w, "w", dev)
+    for t, nm in ((x, "x"), (w, "w")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{nm} must be bfloat16")
+        if t.stride(1) != 1:
+            raise ValueError(f"{nm} rows must be contiguous")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N,K] with the K of x")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    _dev(out, "out", dev)
+    if tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError("out must be [M,N] with contiguous rows")
+    _check(lib.gqa_qkv_gemv(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(out),
+                            _dtype_code(out, "out"), out.stride(0), M, N, K, _stream(dev)))
     return out
 
 

@@ -258,6 +258,28 @@ int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
   return gqa::launch_attn_prefill(a, stream);
 }
 
+int gqa_qkv_gemv(const uint16_t* x, int64_t x_stride, const uint16_t* w, int64_t w_stride,
+                 void* y, gqa_dtype_t y_dtype, int64_t y_stride, int M, int N, int K,
+                 hipStream_t stream) {
+  if (!x || !w || !y) return GQA_ERR_NULL;
+  if (M < 1 || N < 1 || K < 1) return GQA_ERR_SHAPE;
+  if (M > 16 || K % 128 != 0 || !dtype_ok(y_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (x_stride < K || w_stride < K || y_stride < N) return GQA_ERR_SHAPE;
+  if (x_stride % 8 != 0 || w_stride % 8 != 0) return GQA_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, y_dtype == GQA_BF16 ? 2 : 4))
+    return GQA_ERR_ALIGN;
+  // a workgroup addresses its 16 weight rows with 32-bit byte offsets
+  if ((15 * w_stride + K) * 2 > (int64_t)UINT32_MAX) return GQA_ERR_SHAPE;
+  if ((int64_t)N > kMaxWorkgroups * 16 || (int64_t)M * y_stride > kMaxIndex ||
+      (int64_t)N * w_stride > kMaxIndex || (int64_t)M * x_stride > kMaxIndex)
+    return GQA_ERR_SHAPE;
+  gqa::GemvArgs a{};
+  a.x = x; a.x_stride = x_stride; a.w = w; a.w_stride = w_stride;
+  a.y = y; a.y_stride = y_stride; a.out_bf16 = y_dtype == GQA_BF16;
+  a.M = M; a.N = N; a.K = K;
+  return gqa::launch_qkv_gemv(a, stream);
+}
+
 int gqa_num_partitions(int T, int window, int part_tokens) {
   if (T < 1 || part_tokens < 1) return 0;
   return num_parts(T, window, part_tokens);

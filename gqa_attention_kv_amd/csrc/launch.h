@@ -101,6 +101,19 @@ struct PrefillArgs {
   int row_blocks;              // ceil(S * G / prefill_rows_per_block())
 };
 
+// Arguments of the packed QKV projection y[M,N] = x[M,K] W^T, passed by
+// value.  Strides are in elements.
+struct GemvArgs {
+  const uint16_t* x;           // [M, x_stride] bf16
+  int64_t x_stride;
+  const uint16_t* w;           // [N, w_stride] bf16
+  int64_t w_stride;
+  void* y;                     // [M, y_stride] fp32 or bf16
+  int64_t y_stride;
+  int out_bf16;
+  int M, N, K;
+};
+
 int launch_prologue(const PrologueArgs& a, hipStream_t s);
 int launch_attn_final(const KernelArgs& a, hipStream_t s);   // one pass per (seq, KV head)
 int launch_attn_split(const KernelArgs& a, hipStream_t s);   // partition pass
@@ -108,5 +121,6 @@ int launch_decode_step(const KernelArgs& a, hipStream_t s);  // fused whole step
 int launch_merge(const MergeArgs& a, hipStream_t s);
 int prefill_rows_per_block();                                 // (token, head) rows per workgroup
 int launch_attn_prefill(const PrefillArgs& a, hipStream_t s);
+int launch_qkv_gemv(const GemvArgs& a, hipStream_t s);
 
 }  // namespace gqa

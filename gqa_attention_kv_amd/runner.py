@@ -17,6 +17,7 @@ from . import attn_decode, attn_decode_merge, attn_decode_splitk, decode_step, q
 from . import decode_step_ex, qkv_prologue_ex, rope_table
 from . import attn_decode_merge_multi, attn_decode_multi, attn_decode_splitk_multi, attn_prefill
 from . import decode_step_workspace_bytes, splitk_multi_workspace_bytes, splitk_workspace_bytes
+from . import qkv_gemv
 
 BF16_NAN = 0x7FC0
 
@@ -213,3 +214,21 @@ class DeviceStep:
         return dict(out=out, lse=self.lse.cpu().numpy().astype(np.float64),
                     q=self.q.float().cpu().numpy().astype(np.float64),
                     k_cache=bf16_bits(self.k_cache), v_cache=bf16_bits(self.v_cache))
+
+
+class DeviceGemv:
+    """The packed QKV projection of a projection workload with x and W
+    resident in HBM; ``run()`` enqueues y = x W^T on torch's current
+    stream."""
+
+    def __init__(self, g, device="cuda", out_dtype: Optional[str] = None):
+        self.g = g
+        d = torch.device(device)
+        self.x = bf16_tensor(g.x, d)
+        self.w = bf16_tensor(g.w, d)
+        od = out_dtype or g.out_dtype
+        self.y = torch.empty((g.M, g.N), dtype=torch.bfloat16 if od == "bf16" else torch.float32,
+                             device=d)
+
+    def run(self):
+        qkv_gemv(self.x, self.w, out=self.y)

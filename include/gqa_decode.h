@@ -343,6 +343,26 @@ int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
                      void* out, gqa_dtype_t out_dtype, float* lse_out,
                      int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
 
+/*
+ * Packed QKV projection of the decode batch: y[m][n] = sum_k x[m][k] w[n][k]
+ * for m < M, n < N (the projection ahead of the prologue in the cutileGPT
+ * README's runtime list, "packed QKV ... projections"; the weight layout
+ * B[N,K] of the PyGPUkit 0.2.18 page's optimized BF16 GEMV).  With
+ * N = (Hq + 2 Hkv) D, row m of y is q | k_new | v_new of sequence m, and
+ * gqa_qkv_prologue reads it directly with q = y, k_new = y + Hq D,
+ * v_new = y + (Hq + Hkv) D and both batch strides = y_stride.
+ * x [M, x_stride] bf16 and w [N, w_stride] bf16, row-major, 16-byte aligned
+ * with strides a multiple of 8 elements; y [M, y_stride] fp32 or bf16
+ * (round to nearest even).  bf16 products, float32 accumulation in a fixed
+ * order (bit-identical reruns).  1 <= M <= 16 and K a multiple of 128, else
+ * GQA_ERR_UNSUPPORTED; GQA_ERR_SHAPE for strides below the sizes or
+ * 15 * w_stride + K >= 2^31 elements; GQA_ERR_ALIGN for misaligned
+ * pointers or strides.  Nothing is allocated; y must not alias x or w.
+ */
+int gqa_qkv_gemv(const uint16_t* x, int64_t x_stride, const uint16_t* w, int64_t w_stride,
+                 void* y, gqa_dtype_t y_dtype, int64_t y_stride, int M, int N, int K,
+                 hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char* gqa_status_string(int status);
 

@@ -99,3 +99,17 @@ def rope_pairs(x, pos, inv_freq, layout="neox", mscale=1.0):
         y[u] = mscale * (x[u] * c - x[v] * s)
         y[v] = mscale * (x[v] * c + x[u] * s)
     return y
+
+
+def linear(x, w):
+    """Lists x[m][k], w[n][k] -> y[m][n] = sum_k x[m][k] * w[n][k], loops."""
+    y = []
+    for row in x:
+        out = []
+        for wr in w:
+            acc = 0.0
+            for a, b in zip(row, wr):
+                acc += a * b
+            out.append(acc)
+        y.append(out)
+    return y

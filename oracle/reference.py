@@ -36,7 +36,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "bf16_to_f64", "f64_to_bf16", "rmsnorm", "rope_inv_freq", "rope_inv_freq_scaled",
+    "bf16_to_f64", "f64_to_bf16", "linear", "split_qkv", "rmsnorm", "rope_inv_freq", "rope_inv_freq_scaled",
     "rope", "rope_neox", "qkv_prologue", "attend_rows", "attend", "num_partitions",
     "partition_ranges", "attend_partials", "lse_merge", "decode_step",
     "qkv_prologue_multi", "attend_multi",
@@ -51,6 +51,33 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     with np.errstate(invalid="ignore"):
         return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Packed QKV projection (cutileGPT README runtime list: packed QKV
+# projections; PyGPUkit 0.2.18, optimized BF16 GEMV with weights B[N,K])
+# ---------------------------------------------------------------------------
+def linear(x_bits, w_bits) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] w[n, k] in float64, from bf16 bit patterns:
+    x [M,K], w [N,K] (each output's weights are one row).  The product is
+    the library matrix product of the exactly widened values."""
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_bits)
+    if x.shape[-1] != w.shape[-1]:
+        raise ValueError("x and w must share K")
+    return x @ w.T
+
+
+def split_qkv(y: np.ndarray, Hq: int, Hkv: int, D: int):
+    """Views of a packed projection row: q [.., Hq, D], k [.., Hkv, D],
+    v [.., Hkv, D], in that order along the last axis."""
+    lead = y.shape[:-1]
+    if y.shape[-1] != (Hq + 2 * Hkv) * D:
+        raise ValueError("last axis must be (Hq + 2 Hkv) D")
+    q = y[..., :Hq * D].reshape(lead + (Hq, D))
+    k = y[..., Hq * D:(Hq + Hkv) * D].reshape(lead + (Hkv, D))
+    v = y[..., (Hq + Hkv) * D:].reshape(lead + (Hkv, D))
+    return q, k, v
 
 
 def f64_to_bf16(x: np.ndarray) -> np.ndarray:

@@ -655,6 +655,50 @@ def pin_prefill_equal_keys_closed_form(O):
             assert abs(lseb[0, s, h] - (sc + math.log(S))) < 1e-12
 
 
+def pin_linear_matches_bruteforce(O):
+    """The projection against scalar loops, on values whose sums are exact in
+    float64 (so any dropped or misplaced term shows)."""
+    rng = _rng(80)
+    M, N, K = 3, 5, 8
+    xb, wb = _bits(rng, (M, K)), _bits(rng, (N, K))
+    y = O.linear(xb, wb)
+    ref = BF.linear(_torch_bf16_to_f64(xb).tolist(), _torch_bf16_to_f64(wb).tolist())
+    _close(y, np.array(ref), 1e-12, "linear")
+    assert y.shape == (M, N)
+
+
+def pin_linear_identity_and_onehot(O):
+    """Identity weights return x; a cyclic-shift permutation returns
+    y[m][n] = x[m][(n+1) mod K] (its transpose would shift the other way); a
+    one-hot weight row picks one column of x; powers of two add exactly."""
+    rng = _rng(81)
+    K = 6
+    xb = _bits(rng, (2, K))
+    eye = np.zeros((K, K), np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80          # bf16 1.0
+    assert np.array_equal(O.linear(xb, eye), _torch_bf16_to_f64(xb))
+    shift = np.zeros((K, K), np.uint16)
+    shift[np.arange(K), (np.arange(K) + 1) % K] = 0x3F80
+    assert np.array_equal(O.linear(xb, shift), np.roll(_torch_bf16_to_f64(xb), -1, axis=1))
+    w = np.zeros((1, K), np.uint16)
+    w[0, 4] = 0x4000                                  # 2.0
+    assert np.array_equal(O.linear(xb, w)[:, 0], 2.0 * _torch_bf16_to_f64(xb)[:, 4])
+    xs = np.array([[0x3F80, 0x3F00, 0x3E80, 0x3E00, 0, 0]], np.uint16)   # 1, 1/2, 1/4, 1/8
+    ws = np.array([[0x3F80, 0x3F80, 0, 0x3F80, 0x3F80, 0x3F80]], np.uint16)
+    assert O.linear(xs, ws)[0, 0] == 1.0 + 0.5 + 0.125
+
+
+def pin_split_qkv_layout(O):
+    """q | k | v along the packed row, each head's D values contiguous."""
+    Hq, Hkv, D = 4, 2, 3
+    y = np.arange(2 * (Hq + 2 * Hkv) * D, dtype=np.float64).reshape(2, -1)
+    q, k, v = O.split_qkv(y, Hq, Hkv, D)
+    assert q.shape == (2, Hq, D) and k.shape == (2, Hkv, D) and v.shape == (2, Hkv, D)
+    assert q[1, 3, 2] == y[1, 3 * D + 2]
+    assert k[0, 1, 0] == y[0, Hq * D + D]
+    assert v[1, 0, 1] == y[1, (Hq + Hkv) * D + 1]
+
+
 def pin_prologue_multi_matches_bruteforce(O):
     """S new tokens: token s normalised and rotated at pos + s, its K/V row
     appended at row pos + s, every other row untouched."""

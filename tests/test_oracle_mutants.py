@@ -339,6 +339,23 @@ def _multi_bidirectional_first_token_rows(q, k_cache, v_cache, lens, window=0, s
                                  window, scale, causal=False)
 
 
+def _linear_transposed_w(x_bits, w_bits):
+    x, w = R.bf16_to_f64(x_bits), R.bf16_to_f64(w_bits)
+    if w.shape[0] == w.shape[1]:
+        return x @ w
+    return x @ w.T
+
+
+def _linear_drops_last_column(x_bits, w_bits):
+    x, w = R.bf16_to_f64(x_bits), R.bf16_to_f64(w_bits)
+    return x[:, :-1] @ w[:, :-1].T
+
+
+def _split_qkv_k_v_swapped(y, Hq, Hkv, D):
+    q, k, v = _orig["split_qkv"](y, Hq, Hkv, D)
+    return q, v, k
+
+
 MUTANTS = {
     "bf16_truncate": {"f64_to_bf16": _bf16_truncate},
     "bf16_double_round": {"f64_to_bf16": _bf16_double_round},
@@ -382,6 +399,9 @@ MUTANTS = {
     "multi_window_from_last_token": {"attend_multi": _multi_window_from_last},
     "multi_prologue_last_token_position": {"qkv_prologue_multi": _prologue_multi_same_pos},
     "prefill_causal_flag_ignored": {"attend_multi": _multi_causal_flag_ignored},
+    "linear_transposed_weights": {"linear": _linear_transposed_w},
+    "linear_drops_a_column": {"linear": _linear_drops_last_column},
+    "split_qkv_k_v_swapped": {"split_qkv": _split_qkv_k_v_swapped},
     "prefill_bidirectional_first_token_rows": {"attend_multi": _multi_bidirectional_first_token_rows},
 }
 

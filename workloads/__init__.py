@@ -293,3 +293,58 @@ def make(name: str, seed: Optional[int] = None, **over) -> Workload:
         w_q=w_q, w_k=w_k, peaky_rows=peaky_rows,
         rope_layout=p.get("rope_layout", "neox"), rope_scaling=p.get("rope_scaling"), S=S,
         causal=bool(p.get("causal", True)))
+
+
+# ---------------------------------------------------------------------------
+# Packed QKV projection (the step ahead of the prologue)
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class GemvWorkload:
+    """y = x W^T for the decode batch: x [M,K] and W [N,K] bf16 bit patterns,
+    N = (Hq + 2 Hkv) D, so row m of y is q | k_new | v_new of sequence m."""
+
+    name: str
+    seed: int
+    M: int
+    N: int
+    K: int
+    Hq: int
+    Hkv: int
+    D: int
+    x: np.ndarray                    # uint16 [M,K]
+    w: np.ndarray                    # uint16 [N,K]
+    out_dtype: str                   # "f32" | "bf16"
+
+
+def gemv_bytes(g: GemvWorkload) -> int:
+    """HBM bytes one projection moves: the weights, x and y."""
+    ob = 2 if g.out_dtype == "bf16" else 4
+    return g.N * g.K * 2 + g.M * g.K * 2 + g.M * g.N * ob
+
+
+GEMV_CONFIGS: Dict[str, dict] = {
+    # the 70B-shaped decode batch of config 5: hidden 8192, Hq 64, Hkv 8, D 128
+    "8": dict(seed=9, M=8, K=8192, Hq=64, Hkv=8, D=128, out_dtype="bf16"),
+    # the shapes of the PyGPUkit BF16 GEMV table (one row of x): K=2048,
+    # N=8192 and K=4096, N=14336 (written as Hq D with Hkv = 0)
+    "8a": dict(seed=10, M=1, K=2048, Hq=64, Hkv=0, D=128, out_dtype="bf16"),
+    "8b": dict(seed=11, M=1, K=4096, Hq=112, Hkv=0, D=128, out_dtype="bf16"),
+}
+
+
+def make_gemv(name: str, seed: Optional[int] = None, **over) -> GemvWorkload:
+    """x ~ N(0,1) and W ~ N(0,1) 2^-e (e = ceil(log2 sqrt K), an exact bf16
+    scaling, so outputs are O(1)), both rounded to bf16 (nearest even)."""
+    p = dict(GEMV_CONFIGS[name])
+    p.update(over)
+    seed = p["seed"] if seed is None else seed
+    M, K, Hq, Hkv, D = p["M"], p["K"], p["Hq"], p["Hkv"], p["D"]
+    N = p.get("N", (Hq + 2 * Hkv) * D)
+    rng = np.random.default_rng(seed)
+    x = _normal_bf16(rng, (M, K))
+    w = _cache_bf16(seed, 3, (N, K))
+    e = int(np.ceil(np.log2(np.sqrt(K))))
+    wf = (w.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** -e)
+    w = (wf.view(np.uint32) >> 16).astype(np.uint16)
+    return GemvWorkload(name=name, seed=seed, M=M, N=N, K=K, Hq=Hq, Hkv=Hkv, D=D, x=x, w=w,
+                        out_dtype=p["out_dtype"])
