@@ -77,6 +77,9 @@ def _parse():
                     help="cache sweep between steps: read a 1 GiB buffer (default), "
                          "read-modify-write it, or none (warm-cache figure)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the warm-cache figure (its extra launches would otherwise "
+                         "appear in a kernel trace of this run)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent timing the oracle")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -242,6 +245,7 @@ def _cpu_baseline(w, min_seconds: float):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": _cpu_model(),
         "sample": (f"{reps} full decode step(s) of the same workload (prologue + unsplit "
                    f"attention, float64 numpy), {el:.1f} s wall, "
                    f"{1e6 * el / reps:.0f} us/step"),
@@ -280,11 +284,41 @@ def _cpu_baseline_prefill(w, min_seconds: float):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": _cpu_model(),
         "sample": (f"{toks} of the step's {w.S} query tokens (all {w.B} sequences and "
                    f"{w.Hq} heads each; float64 numpy attention), {el:.1f} s wall, "
                    f"scaled by attended rows to {est_step:.1f} s per step; the prologue "
                    f"is not timed"),
     }
+
+
+def _context(dev, flush, sweep, run_once, warm_steps: int = 20):
+    """A context figure outside the K timed steps: the step with warm caches
+    (no sweep in between; the mean of ``warm_steps`` runs, HIP events)."""
+    import torch
+    ev = _HipEvents(2 * warm_steps)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    run_once()
+    torch.cuda.synchronize()
+    for i in range(warm_steps):
+        ev.record(2 * i, stream)
+        run_once()
+        ev.record(2 * i + 1, stream)
+    torch.cuda.synchronize()
+    warm = statistics.fmean(ev.ms(2 * i, 2 * i + 1) for i in range(warm_steps))
+    ev.close()
+    return {"warm_us_per_step": round(1e3 * warm, 2)}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _copy_probe(mib: int, dev, sweep):
@@ -348,6 +382,7 @@ def _bench_gemv(args, dev):
     timer.close()
     mean = statistics.fmean(ms)
     gbps = nbytes / (mean * 1e-3) / 1e9
+    context = None if args.no_context else _context(dev, flush, sweep, run.run)
     copy_probe = _copy_probe(args.copy_probe_mib, dev, sweep)
     cpu = None
     if not args.no_cpu_baseline:
@@ -363,7 +398,7 @@ def _bench_gemv(args, dev):
             if el >= args.cpu_seconds:
                 break
         cpu = {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": _cpu_model(),
                "sample": (f"{reps} full projection(s) of the same workload (bf16 widened to "
                           f"float64, numpy matrix product), {el:.1f} s wall, "
                           f"{1e6 * el / reps:.0f} us each")}
@@ -400,9 +435,11 @@ def _bench_gemv(args, dev):
         "kernels_us": {
             "mode": "gemv",
             "gemv": round(1e3 * mean, 2),
+            "step_median": round(1e3 * statistics.median(ms), 2),
             "step_p10": round(1e3 * sorted(ms)[len(ms) // 10], 2),
             "step_p90": round(1e3 * sorted(ms)[(9 * len(ms)) // 10], 2),
         },
+        "context": context,
         "wall_s_timed_loop": round(wall, 4),
         "output_finite": bool(torch.isfinite(run.y.float()).all().item()),
         "cpu_baseline": cpu,
@@ -496,6 +533,15 @@ def main():
     timer.close()
     mean_step = statistics.fmean(step_ms)
     mean_attn = statistics.fmean(attn_ms)
+
+    def run_once():
+        if mode == "fused":
+            step.fused()
+        else:
+            step.prologue()
+            step.attention()
+            step.merge()
+    context = None if args.no_context else _context(dev, flush, sweep, run_once)
     value = kvb / (mean_step * 1e-3) / 1e9
     achieved = kvb / (mean_attn * 1e-3) / 1e9
 
@@ -567,9 +613,11 @@ def main():
             "prologue": round(1e3 * statistics.fmean(pro_ms), 2),
             "attn": round(1e3 * mean_attn, 2),
             "merge": round(1e3 * statistics.fmean(merge_ms), 2),
+            "step_median": round(1e3 * statistics.median(step_ms), 2),
             "step_p10": round(1e3 * sorted(step_ms)[len(step_ms) // 10], 2),
             "step_p90": round(1e3 * sorted(step_ms)[(9 * len(step_ms)) // 10], 2),
         },
+        "context": context,
         "wall_s_timed_loop": round(wall, 4),
         "output_finite": finite,
         "cpu_baseline": cpu,
