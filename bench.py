@@ -292,7 +292,7 @@ def _cpu_baseline_prefill(w, min_seconds: float):
     }
 
 
-def _context(dev, flush, sweep, run_once, warm_steps: int = 20):
+def _context(dev, run_once, warm_steps: int = 20):
     """A context figure outside the K timed steps: the step with warm caches
     (no sweep in between; the mean of ``warm_steps`` runs, HIP events)."""
     import torch
@@ -382,7 +382,7 @@ def _bench_gemv(args, dev):
     timer.close()
     mean = statistics.fmean(ms)
     gbps = nbytes / (mean * 1e-3) / 1e9
-    context = None if args.no_context else _context(dev, flush, sweep, run.run)
+    context = None if args.no_context else _context(dev, run.run)
     copy_probe = _copy_probe(args.copy_probe_mib, dev, sweep)
     cpu = None
     if not args.no_cpu_baseline:
@@ -541,7 +541,7 @@ def main():
             step.prologue()
             step.attention()
             step.merge()
-    context = None if args.no_context else _context(dev, flush, sweep, run_once)
+    context = None if args.no_context else _context(dev, run_once)
     value = kvb / (mean_step * 1e-3) / 1e9
     achieved = kvb / (mean_attn * 1e-3) / 1e9
 
