@@ -90,6 +90,48 @@ def test_gpu_prefill(name, over, what):
         check_prologue_multi(w, got, ref, f"prefill {name} {over}")
 
 
+# bf16 q (given directly) and a bf16 output at D = 128, the chunked-prefill
+# configuration: every group size, windows, bidirectional, ragged blocks
+BF16_PATH = [
+    dict(B=2, L=700, S=300),                          # ragged 256-row block (1200 rows)
+    dict(B=2, L=500, S=64, Hq=16, Hkv=2),             # G=8
+    dict(B=2, L=400, S=200, Hq=8, Hkv=8),             # G=1
+    dict(B=1, L=300, S=40, Hq=16, Hkv=1),             # G=16: 640 rows
+    dict(B=2, L=900, S=100, Hq=8, Hkv=4),             # G=2
+    dict(B=3, L=2000, S=256, window=300),             # window per token
+    dict(B=2, L=600, S=96, window=128, causal=False),  # window, bidirectional
+    dict(B=2, L=512, S=512, causal=False),            # fresh-length bidirectional
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("over", BF16_PATH, ids=[f"b{i}" for i in range(len(BF16_PATH))])
+def test_gpu_prefill_bf16_path(over):
+    _gpu()
+    from test_gpu_parity import check_attention
+    w = W.make("7", **over)
+    print(f"\n[case] prefill bf16 path {over}", flush=True)
+    ref = O.decode_step(w)
+    got = _step(w)
+    check_attention(got, ref, w.out_dtype, f"prefill bf16 path {over}")
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_bf16_poisoned_ragged():
+    """bf16 q and output with ragged lengths, a window and NaN outside every
+    token's rows."""
+    _gpu()
+    from test_gpu_parity import check_attention
+    w = W.make("7", B=3, L=1500, S=200, window=400)
+    rng = np.random.default_rng(5)
+    w.lens[:] = rng.integers(150, 1500, size=3).astype(np.int32)
+    w.lens[1] = 120                                    # first tokens see no row
+    print(f"\n[case] prefill bf16 poisoned lens={w.lens.tolist()}", flush=True)
+    ref = O.decode_step(w)
+    got = _step(w, poison=True)
+    check_attention(got, ref, w.out_dtype, "prefill bf16 poisoned")
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("causal", [True, False])
 def test_gpu_prefill_poisoned_rows(causal):
