@@ -159,9 +159,7 @@ struct TileBuf {
 // Register budget: three waves per SIMD (168 VGPRs); G = 16 keeps two q
 // operands (hi and lo) live and gets two waves (256 VGPRs) so that nothing
 // spills to scratch inside the tile loop.
-#ifndef GQA_WAVES_PER_EU
-#define GQA_WAVES_PER_EU 3
-#endif
+constexpr int kWavesPerEU = 3;
 
 // The last workgroup of a (sequence, KV head) team merges the team's
 // partitions (one per member): M = max_k lse_k, w_k = e^(lse_k - M),
@@ -304,7 +302,7 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
 // MT: several tokens (S > 1), whose columns attend different row ranges;
 // the single-token instances keep the plainer inner loop.
 template <int D, int CT, int NW, typename IT, Mode MODE, bool MT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CT >= 16 ? 2 : GQA_WAVES_PER_EU))) void
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CT >= 16 ? 2 : kWavesPerEU))) void
 attn_decode_mfma_kernel(const KernelArgs a) {
   static_assert(CT <= 16, "one 16-column MFMA tile holds at most 16 query rows");
   constexpr int KC = D / 32;          // QK calls per tile (per q part)
@@ -909,13 +907,12 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   }
 }
 
-#ifndef GQA_MFMA_NW
-#define GQA_MFMA_NW 4
-#endif
+// Waves per workgroup: four, one per SIMD of the CU.
+constexpr int kWavesPerGroup = 4;
 
 template <int D, int CT, typename IT, Mode MODE>
 static int launch_mode(const KernelArgs& a, hipStream_t s) {
-  constexpr int NW = GQA_MFMA_NW;
+  constexpr int NW = kWavesPerGroup;
   const dim3 grid((MODE == Mode::Final ? 1 : a.num_parts) * a.B * a.Hkv);
   if (MODE != Mode::Step && a.S > 1)
     hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, IT, MODE, MODE != Mode::Step>), grid,
