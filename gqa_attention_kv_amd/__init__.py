@@ -10,8 +10,9 @@ Functions follow the C entry points' names without the ``gqa_`` prefix:
 ``qkv_prologue``, ``qkv_prologue_ex``, ``attn_decode``,
 ``attn_decode_splitk``, ``attn_decode_merge``, ``attn_decode_multi``,
 ``attn_decode_splitk_multi``, ``attn_decode_merge_multi``, ``decode_step``,
-``decode_step_ex``, ``rope_table``, ``splitk_workspace_bytes``,
-``splitk_multi_workspace_bytes``, ``decode_step_workspace_bytes``,
+``decode_step_ex``, ``decode_step_multi``, ``attn_prefill``, ``qkv_gemv``,
+``rope_table``, ``splitk_workspace_bytes``, ``splitk_multi_workspace_bytes``,
+``decode_step_workspace_bytes``, ``decode_step_multi_workspace_bytes``,
 ``num_partitions``.
 """
 from __future__ import annotations
@@ -29,7 +30,8 @@ __all__ = [
     "attn_decode_splitk", "attn_decode_merge", "splitk_workspace_bytes", "num_partitions",
     "decode_step", "decode_step_ex", "decode_step_workspace_bytes", "rope_table",
     "attn_decode_multi", "attn_decode_splitk_multi", "attn_decode_merge_multi",
-    "splitk_multi_workspace_bytes",
+    "splitk_multi_workspace_bytes", "decode_step_multi", "decode_step_multi_workspace_bytes",
+    "attn_prefill", "qkv_gemv",
     "F32", "BF16", "SYMBOLS", "ROPE_NEOX", "ROPE_INTERLEAVED", "ROPE_KINDS",
 ]
 
@@ -77,6 +79,10 @@ SYMBOLS = {
     "gqa_decode_step_ex": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _p,
                                 _p, _p, _i, _f, _i, _p, _sz, _p, _i, _p, _p, _i, _i, _i, _i,
                                 _i, _p]),
+    "gqa_decode_step_multi_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "gqa_decode_step_multi": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _i,
+                                   _p, _p, _p, _i, _f, _i, _p, _sz, _p, _i, _p, _p, _i, _i,
+                                   _i, _i, _i, _p]),
     "gqa_attn_prefill": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _f, _p, _i, _p, _i, _i, _i, _i,
                               _i, _p]),
     "gqa_qkv_gemv": (_i, [_p, _i64, _p, _i64, _p, _i, _i64, _i, _i, _i, _p]),
@@ -528,15 +534,55 @@ def decode_step_ex(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens: in
     return out, workspace
 
 
+def decode_step_multi_workspace_bytes(B: int, S: int, Hq: int, Hkv: int, D: int, T: int,
+                                      window: int, part_tokens: int) -> int:
+    return int(lib.gqa_decode_step_multi_workspace_bytes(B, S, Hq, Hkv, D, T, window,
+                                                         part_tokens))
+
+
+def decode_step_multi(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens: int,
+                      workspace=None, inv_freq=None, rope_mscale: float = 1.0,
+                      rope_layout="neox", q_norm_w=None, k_norm_w=None, eps: float = 1e-6,
+                      window: int = 0, scale: float = 0.0, out=None, out_dtype=torch.float32,
+                      lse_out=None, q_out=None):
+    """The whole multi-token step in one launch: q [B,S,Hq,D], k_new and
+    v_new [B,S,Hkv,D] (tokens and heads dense; a batch stride of their own),
+    token s rotated at pos[b] + s and appended at row pos[b] + s, then the
+    attention of ``attn_decode_multi``.  ``inv_freq``: host float64 [D/2]
+    rotary table or None.  Returns ``(out [B,S,Hq,D], workspace)``; the
+    workspace's tickets start at zero (allocated zeroed when None)."""
+    a = _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, workspace,
+                     q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out, multi=True)
+    dev, B, S, Hq, Hkv, D, T, code, workspace, out, nbytes, pro = a
+    f = _host_table(inv_freq, D)
+    _check(lib.gqa_decode_step_multi(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0),
+        k_new.stride(0) if pro else S * Hkv * D,
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), None if f is None else f.ctypes.data,
+        float(rope_mscale), _layout_code(rope_layout), _ptr(pos), S,
+        _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(window), float(scale), int(part_tokens),
+        _ptr(workspace), nbytes, _ptr(out), _dtype_code(out, "out"), _ptr(lse_out),
+        _ptr(q_out), B, Hq, Hkv, D, T, _stream(dev)))
+    return out, workspace
+
+
 def _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, workspace,
-                 q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out):
+                 q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out, multi=False):
+    """Checks of the one-launch step.  ``multi``: q, k_new, v_new, out and
+    q_out carry a token axis ([B,S,H,D], tokens and heads dense)."""
     dev = k_cache.device
     pro = pos is not None
     if (k_new is None) == pro or (v_new is None) == pro:
         raise ValueError("pos, k_new and v_new come together (or all None: no prologue)")
     for t, w in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (lens, "lens")):
         _dev(t, w, dev)
-    B, Hq, D = q.shape
+    if multi:
+        if q.dim() != 4:
+            raise ValueError("q: expected [B,S,Hq,D]")
+        B, S, Hq, D = q.shape
+    else:
+        B, Hq, D = q.shape
+        S = 1
     _, Hkv, T, _ = k_cache.shape
     code = _dtype_code(q, "q")
     news = ((k_new, "k_new", Hkv), (v_new, "v_new", Hkv)) if pro else ()
@@ -544,7 +590,11 @@ def _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, work
         _dev(t, w, dev)
         if t.dtype != q.dtype:
             raise TypeError("q, k_new and v_new must share a dtype")
-        if tuple(t.shape) != (B, h, D) or t.stride(2) != 1 or t.stride(1) != D:
+        if multi:
+            if (tuple(t.shape) != (B, S, h, D) or t.stride(3) != 1 or t.stride(2) != D
+                    or t.stride(1) != h * D):
+                raise ValueError(f"{w}: expected [B,S,{h},D] with contiguous tokens and heads")
+        elif tuple(t.shape) != (B, h, D) or t.stride(2) != 1 or t.stride(1) != D:
             raise ValueError(f"{w}: expected [B,{h},D] with contiguous heads")
     if pro and k_new.stride(0) != v_new.stride(0):
         raise ValueError("k_new and v_new must share a batch stride")
@@ -565,20 +615,33 @@ def _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, work
             if w.dtype != torch.float32 or tuple(w.shape) != (D,):
                 raise ValueError(f"{nm} must be float32 [D]")
             _contig(w, nm)
-    need = decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens)
+    need = (decode_step_multi_workspace_bytes(B, S, Hq, Hkv, D, T, window, part_tokens) if multi
+            else decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens))
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
     _dev(workspace, "workspace", dev)
     _contig(workspace, "workspace")
+    rows = (B, S, Hq) if multi else (B, Hq)
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=out_dtype, device=dev)
+        out = torch.empty(rows + (D,), dtype=out_dtype, device=dev)
     _dev(out, "out", dev)
     _contig(out, "out")
-    _lse_check(lse_out, B, Hq, dev)
+    if multi:
+        if tuple(out.shape) != rows + (D,):
+            raise ValueError("out: expected [B,S,Hq,D]")
+        if lse_out is not None:
+            _dev(lse_out, "lse_out", dev)
+            _contig(lse_out, "lse_out")
+            if lse_out.dtype != torch.float32 or tuple(lse_out.shape) != rows:
+                raise ValueError("lse_out must be float32 [B,S,Hq]")
+    else:
+        _lse_check(lse_out, B, Hq, dev)
     if q_out is not None:
         _dev(q_out, "q_out", dev)
         _contig(q_out, "q_out")
-        if q_out.dtype != torch.float32 or tuple(q_out.shape) != (B, Hq, D):
-            raise ValueError("q_out must be float32 [B,Hq,D]")
+        if q_out.dtype != torch.float32 or tuple(q_out.shape) != rows + (D,):
+            raise ValueError(f"q_out must be float32 {list(rows + (D,))}")
     nbytes = workspace.numel() * workspace.element_size()
+    if multi:
+        return dev, B, S, Hq, Hkv, D, T, code, workspace, out, nbytes, pro
     return dev, B, Hq, Hkv, D, T, code, workspace, out, nbytes, pro

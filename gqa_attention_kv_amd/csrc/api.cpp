@@ -375,7 +375,12 @@ int gqa_attn_decode_merge_multi(const void* workspace, size_t workspace_bytes, i
 
 size_t gqa_decode_step_workspace_bytes(int B, int Hq, int Hkv, int D, int T, int window,
                                        int part_tokens) {
-  const size_t base = gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens);
+  return gqa_decode_step_multi_workspace_bytes(B, 1, Hq, Hkv, D, T, window, part_tokens);
+}
+
+size_t gqa_decode_step_multi_workspace_bytes(int B, int S, int Hq, int Hkv, int D, int T,
+                                             int window, int part_tokens) {
+  const size_t base = gqa_splitk_multi_workspace_bytes(B, S, Hq, D, T, window, part_tokens);
   if (base == 0 || Hkv < 1) return 0;
   return align256(base) + (size_t)B * Hkv * sizeof(uint32_t);
 }
@@ -390,6 +395,23 @@ int gqa_decode_step_ex(const void* q, const void* k_new, const void* v_new,
                        void* workspace, size_t workspace_bytes,
                        void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
                        int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  return gqa_decode_step_multi(q, k_new, v_new, in_dtype, q_bstride, kv_bstride, q_norm_w,
+                               k_norm_w, eps, inv_freq, rope_mscale, rope_layout, pos, 1,
+                               k_cache, v_cache, lens, window, scale, part_tokens, workspace,
+                               workspace_bytes, out, out_dtype, lse_out, q_out, B, Hq, Hkv, D,
+                               T, stream);
+}
+
+int gqa_decode_step_multi(const void* q, const void* k_new, const void* v_new,
+                          gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                          const float* q_norm_w, const float* k_norm_w, float eps,
+                          const double* inv_freq, double rope_mscale, int rope_layout,
+                          const int32_t* pos, int S,
+                          uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                          int window, float scale, int part_tokens,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                          int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !lens || !workspace || !out) return GQA_ERR_NULL;
   // the prologue inputs come all together or not at all
   const bool pro = pos != nullptr;
@@ -399,9 +421,10 @@ int gqa_decode_step_ex(const void* q, const void* k_new, const void* v_new,
     return GQA_ERR_NULL;
   int rc = check_shapes(B, Hq, Hkv, D, T);
   if (rc) return rc;
-  if ((rc = check_split(B, Hkv, T, window, part_tokens))) return rc;
+  if ((rc = check_tokens(S, B, Hq, Hkv))) return rc;
+  if ((rc = check_split(B, Hkv, T, window, part_tokens, S))) return rc;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
-  if (q_bstride < (int64_t)Hq * D || kv_bstride < (int64_t)Hkv * D) return GQA_ERR_SHAPE;
+  if (q_bstride < (int64_t)S * Hq * D || kv_bstride < (int64_t)S * Hkv * D) return GQA_ERR_SHAPE;
   if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
   if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
   if ((rc = check_rope(inv_freq, rope_mscale, rope_layout, D))) return rc;
@@ -414,23 +437,25 @@ int gqa_decode_step_ex(const void* q, const void* k_new, const void* v_new,
       !aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse_out, 4) ||
       !aligned(q_out, 16))
     return GQA_ERR_ALIGN;
-  if (workspace_bytes < gqa_decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens))
+  if (workspace_bytes <
+      gqa_decode_step_multi_workspace_bytes(B, S, Hq, Hkv, D, T, window, part_tokens))
     return GQA_ERR_WORKSPACE;
-  const int np = gqa_num_partitions(T, window, part_tokens);
-  // the merge reads one (sequence, KV head)'s partials with 32-bit offsets
-  if ((int64_t)(Hq / Hkv) * np * D * 4 >= (INT64_C(1) << 31)) return GQA_ERR_SHAPE;
+  const int np = num_parts(T, window, part_tokens, S);
+  // the merge reads one (sequence, KV head)'s partials -- rows of S tokens,
+  // Hq apart -- with 32-bit offsets
+  const int64_t team_rows = (int64_t)(S - 1) * Hq + Hq / Hkv;
+  if (team_rows * np * D * 4 >= (INT64_C(1) << 31)) return GQA_ERR_SHAPE;
   gqa::KernelArgs a{};
   a.q = q; a.q_bstride = q_bstride; a.in_bf16 = in_dtype == GQA_BF16;
+  a.S = S; a.q_sstride = (int64_t)Hq * D;
   a.k_cache = k_cache; a.v_cache = v_cache; a.k_cache_w = k_cache; a.v_cache_w = v_cache;
   a.lens = lens; a.window = window; a.qscale = softmax_qscale(scale, D);
   a.part_tokens = part_tokens; a.num_parts = np;
   char* ws = static_cast<char*>(workspace);
-  const size_t lse_sz = align256(lse_bytes((size_t)B * Hq, np));
   a.ws_lse = reinterpret_cast<float*>(ws);
-  a.ws_o = reinterpret_cast<float*>(ws + lse_sz);
-  a.S = 1; a.q_sstride = (int64_t)Hq * D;
+  a.ws_o = reinterpret_cast<float*>(ws + align256(lse_bytes((size_t)B * S * Hq, np)));
   a.ws_cnt = reinterpret_cast<uint32_t*>(
-      ws + align256(gqa_splitk_workspace_bytes(B, Hq, D, T, window, part_tokens)));
+      ws + align256(gqa_splitk_multi_workspace_bytes(B, S, Hq, D, T, window, part_tokens)));
   a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   a.k_new = k_new; a.v_new = v_new; a.kv_bstride = kv_bstride;

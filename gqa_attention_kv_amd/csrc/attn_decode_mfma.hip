@@ -140,6 +140,29 @@ __device__ __forceinline__ float load1f<uint16_t>(const uint16_t* p, int64_t i) 
   return bf16_to_f32(p[i]);
 }
 
+// Eight q elements as loaded (raw) and their float32 values (unpack), so
+// that the conversion of a bf16 q can be placed after later loads are issued.
+template <typename T>
+struct QRaw;
+template <>
+struct QRaw<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void unpack(float f[8]) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+};
+template <>
+struct QRaw<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void unpack(float f[8]) const { unpack8(v, f); }
+};
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
 
@@ -172,10 +195,14 @@ constexpr int kWavesPerEU = 3;
 // which do not hit stale L2 lines; a batch of up to MB partitions is one
 // memory round trip.  The team's slice of o is below 2 GiB (checked on the
 // host), so 32-bit buffer offsets reach all of it.
-template <int D, int G, int NW>
-__device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head0) {
+// Column h of the team is output row head0 + rel(h): rel(h) = h with one
+// token (CT = G columns); with several tokens (MT) column h is token h / G,
+// head h % G, so rel(h) = (h / G) Hq + h % G, and columns h >= nc are padding.
+template <int D, int CT, int NW, bool MT>
+__device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head0, int G,
+                                               int nc) {
   constexpr int NTH = NW * 64;
-  constexpr int NG = G * D / 4;                 // float4 output groups
+  constexpr int NG = CT * D / 4;                // float4 output groups
   constexpr int GPT = NG > NTH ? NG / NTH : 1;  // groups per thread
   constexpr int TPS = NG < NTH ? NG : NTH;      // threads per partition subset
   constexpr int KS = NTH / TPS;                 // partition subsets
@@ -184,8 +211,13 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
   const int num_parts = a.num_parts;
   const int t = threadIdx.x;
   const int s = t / TPS;
+  auto rel = [&](int h) -> int64_t {
+    if constexpr (MT) return (int64_t)(h / G) * a.Hq + h % G;
+    return h;
+  };
+  const int64_t span = MT ? rel(nc - 1) + 1 : CT;   // rows from head0 to the last column's
   const __amdgpu_buffer_rsrc_t Ors =
-      make_rsrc(a.ws_o + head0 * num_parts * D, (uint32_t)((size_t)G * num_parts * D * 4));
+      make_rsrc(a.ws_o + head0 * num_parts * D, (uint32_t)((size_t)span * num_parts * D * 4));
   float Mx[GPT], Wx[GPT];
   float Ax[GPT][4];
 #pragma unroll
@@ -203,15 +235,17 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
       const int gi = t % TPS + j * TPS;
       const int h = gi / (D / 4);
       const int d4 = gi % (D / 4);
-      const float* Lh = a.ws_lse + (head0 + h) * num_parts;
+      const bool col = !MT || h < nc;
+      const int64_t rh = rel(col ? h : 0);
+      const float* Lh = a.ws_lse + (head0 + rh) * num_parts;
 #pragma unroll
       for (int k = 0; k < MB; ++k) {
         const int kk = k0 + k * KS;
         lk[j][k] = -INFINITY;
         ov[j][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (kk < num_parts) {
+        if (kk < num_parts && col) {
           lk[j][k] = __hip_atomic_load(Lh + kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint32_t off = (uint32_t)((((int64_t)h * num_parts + kk) * D + 4 * d4) * 4);
+          const uint32_t off = (uint32_t)(((rh * num_parts + kk) * D + 4 * d4) * 4);
           ov[j][k] = __builtin_amdgcn_raw_buffer_load_b128(Ors, off, 0, kCoherent);
         }
       }
@@ -278,11 +312,12 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
     const int gi = t % TPS + j * TPS;
     const int h = gi / (D / 4);
     const int d4 = gi % (D / 4);
+    if (MT && h >= nc) continue;
     const bool any = Wx[j] > 0.0f;
     float ov[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) ov[e] = any ? Ax[j][e] / Wx[j] : 0.0f;
-    const int64_t oi = (head0 + h) * D + 4 * d4;
+    const int64_t oi = (head0 + rel(h)) * D + 4 * d4;
     if (a.out_bf16) {
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
           make_uint2(pack2(f32_to_bf16(ov[0]), f32_to_bf16(ov[1])),
@@ -292,7 +327,7 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
           make_float4(ov[0], ov[1], ov[2], ov[3]);
     }
     if (d4 == 0 && a.lse_out != nullptr)
-      a.lse_out[head0 + h] = any ? Mx[j] + logf(Wx[j]) : -INFINITY;
+      a.lse_out[head0 + rel(h)] = any ? Mx[j] + logf(Wx[j]) : -INFINITY;
   }
 }
 
@@ -472,25 +507,27 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   // into the one tile that holds row psub.
   __shared__ u32x4_t snew[NW][2][PPR];
   int psub = -1;
+  // Step with several tokens: the new rows [sub_lo, sub_hi) this workgroup
+  // attends, token s's row at sub_k[s] (shared by the waves), and token s's
+  // rotary angles at ang[s] (cos of pair i at i, sin at D/2 + i).
+  __shared__ u32x4_t sub_k[MT ? CT : 1][2][PPR];
+  __shared__ float ang[MT ? CT : 1][D];
+  int sub_lo = -1, sub_hi = -1, p_new = 0;
 
   if constexpr (MODE == Mode::Step) {
     // ---- fused prologue: QK-RMSNorm, NeoX RoPE at pos[b], K/V append ----
     // (skipped when no prologue inputs are given: q is then used as is)
     const bool has_pro = a.pos != nullptr;
     const int p = has_pro ? a.pos[b] : -1;
-    // Partition 0 writes row pos[b] of the cache; positions outside [0, T)
-    // write nothing.  The workgroup whose partition attends that row uses
-    // the values it computes itself in place of loading it, so no
-    // workgroup waits for the write.
-    const bool in_range = has_pro && p >= 0 && p < T;
-    const bool attended = has_pro && p >= t0 && p < t1;
-    const bool kwrite = in_range && part == 0 && wave == 0;
-    const bool need_k = attended || kwrite;
     // Every global load of the prologue is issued before the first tiles:
     // loads complete in order, so waiting for these never waits for a tile.
     const IT* qs = reinterpret_cast<const IT*>(a.q) + qoff;
+    QRaw<IT> qraw[KC];   // several tokens: unpacked after the tiles are issued
 #pragma unroll
-    for (int c = 0; c < KC; ++c) load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
+    for (int c = 0; c < KC; ++c) {
+      if constexpr (MT) qraw[c].load(qs + 32 * c + 8 * lg);
+      else load8f<IT>(qs + 32 * c + 8 * lg, qf[c]);
+    }
     const bool qnorm = has_pro && a.wq != nullptr;
     const bool rope = has_pro && a.rope;
     float wq8[KC][8];
@@ -498,53 +535,34 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     for (int c = 0; c < KC; ++c) {
       if (qnorm) load8f<float>(a.wq + 32 * c + 8 * lg, wq8[c]);
     }
+    // Query head g*G + hq: RMSNorm over D (the lane's D/4 elements, summed
+    // over the four lane groups of head n).
+    auto apply_qnorm = [&]() {
+      if (!qnorm) return;
+      float ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(qf[c][j], qf[c][j], ss);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qf[c][j] = qf[c][j] * r * wq8[c][j];
+    };
     const int fi = lane % HALF;               // rotary pair of this lane
     const bool il = a.rope_interleaved != 0;  // pairs (2i, 2i+1), else (i, i+D/2)
     const int e0 = il ? 2 * fi : fi, e1 = il ? 2 * fi + 1 : fi + HALF;
     const double inv_rev = rope ? a.inv_freq_rev[fi] : 0.0;
-    // raw values: converted only after the tiles are issued
-    IT rx0 = 0, rx1 = 0, rv0 = 0, rv1 = 0;
-    float wk0 = 1.0f, wk1 = 1.0f;
-    if (need_k) {
-      const IT* ks = reinterpret_cast<const IT*>(a.k_new) + (int64_t)b * a.kv_bstride +
-                     (int64_t)g * D;
-      const IT* vs = reinterpret_cast<const IT*>(a.v_new) + (int64_t)b * a.kv_bstride +
-                     (int64_t)g * D;
-      rx0 = ks[e0];
-      rx1 = ks[e1];
-      rv0 = vs[e0];
-      rv1 = vs[e1];
-      if (a.wk != nullptr) {
-        wk0 = a.wk[e0];
-        wk1 = a.wk[e1];
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    prime();
-    __builtin_amdgcn_sched_barrier(0);
-    // Rotary angle of pair fi: the phase p * f_fi / (2 pi) is formed and
-    // reduced in float64 from the host-computed table, leaving a float32
-    // sincos of an angle in [-pi, pi]; cos and sin carry the magnitude
-    // factor, so it reaches both q and k.
-    float cs = 1.0f, sn = 0.0f;
-    double fr = 0.0;
-    if (rope) {
-      const double rev = (double)p * inv_rev;
-      fr = rev - rint(rev);
-      sincosf((float)(fr * 6.283185307179586), &sn, &cs);
-      cs *= a.rope_mscale;
-      sn *= a.rope_mscale;
-    }
-    // Angles and the new K row cross lanes through this wave's LDS slab (in
-    // order within the wave; each asm hides an index from per-lane alias
-    // analysis, so the compiler keeps program order).
-    float* af = reinterpret_cast<float*>(slab);
-    if (need_k) {
-      // The appended K row in float64 (weights, a float64 sin/cos and the
-      // rotation on the exact inputs, the RMS factor last), rounded once:
-      // an element much smaller than its inputs keeps ~1e-7 relative
-      // accuracy, so it lands within one bf16 ulp of the exact value.
-      const float xf0 = to_f32(rx0), xf1 = to_f32(rx1);
+    // The appended K pair (e0, e1) in float64 (weights, a float64 sin/cos of
+    // the reduced phase fr and the rotation on the exact inputs, the RMS
+    // factor last), rounded once: an element much smaller than its inputs
+    // keeps ~1e-7 relative accuracy, so it lands within one bf16 ulp of the
+    // exact value.  Called by whole waves (the sum of squares crosses lanes).
+    auto k_pair = [&](float xf0, float xf1, float wk0, float wk1, double fr, uint16_t& k0,
+                      uint16_t& k1) {
       double x0 = xf0, x1 = xf1, r = 1.0;
       if (a.wk != nullptr) {
         const float ss = group_sum_shfl<HALF>(xf0 * xf0 + xf1 * xf1);
@@ -561,52 +579,200 @@ attn_decode_mfma_kernel(const KernelArgs a) {
         x0 = y0;
         x1 = y1;
       }
-      const uint16_t k0 = f32_to_bf16((float)(x0 * r)), k1 = f32_to_bf16((float)(x1 * r));
-      const uint16_t v0 = bits_bf16(&rv0, 0), v1 = bits_bf16(&rv1, 0);
-      if (kwrite && lane < HALF) {
-        uint16_t* krow = a.k_cache_w + slab_off + (int64_t)p * D;
-        uint16_t* vrow = a.v_cache_w + slab_off + (int64_t)p * D;
-        krow[e0] = k0;
-        krow[e1] = k1;
-        vrow[e0] = v0;
-        vrow[e1] = v1;
+      k0 = f32_to_bf16((float)(x0 * r));
+      k1 = f32_to_bf16((float)(x1 * r));
+    };
+    // Rotary phase p * f / (2 pi) of this lane's pair, formed and reduced to
+    // [-1/2, 1/2] in float64 from the host-computed table.
+    auto phase = [&](int64_t pos_s) {
+      const double rev = (double)pos_s * inv_rev;
+      return rev - rint(rev);
+    };
+    float cs = 1.0f, sn = 0.0f;
+    if constexpr (!MT) {
+      // The workgroup whose partition holds row pos[b] computes it, uses it
+      // in place of loading it and writes it to the cache (so no workgroup
+      // waits for the write); partition 0 writes it when it lies in the
+      // cache but outside the attended rows.  Positions outside [0, T) write
+      // nothing.
+      const bool in_range = has_pro && p >= 0 && p < T;
+      const bool attended = has_pro && p >= t0 && p < t1;
+      const bool outside = in_range && (p < lo || p >= nrow);
+      const bool kwrite = wave == 0 && (attended || (part == 0 && outside));
+      const bool need_k = attended || kwrite;
+      // raw values: converted only after the tiles are issued
+      IT rx0 = 0, rx1 = 0, rv0 = 0, rv1 = 0;
+      float wk0 = 1.0f, wk1 = 1.0f;
+      if (need_k) {
+        const IT* ks = reinterpret_cast<const IT*>(a.k_new) + (int64_t)b * a.kv_bstride +
+                       (int64_t)g * D;
+        const IT* vs = reinterpret_cast<const IT*>(a.v_new) + (int64_t)b * a.kv_bstride +
+                       (int64_t)g * D;
+        rx0 = ks[e0];
+        rx1 = ks[e1];
+        rv0 = vs[e0];
+        rv1 = vs[e1];
+        if (a.wk != nullptr) {
+          wk0 = a.wk[e0];
+          wk1 = a.wk[e1];
+        }
       }
-      if (attended && lane < HALF) {
-        uint16_t* kh = reinterpret_cast<uint16_t*>(&snew[wave][0][0]);
-        int kidx = fi;
-        asm volatile("" : "+v"(kidx));
-        const int k0i = il ? 2 * kidx : kidx, k1i = il ? 2 * kidx + 1 : kidx + HALF;
-        kh[k0i] = k0;
-        kh[k1i] = k1;
-        kh[D + k0i] = v0;
-        kh[D + k1i] = v1;
+      __builtin_amdgcn_sched_barrier(0);
+      prime();
+      __builtin_amdgcn_sched_barrier(0);
+      // (the asm keeps the weights' conversion, and so the wait for them,
+      // from moving ahead of the tile loads)
+      asm volatile("" : "+v"(wk0), "+v"(wk1));
+      // float32 sincos of the angle in [-pi, pi]; cos and sin carry the
+      // magnitude factor, so it reaches both q and k.
+      double fr = 0.0;
+      if (rope) {
+        fr = phase(p);
+        sincosf((float)(fr * 6.283185307179586), &sn, &cs);
+        cs *= a.rope_mscale;
+        sn *= a.rope_mscale;
       }
-      if (attended) psub = p;
+      if (need_k) {
+        uint16_t k0, k1;
+        k_pair(to_f32(rx0), to_f32(rx1), wk0, wk1, fr, k0, k1);
+        const uint16_t v0 = bits_bf16(&rv0, 0), v1 = bits_bf16(&rv1, 0);
+        if (kwrite && lane < HALF) {
+          uint16_t* krow = a.k_cache_w + slab_off + (int64_t)p * D;
+          uint16_t* vrow = a.v_cache_w + slab_off + (int64_t)p * D;
+          krow[e0] = k0;
+          krow[e1] = k1;
+          vrow[e0] = v0;
+          vrow[e1] = v1;
+        }
+        // the wave's copy crosses lanes through LDS in program order (the
+        // asm hides the index from per-lane alias analysis)
+        if (attended && lane < HALF) {
+          uint16_t* kh = reinterpret_cast<uint16_t*>(&snew[wave][0][0]);
+          int kidx = fi;
+          asm volatile("" : "+v"(kidx));
+          const int k0i = il ? 2 * kidx : kidx, k1i = il ? 2 * kidx + 1 : kidx + HALF;
+          kh[k0i] = k0;
+          kh[k1i] = k1;
+          kh[D + k0i] = v0;
+          kh[D + k1i] = v1;
+        }
+        if (attended) psub = p;
+      }
+    } else {
+      // Several tokens: token s sits at position p + s and is appended at
+      // cache row p + s (rows inside [0, T) only).  Every workgroup computes
+      // the new rows its partition holds, substitutes them for what it loads
+      // (as with one token) and writes them to the cache; partition 0 writes
+      // the new rows no token attends.  So each row is written once, and by
+      // a workgroup that computes it anyway.  Wave w takes tokens w, w + NW,
+      // ...; the angle table and the new rows are shared by the waves
+      // through LDS (one barrier).
+      constexpr int RW = (CT + NW - 1) / NW;   // tokens per wave at most
+      if (has_pro) {
+        sub_lo = (int)max((int64_t)p, (int64_t)t0);
+        sub_hi = (int)min((int64_t)p + S, (int64_t)t1);
+        p_new = p;
+      }
+      bool need[RW];
+      bool any_new = false;
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const int st = wave + NW * j;
+        const int64_t row = (int64_t)p + st;
+        // written by the workgroup whose partition holds it (that one
+        // computes it anyway), or by partition 0 when it lies in the cache
+        // but outside the rows the tokens attend
+        const bool outside = row >= 0 && row < T && (row < lo || row >= nrow);
+        need[j] = has_pro && st < S &&
+                  ((row >= sub_lo && row < sub_hi) || (part == 0 && outside));
+        any_new = any_new || need[j];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      prime();
+      __builtin_amdgcn_sched_barrier(0);
+      // The norm waits only for the loads issued before the tiles, and frees
+      // the weights' registers; the angle table needs no load.
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qraw[c].unpack(qf[c]);
+      apply_qnorm();
+      if (rope) {
+        for (int e = threadIdx.x; e < S * HALF; e += NW * 64) {
+          const int st = e / HALF, i = e % HALF;
+          const double rev = (double)((int64_t)p + st) * a.inv_freq_rev[i];
+          double sd, cd;
+          sincos_pi_f64((rev - rint(rev)) * 6.283185307179586, &sd, &cd);
+          ang[st][i] = (float)cd * a.rope_mscale;
+          ang[st][HALF + i] = (float)sd * a.rope_mscale;
+        }
+      }
+      // The new rows' inputs are loaded after the tiles: a value loaded
+      // under a condition and merged with a default makes the compiler wait
+      // for it (and for every load before it) ahead of the tile loads.
+      IT rx0[RW], rx1[RW], rv0[RW], rv1[RW];
+      float wk0 = 1.0f, wk1 = 1.0f;
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        if (!need[j]) continue;                         // wave-uniform
+        const int st = wave + NW * j;
+        const int64_t off = (int64_t)b * a.kv_bstride + ((int64_t)st * Hkv + g) * D;
+        const IT* ks = reinterpret_cast<const IT*>(a.k_new) + off;
+        const IT* vs = reinterpret_cast<const IT*>(a.v_new) + off;
+        rx0[j] = ks[e0];
+        rx1[j] = ks[e1];
+        rv0[j] = vs[e0];
+        rv1[j] = vs[e1];
+      }
+      if (any_new && a.wk != nullptr) {
+        wk0 = a.wk[e0];
+        wk1 = a.wk[e1];
+      }
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        if (!need[j]) continue;                         // wave-uniform
+        const int st = wave + NW * j;
+        const int row = p + st;
+        uint16_t k0, k1;
+        k_pair(to_f32(rx0[j]), to_f32(rx1[j]), wk0, wk1, rope ? phase(row) : 0.0, k0, k1);
+        const uint16_t v0 = bits_bf16(&rv0[j], 0), v1 = bits_bf16(&rv1[j], 0);
+        if (lane < HALF) {                              // row is inside [0, T)
+          uint16_t* krow = a.k_cache_w + slab_off + (int64_t)row * D;
+          uint16_t* vrow = a.v_cache_w + slab_off + (int64_t)row * D;
+          krow[e0] = k0;
+          krow[e1] = k1;
+          vrow[e0] = v0;
+          vrow[e1] = v1;
+        }
+        if (row >= sub_lo && row < sub_hi && lane < HALF) {
+          uint16_t* kh = reinterpret_cast<uint16_t*>(&sub_k[st][0][0]);
+          kh[e0] = k0;
+          kh[e1] = k1;
+          kh[D + e0] = v0;
+          kh[D + e1] = v1;
+        }
+      }
+      __syncthreads();   // the angle table and the new rows, for every wave
     }
-    // Query head g*G + hq: RMSNorm over D (the lane's D/4 elements, summed
-    // over the four lane groups of head n), then RoPE.  NeoX: element e < D/2
-    // of slice c pairs with e + D/2 in slice c + KC/2 of the same lane.
-    // Interleaved: elements 2i, 2i+1 sit next to each other in one slice.
-    if (qnorm) {
-      float ss = 0.0f;
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(qf[c][j], qf[c][j], ss);
-      ss += __shfl_xor(ss, 16, 64);
-      ss += __shfl_xor(ss, 32, 64);
-      const float r = 1.0f / sqrtf(ss / (float)D + a.eps);
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qf[c][j] = qf[c][j] * r * wq8[c][j];
-    }
+    // Then RoPE.  NeoX: element e < D/2 of slice c pairs with e + D/2 in
+    // slice c + KC/2 of the same lane.  Interleaved: elements 2i, 2i+1 sit
+    // next to each other in one slice.
+    if (!MT) apply_qnorm();
     if (rope) {
-      int aidx = fi;
-      asm volatile("" : "+v"(aidx));
-      if (lane < HALF) {
-        af[aidx] = cs;
-        af[HALF + aidx] = sn;
+      // One token: the angles cross lanes through this wave's LDS slab (in
+      // order within the wave; each asm hides an index from per-lane alias
+      // analysis, so the compiler keeps program order).  Several tokens:
+      // column hn reads its token's row of the shared table.
+      const float* af;
+      if constexpr (MT) {
+        af = &ang[tq][0];
+      } else {
+        float* aw = reinterpret_cast<float*>(slab);
+        int aidx = fi;
+        asm volatile("" : "+v"(aidx));
+        if (lane < HALF) {
+          aw[aidx] = cs;
+          aw[HALF + aidx] = sn;
+        }
+        af = aw;
       }
       if (il) {
         int ridx = 4 * lg;                   // pair of element 32c + 8lg + j is 16c + 4lg + j/2
@@ -706,8 +872,30 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     // The appended row (Step only) replaces whatever was loaded for it, in
     // the slab (K) and in the registers (V): a wave-uniform test, taken for
     // at most one tile of the range.
+    if constexpr (MODE == Mode::Step && MT) {
+      // several tokens: rows [sub_lo, sub_hi) come from the shared table
+      // (taken for at most two tiles; the asm keeps the table reads inside
+      // the branch instead of letting the compiler run them every tile)
+      if (sub_hi > base && sub_lo < base + 16) {     // wave-uniform
+        int sk = kp, sv = VB * n;
+        asm volatile("" : "+v"(sk), "+v"(sv));
+        const u32x4_t* tk = &sub_k[0][0][0];
+#pragma unroll
+        for (int i = 0; i < 16 / RPI; ++i) {
+          const int row = base + RPI * i + kr;
+          if (row >= sub_lo && row < sub_hi)
+            slab[widx + RPI * i * ROWU4] = tk[(row - p_new) * 2 * PPR + sk];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = base + 4 * r + lg;
+          if (row >= sub_lo && row < sub_hi)
+            buf.v[r].load(reinterpret_cast<const uint16_t*>(&sub_k[row - p_new][1][0]) + sv);
+        }
+      }
+    }
     const int dp = psub - base;
-    if ((unsigned)dp < 16u) {
+    if (!MT && (unsigned)dp < 16u) {
       int cidx = dp * ROWU4 + lane;
       asm volatile("" : "+v"(cidx));
       if (lane < PPR) slab[cidx] = snew[wave][0][lane];
@@ -900,8 +1088,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    // Step runs one token (S = 1, NC = G = CT): column c is row head0 + c.
-    merge_partials<D, CT, NW>(a, (int64_t)b * Hq + (int64_t)g * G);
+    merge_partials<D, CT, NW, MT>(a, head0, G, NC);
     if (threadIdx.x == 0)
       __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -914,8 +1101,10 @@ template <int D, int CT, typename IT, Mode MODE>
 static int launch_mode(const KernelArgs& a, hipStream_t s) {
   constexpr int NW = kWavesPerGroup;
   const dim3 grid((MODE == Mode::Final ? 1 : a.num_parts) * a.B * a.Hkv);
-  if (MODE != Mode::Step && a.S > 1)
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, IT, MODE, MODE != Mode::Step>), grid,
+  bool multi = false;
+  if constexpr (CT > 1) multi = a.S > 1;   // one column holds one token
+  if (multi)
+    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, IT, MODE, CT != 1>), grid,
                        dim3(NW * 64), 0, s, a);
   else
     hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, IT, MODE, false>), grid,

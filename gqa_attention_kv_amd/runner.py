@@ -16,8 +16,8 @@ import torch
 from . import attn_decode, attn_decode_merge, attn_decode_splitk, decode_step, qkv_prologue
 from . import decode_step_ex, qkv_prologue_ex, rope_table
 from . import attn_decode_merge_multi, attn_decode_multi, attn_decode_splitk_multi, attn_prefill
-from . import decode_step_workspace_bytes, splitk_multi_workspace_bytes, splitk_workspace_bytes
-from . import qkv_gemv
+from . import splitk_multi_workspace_bytes
+from . import decode_step_multi, decode_step_multi_workspace_bytes, qkv_gemv
 
 BF16_NAN = 0x7FC0
 
@@ -36,7 +36,8 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 class DeviceStep:
     """One decode step of workload ``w`` with all inputs resident in HBM.
 
-    ``mode``: "fused" runs the whole step as one launch (gqa_decode_step);
+    ``mode``: "fused" runs the whole step as one launch (gqa_decode_step, or
+    gqa_decode_step_multi with several tokens);
     "split" runs the prologue, the split-K partition pass over
     ``part_tokens``-row partitions (default: the workload's own size) and the
     merge as three launches; "unsplit" runs the prologue and the unsplit
@@ -55,8 +56,6 @@ class DeviceStep:
         self.dev = torch.device(device)
         self.S = int(getattr(w, "S", 1))     # query tokens per sequence
         self.mode = mode or ("split" if split else "unsplit")
-        if self.S > 1 and self.mode == "fused":
-            raise NotImplementedError("the one-launch step runs one token per sequence")
         self.causal = bool(getattr(w, "causal", True))
         if not self.causal and self.mode != "prefill":
             raise NotImplementedError("bidirectional attention runs on the prefill kernel")
@@ -116,8 +115,8 @@ class DeviceStep:
                                               self.part_tokens)
             self.ws = torch.empty(nb, dtype=torch.uint8, device=d)
         elif self.mode == "fused":
-            nb = decode_step_workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.T, w.window,
-                                             self.part_tokens)
+            nb = decode_step_multi_workspace_bytes(w.B, self.S, w.Hq, w.Hkv, w.D, w.T, w.window,
+                                                   self.part_tokens)
             self.ws = torch.zeros(nb, dtype=torch.uint8, device=d)   # tickets start at 0
 
     # -- the three stages, each one C-ABI call ------------------------------
@@ -174,6 +173,18 @@ class DeviceStep:
 
     def fused(self):
         w = self.w
+        if self.S > 1:
+            pro = w.pos is not None
+            decode_step_multi(self.q_in if pro else self.q, self.k_new if pro else None,
+                              self.v_new if pro else None, self.pos if pro else None,
+                              self.k_cache, self.v_cache, self.lens, self.part_tokens,
+                              workspace=self.ws, inv_freq=self.inv_freq if pro else None,
+                              rope_mscale=self.rope_mscale, rope_layout=self.rope_layout,
+                              q_norm_w=self.w_q if pro else None,
+                              k_norm_w=self.w_k if pro else None, eps=w.eps,
+                              window=w.window, scale=self.scale, out=self.out,
+                              lse_out=self.lse, q_out=self.q if pro else None)
+            return
         if w.pos is None:        # no prologue: attention and merge in one launch
             decode_step(self.q, None, None, None, self.k_cache, self.v_cache, self.lens,
                         self.part_tokens, workspace=self.ws, window=w.window,
@@ -196,7 +207,8 @@ class DeviceStep:
         """The fused step's arrival tickets (int32 view of the workspace
         tail, [B*Hkv]); they are zero between calls."""
         w = self.w
-        base = splitk_workspace_bytes(w.B, w.Hq, w.D, w.T, w.window, self.part_tokens)
+        base = splitk_multi_workspace_bytes(w.B, self.S, w.Hq, w.D, w.T, w.window,
+                                            self.part_tokens)
         off = base + (-base) % 256
         return self.ws[off:off + 4 * w.B * w.Hkv].view(torch.int32)
 

@@ -317,6 +317,43 @@ int gqa_attn_decode_merge_multi(const void* workspace, size_t workspace_bytes, i
                                 int B, int Hq, int D, int T, hipStream_t stream);
 
 /*
+ * The whole multi-token step in one launch: the effect of
+ * gqa_qkv_prologue_ex over S tokens followed by gqa_attn_decode_splitk_multi
+ * and gqa_attn_decode_merge_multi, as gqa_decode_step_ex is for one token
+ * (which is this call with S = 1).  Token s of sequence b is rotated at
+ * position pos[b] + s and appended at cache row pos[b] + s (rows outside
+ * [0, T) are not written); the attended rows are those of
+ * gqa_attn_decode_multi.  Every workgroup whose partition attends one of the
+ * new rows computes it and uses it in place of reading it; partition 0
+ * writes them to the cache.
+ *   q       [B,S,Hq,D] in in_dtype: sequences q_bstride >= S*Hq*D elements
+ *           apart, tokens Hq*D apart, heads dense.
+ *   k_new, v_new  [B,S,Hkv,D]: sequences kv_bstride >= S*Hkv*D apart,
+ *           tokens Hkv*D apart.
+ *   out     [B,S,Hq,D]; lse_out [B,S,Hq] or NULL; q_out float32 [B,S,Hq,D]
+ *           or NULL.
+ *   workspace  gqa_decode_step_multi_workspace_bytes() bytes, 256-byte
+ *           aligned: the layout of gqa_splitk_multi_workspace_bytes, then
+ *           (at the next 256-byte boundary) the uint32 [B,Hkv] tickets, zero
+ *           before the first call and left zero by every call that completes.
+ * G * S <= 16 (else GQA_ERR_UNSUPPORTED); the partials of one (sequence, KV
+ * head), ((S-1)*Hq + G) * partitions * D * 4 bytes, below 2 GiB (else
+ * GQA_ERR_SHAPE).  Other arguments and errors as for gqa_decode_step_ex.
+ */
+size_t gqa_decode_step_multi_workspace_bytes(int B, int S, int Hq, int Hkv, int D, int T,
+                                             int window, int part_tokens);
+int gqa_decode_step_multi(const void* q, const void* k_new, const void* v_new,
+                          gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                          const float* q_norm_w, const float* k_norm_w, float eps,
+                          const double* inv_freq, double rope_mscale, int rope_layout,
+                          const int32_t* pos, int S,
+                          uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                          int window, float scale, int part_tokens,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                          int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
+/*
  * Prefill: attention of S query tokens per sequence over the cache, causal
  * or bidirectional (fusedtok README, "Operators" row attention_prefill),
  * with the GQA head mapping, lengths and window of attention_decode.  The S

@@ -1,6 +1,7 @@
 """Seeded random sweep over the whole surface: the decode step (split,
-unsplit and fused), several tokens per sequence, the prefill (causal and
-bidirectional) and the packed QKV projection.  Each case draws its sizes
+unsplit and fused), several tokens per sequence (split, unsplit and in one
+launch), the prefill (causal and bidirectional) and the packed QKV
+projection.  Each case draws its sizes
 from a fixed-seed generator -- group size, head dim, batch, cache length,
 lengths (ragged, some zero), window, partition size, token count, output
 dtype -- and is checked against the fp64 oracle at the same bars as the
@@ -34,7 +35,7 @@ def _decode_cases(n=60, seed=1234):
     return out
 
 
-def _tokens_cases(n=60, seed=4321, prefill=False):
+def _tokens_cases(n=60, seed=4321, prefill=False, fused=False):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -49,6 +50,8 @@ def _tokens_cases(n=60, seed=4321, prefill=False):
         T = int(rng.integers(S + 1, S + 700))
         window = 0 if rng.random() < 0.5 else int(rng.integers(1, T + 1))
         mode = "prefill" if prefill else str(rng.choice(["split", "unsplit"]))
+        if fused:
+            mode = "fused"
         out.append(dict(G=G, Hkv=Hkv, D=D, B=B, S=S, T=T, window=window, mode=mode,
                         prologue=bool(rng.random() < 0.6), norm=bool(rng.random() < 0.5),
                         causal=bool(rng.random() < 0.7) if prefill else True,
@@ -120,6 +123,12 @@ def test_gpu_sweep_decode(c):
 @pytest.mark.gpu
 @pytest.mark.parametrize("c", _tokens_cases(), ids=_cid)
 def test_gpu_sweep_tokens(c):
+    _run(c)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("c", _tokens_cases(n=40, seed=5678, fused=True), ids=_cid)
+def test_gpu_sweep_tokens_one_launch(c):
     _run(c)
 
 
