@@ -109,6 +109,13 @@ __device__ __forceinline__ uint32_t dup_bf16(const VRow<D>& r, int e) {
   return __builtin_amdgcn_perm(w, w, (e & 1) ? 0x03020302u : 0x01000100u);
 }
 
+// Two floats rounded to bf16 (nearest even, one v_cvt_pk_bf16_f32), a in
+// the low half of the dword.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // x as a bf16 pair (hi, lo) with hi = bf16(x) and lo = bf16(x - hi): hi + lo
 // carries ~16 significant bits of x.  hi in the low half of the dword.
 __device__ __forceinline__ uint32_t split_bf16(float x) {
@@ -320,8 +327,7 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
     const int64_t oi = (head0 + rel(h)) * D + 4 * d4;
     if (a.out_bf16) {
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oi) =
-          make_uint2(pack2(f32_to_bf16(ov[0]), f32_to_bf16(ov[1])),
-                     pack2(f32_to_bf16(ov[2]), f32_to_bf16(ov[3])));
+          make_uint2(pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3]));
     } else {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oi) =
           make_float4(ov[0], ov[1], ov[2], ov[3]);
@@ -623,12 +629,15 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       // (the asm keeps the weights' conversion, and so the wait for them,
       // from moving ahead of the tile loads)
       asm volatile("" : "+v"(wk0), "+v"(wk1));
-      // float32 sincos of the angle in [-pi, pi]; cos and sin carry the
+      // q's sin and cos from the hardware's v_sin_f32 / v_cos_f32, which
+      // take the angle in turns: the reduced phase in [-1/2, 1/2] is exactly
+      // that, so no range reduction is needed.  cos and sin carry the
       // magnitude factor, so it reaches both q and k.
       double fr = 0.0;
       if (rope) {
         fr = phase(p);
-        sincosf((float)(fr * 6.283185307179586), &sn, &cs);
+        sn = __builtin_amdgcn_sinf((float)fr);
+        cs = __builtin_amdgcn_cosf((float)fr);
         cs *= a.rope_mscale;
         sn *= a.rope_mscale;
       }
@@ -835,17 +844,17 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   const bool lo_col = kFold && n >= 8;
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    uint16_t h16[8], l16[8];
+    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      h16[j] = f32_to_bf16(qf[c][j]);
-      l16[j] = f32_to_bf16(qf[c][j] - bf16_to_f32(h16[j]));
-      if (lo_col) h16[j] = l16[j];
+    for (int w = 0; w < 4; ++w) {
+      const float x0 = qf[c][2 * w], x1 = qf[c][2 * w + 1];
+      hw[w] = pack_bf16(x0, x1);
+      lw[w] = pack_bf16(x0 - __uint_as_float(hw[w] << 16),
+                        x1 - __uint_as_float(hw[w] & 0xffff0000u));
+      if (lo_col) hw[w] = lw[w];
     }
-    qhi[c] = make_uint4(pack2(h16[0], h16[1]), pack2(h16[2], h16[3]),
-                        pack2(h16[4], h16[5]), pack2(h16[6], h16[7]));
-    qlo[c] = make_uint4(pack2(l16[0], l16[1]), pack2(l16[2], l16[3]),
-                        pack2(l16[4], l16[5]), pack2(l16[6], l16[7]));
+    qhi[c] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    qlo[c] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
 
   float m = -INFINITY;   // running max of head n (same in all four lane groups)
@@ -1049,7 +1058,8 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     const float ov = any ? A / L : 0.0f;
     const float lse = any ? (M + log2f(L)) * kLn2 : -INFINITY;
     if (write_final) {
-      if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oh * D + d] = f32_to_bf16(ov);
+      if (a.out_bf16)
+        reinterpret_cast<uint16_t*>(a.out)[oh * D + d] = __builtin_bit_cast(uint16_t, (__bf16)ov);
       else reinterpret_cast<float*>(a.out)[oh * D + d] = ov;
       if (d == 0 && a.lse_out != nullptr) a.lse_out[oh] = lse;
     } else if (MODE == Mode::Split) {
