@@ -3,9 +3,8 @@
 One step = one pass of the whole decode hot path over one batch: the fused
 prologue (QK-RMSNorm + NeoX RoPE + K/V append), the split-K attention pass
 and the log-sum-exp merge.  By default (--mode fused) that is one C-ABI call,
-gqa_decode_step, i.e. one kernel launch (with several query tokens per
-sequence the three launches are the default; --one-launch times
-gqa_decode_step_multi instead); --mode split makes it three calls
+gqa_decode_step (gqa_decode_step_multi with several query tokens per
+sequence), i.e. one kernel launch; --mode split makes it three calls
 (prologue, split-K pass, merge).  Every launch goes to torch's current
 stream and every input is already resident in HBM.  Before each timed step,
 a read-only sweep of a 1 GiB buffer evicts the KV window from the L2s and the
@@ -93,9 +92,6 @@ def _parse():
                          "prologue, split-K pass and merge as three launches; prefill: "
                          "prologue and the matrix-core prefill kernel (the default "
                          "for the prefill workloads)")
-    ap.add_argument("--one-launch", action="store_true",
-                    help="several query tokens: time the one-launch step "
-                         "(gqa_decode_step_multi) instead of the three launches")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn two rocprofv3 --pmc output directories "
                          "(FETCH_SIZE, WRITE_SIZE; each from a bench run with "
@@ -485,10 +481,6 @@ def main():
     mode = args.mode
     if args.workload in PREFILL_WORKLOADS:
         mode = "prefill"
-    elif w.S > 1 and mode == "fused" and not args.one_launch:
-        # several tokens: the three launches measure ~2 us faster than the
-        # one-launch step (gqa_decode_step_multi), so they are the default
-        mode = "split"
     step = DeviceStep(w, device=dev, mode=mode)
     flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
                                                           device=dev)
