@@ -92,6 +92,9 @@ def _parse():
                          "prologue, split-K pass and merge as three launches; prefill: "
                          "prologue and the matrix-core prefill kernel (the default "
                          "for the prefill workloads)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="prefill: key splits per row block (0: the library's "
+                         "suggestion for the device, gqa_attn_prefill_default_splits)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: turn two rocprofv3 --pmc output directories "
                          "(FETCH_SIZE, WRITE_SIZE; each from a bench run with "
@@ -463,6 +466,7 @@ def main():
     import torch
 
     import workloads
+    from gqa_attention_kv_amd import prefill_default_splits
     from gqa_attention_kv_amd.runner import DeviceStep
 
     if not torch.cuda.is_available():
@@ -479,9 +483,12 @@ def main():
         w.part_tokens = args.part_tokens
     kvb = workloads.kv_bytes(w)
     mode = args.mode
+    splits = 1
     if args.workload in PREFILL_WORKLOADS:
         mode = "prefill"
-    step = DeviceStep(w, device=dev, mode=mode)
+        # key splits: the library's suggestion for this device unless given
+        splits = args.splits or prefill_default_splits(w.B, w.S, w.Hq, w.Hkv)
+    step = DeviceStep(w, device=dev, mode=mode, splits=splits)
     flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
                                                           device=dev)
     flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
@@ -600,6 +607,7 @@ def main():
             "query_tokens": w.S,
             "window": w.window, "part_tokens": w.part_tokens, "out_dtype": w.out_dtype,
             "path": mode,
+            **({"key_splits": splits} if mode == "prefill" else {}),
             "prologue": ("qk_rmsnorm+rope+append" if w.w_q is not None else
                          "rope+append") if w.pos is not None else "none",
             "kv_bytes_per_step": kvb,

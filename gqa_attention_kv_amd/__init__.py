@@ -10,7 +10,8 @@ Functions follow the C entry points' names without the ``gqa_`` prefix:
 ``qkv_prologue``, ``qkv_prologue_ex``, ``attn_decode``,
 ``attn_decode_splitk``, ``attn_decode_merge``, ``attn_decode_multi``,
 ``attn_decode_splitk_multi``, ``attn_decode_merge_multi``, ``decode_step``,
-``decode_step_ex``, ``decode_step_multi``, ``attn_prefill``, ``qkv_gemv``,
+``decode_step_ex``, ``decode_step_multi``, ``attn_prefill`` (with key
+``splits``: ``prefill_workspace_bytes``, ``prefill_default_splits``), ``qkv_gemv``,
 ``rope_table``, ``splitk_workspace_bytes``, ``splitk_multi_workspace_bytes``,
 ``decode_step_workspace_bytes``, ``decode_step_multi_workspace_bytes``,
 ``num_partitions``.
@@ -31,7 +32,7 @@ __all__ = [
     "decode_step", "decode_step_ex", "decode_step_workspace_bytes", "rope_table",
     "attn_decode_multi", "attn_decode_splitk_multi", "attn_decode_merge_multi",
     "splitk_multi_workspace_bytes", "decode_step_multi", "decode_step_multi_workspace_bytes",
-    "attn_prefill", "qkv_gemv",
+    "attn_prefill", "qkv_gemv", "prefill_workspace_bytes", "prefill_default_splits",
     "F32", "BF16", "SYMBOLS", "ROPE_NEOX", "ROPE_INTERLEAVED", "ROPE_KINDS",
 ]
 
@@ -86,6 +87,10 @@ SYMBOLS = {
     "gqa_attn_prefill": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _f, _p, _i, _p, _i, _i, _i, _i,
                               _i, _p]),
     "gqa_qkv_gemv": (_i, [_p, _i64, _p, _i64, _p, _i, _i64, _i, _i, _i, _p]),
+    "gqa_attn_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "gqa_attn_prefill_default_splits": (_i, [_i, _i, _i, _i]),
+    "gqa_attn_prefill_split": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _f, _i, _p, _sz, _p, _i,
+                                    _p, _i, _i, _i, _i, _i, _p]),
 }
 for _name, (_res, _args) in SYMBOLS.items():
     _fn = getattr(lib, _name)
@@ -394,11 +399,15 @@ def attn_decode_multi(q, k_cache, v_cache, lens, window: int = 0, scale: float =
 
 
 def attn_prefill(q, k_cache, v_cache, lens, causal: bool = True, window: int = 0,
-                 scale: float = 0.0, out=None, out_dtype=torch.float32, lse_out=None):
+                 scale: float = 0.0, out=None, out_dtype=torch.float32, lse_out=None,
+                 splits: int = 1, workspace=None):
     """S query tokens per sequence (q [B,S,Hq,D]) over the cache on the matrix
     cores, any S.  causal: token s attends lens[b] - (S-1-s) rows (as
     attn_decode_multi); otherwise every token attends lens[b] rows.  Returns
-    out [B,S,Hq,D]; writes the LSE into ``lse_out`` (float32 [B,S,Hq])."""
+    out [B,S,Hq,D]; writes the LSE into ``lse_out`` (float32 [B,S,Hq]).
+    ``splits`` > 1 shares each row block's keys among that many workgroups
+    (gqa_attn_prefill_split); ``workspace`` (uint8, its tickets zero) is
+    allocated zeroed when None -- reuse it across calls."""
     dev, B, S, Hq, Hkv, D, T = _multi_common(q, k_cache, v_cache, lens)
     if out is None:
         out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=dev)
@@ -408,11 +417,28 @@ def attn_prefill(q, k_cache, v_cache, lens, causal: bool = True, window: int = 0
         raise ValueError("out must be [B,S,Hq,D]")
     if lse_out is not None:
         _lse_check(lse_out.reshape(B, S * Hq), B, S * Hq, dev)
-    _check(lib.gqa_attn_prefill(
+    nbytes = 0
+    if splits > 1:
+        need = prefill_workspace_bytes(B, S, Hq, Hkv, D, splits)
+        if workspace is None:
+            workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+        _dev(workspace, "workspace", dev)
+        _contig(workspace, "workspace")
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gqa_attn_prefill_split(
         _ptr(q), _dtype_code(q, "q"), _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(S),
-        1 if causal else 0, int(window), float(scale), _ptr(out), _dtype_code(out, "out"),
+        1 if causal else 0, int(window), float(scale), int(splits),
+        _ptr(workspace) if splits > 1 else None, nbytes, _ptr(out), _dtype_code(out, "out"),
         _ptr(lse_out), B, Hq, Hkv, D, T, _stream(dev)))
     return out
+
+
+def prefill_workspace_bytes(B: int, S: int, Hq: int, Hkv: int, D: int, splits: int) -> int:
+    return int(lib.gqa_attn_prefill_workspace_bytes(B, S, Hq, Hkv, D, splits))
+
+
+def prefill_default_splits(B: int, S: int, Hq: int, Hkv: int) -> int:
+    return int(lib.gqa_attn_prefill_default_splits(B, S, Hq, Hkv))
 
 
 def qkv_gemv(x, w, out=None, out_dtype=torch.bfloat16):

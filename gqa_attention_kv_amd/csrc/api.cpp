@@ -232,21 +232,68 @@ int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
                      const int32_t* lens, int S, int causal, int window, float scale,
                      void* out, gqa_dtype_t out_dtype, float* lse_out,
                      int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  return gqa_attn_prefill_split(q, q_dtype, k_cache, v_cache, lens, S, causal, window, scale, 1,
+                                nullptr, 0, out, out_dtype, lse_out, B, Hq, Hkv, D, T, stream);
+}
+
+// Prefill key-split workspace: partial o [teams, splits, rows, D], then
+// (256-byte aligned) partial lse [teams, splits, rows], then tickets
+// [teams]; teams = B * Hkv * row blocks.
+static int64_t prefill_teams(int B, int S, int Hq, int Hkv) {
+  const int64_t rows = (int64_t)S * (Hq / Hkv);
+  const int per = gqa::prefill_rows_per_block();
+  return (int64_t)B * Hkv * ((rows + per - 1) / per);
+}
+
+size_t gqa_attn_prefill_workspace_bytes(int B, int S, int Hq, int Hkv, int D, int splits) {
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || D < 1 || splits < 1 || Hq % Hkv != 0) return 0;
+  if (splits == 1) return 0;
+  const int64_t teams = prefill_teams(B, S, Hq, Hkv);
+  const size_t part = (size_t)teams * splits * gqa::prefill_rows_per_block();
+  return align256(part * D * sizeof(float)) + align256(part * sizeof(float)) +
+         (size_t)teams * sizeof(uint32_t);
+}
+
+int gqa_attn_prefill_default_splits(int B, int S, int Hq, int Hkv) {
+  if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return 1;
+  // Fewer row blocks than two per CU: two splits.  More splits measured
+  // slower on the fresh S = 1024 prefill (each split writes and the last
+  // reads back a 64 KB partial, as much as its share of the keys).
+  const int64_t wgs = prefill_teams(B, S, Hq, Hkv);
+  return wgs < 2 * (int64_t)cus ? 2 : 1;
+}
+
+int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,
+                           const uint16_t* k_cache, const uint16_t* v_cache,
+                           const int32_t* lens, int S, int causal, int window, float scale,
+                           int splits, void* workspace, size_t workspace_bytes,
+                           void* out, gqa_dtype_t out_dtype, float* lse_out,
+                           int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
   if (!q || !k_cache || !v_cache || !lens || !out) return GQA_ERR_NULL;
   int rc = check_shapes(B, Hq, Hkv, D, T);
   if (rc) return rc;
   if (S < 1) return GQA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return GQA_ERR_VALUE;
+  if (splits < 1 || splits > 16) return GQA_ERR_VALUE;
+  if (splits > 1 && !workspace) return GQA_ERR_NULL;
   if (!dtype_ok(q_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
   if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(lens, 4) || !aligned(lse_out, 4))
+      !aligned(lens, 4) || !aligned(lse_out, 4) || !aligned(workspace, 256))
     return GQA_ERR_ALIGN;
   const int64_t rows = (int64_t)S * (Hq / Hkv);   // (token, head) rows per KV head
   if (rows > INT32_MAX / 2 || (int64_t)B * S * Hq > kMaxIndex / D) return GQA_ERR_SHAPE;
   const int per = gqa::prefill_rows_per_block();
   const int64_t row_blocks = (rows + per - 1) / per;
-  if ((int64_t)B * Hkv * row_blocks > kMaxWorkgroups) return GQA_ERR_SHAPE;
+  if ((int64_t)B * Hkv * row_blocks * splits > kMaxWorkgroups) return GQA_ERR_SHAPE;
+  if (splits > 1 &&
+      workspace_bytes < gqa_attn_prefill_workspace_bytes(B, S, Hq, Hkv, D, splits))
+    return GQA_ERR_WORKSPACE;
   gqa::PrefillArgs a{};
   a.q = q; a.in_bf16 = q_dtype == GQA_BF16;
   a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens;
@@ -255,6 +302,15 @@ int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
   a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   a.row_blocks = (int)row_blocks;
+  a.splits = splits;
+  if (splits > 1) {
+    const size_t part = (size_t)B * Hkv * row_blocks * splits * per;
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws);
+    a.ws_lse = reinterpret_cast<float*>(ws + align256(part * D * sizeof(float)));
+    a.ws_cnt = reinterpret_cast<uint32_t*>(ws + align256(part * D * sizeof(float)) +
+                                           align256(part * sizeof(float)));
+  }
   return gqa::launch_attn_prefill(a, stream);
 }
 

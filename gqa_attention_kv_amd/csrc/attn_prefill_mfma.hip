@@ -97,7 +97,9 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int D, bool QF32, bool PLO>
+// SPLIT: the launch shares each row block's keys among a.splits > 1
+// workgroups (the instances without it keep the plain loop and epilogue).
+template <int D, bool QF32, bool PLO, bool SPLIT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void
 attn_prefill_kernel(const PrefillArgs a) {
   constexpr int KC = D / 32;            // QK slices
@@ -121,21 +123,25 @@ attn_prefill_kernel(const PrefillArgs a) {
   const int nrb = a.row_blocks;
   const int npairs = a.B * Hkv;
 
-  // Workgroup -> (sequence, KV head, row block).  Workgroup x runs on XCD
-  // x % 8; when the pairs split evenly, every row block of a pair lands on
-  // the same XCD so its K/V rows are reused from that XCD's L2.  Row blocks
-  // run from the last (most keys under the causal mask) to the first.
+  // Workgroup -> (sequence, KV head, row block, key split).  Workgroup x
+  // runs on XCD x % 8; when the pairs split evenly, every row block of a
+  // pair lands on the same XCD so its K/V rows are reused from that XCD's
+  // L2.  Row blocks run from the last (most keys under the causal mask) to
+  // the first; the splits of a row block are adjacent.
+  const int splits = SPLIT ? a.splits : 1;
+  const int nunits = nrb * splits;
   const int x = blockIdx.x;
-  int pair, rbi;
+  int pair, ui;
   if ((npairs & 7) == 0) {
     const int slot = x >> 3;
-    pair = (x & 7) + 8 * (slot / nrb);
-    rbi = slot % nrb;
+    pair = (x & 7) + 8 * (slot / nunits);
+    ui = slot % nunits;
   } else {
-    pair = x / nrb;
-    rbi = x % nrb;
+    pair = x / nunits;
+    ui = x % nunits;
   }
-  const int rb = nrb - 1 - rbi;
+  const int rb = nrb - 1 - ui / splits;
+  const int sp = ui % splits;
   const int b = pair / Hkv, g = pair % Hkv;
 
   const int tid = threadIdx.x;
@@ -234,6 +240,11 @@ attn_prefill_kernel(const PrefillArgs a) {
   const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache + slab, slab_bytes);
 
   const int ntiles = kend > kbeg ? (kend - kbeg + kKeys - 1) / kKeys : 0;
+  // This split's tiles [tb, te): the row block's tiles in `splits` nearly
+  // equal runs (all of them with one split).
+  const int per = (ntiles + splits - 1) / splits;
+  const int tb = min(sp * per, ntiles);
+  const int te = min(tb + per, ntiles);
 
   // Tile fill.  K: thread t moves chunks t + 256 f (row-major, CPR chunks a
   // row).  V: item t + 256 f (< VITEMS) is chunk it / (kKeys/2) of keys
@@ -294,14 +305,14 @@ attn_prefill_kernel(const PrefillArgs a) {
     }
   };
 
-  if (ntiles > 0) {
-    fetch(0);
+  if (te > tb) {
+    fetch(tb);
     stash(0);
-    if (ntiles > 1) fetch(1);
+    if (te > tb + 1) fetch(tb + 1);
   }
   __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const unsigned char* cur = lds + (tile & 1) * STAGE;
+  for (int tile = tb; tile < te; ++tile) {
+    const unsigned char* cur = lds + ((tile - tb) & 1) * STAGE;
     const int k0 = kbeg + kKeys * tile;
     const bool work = wave_live && k0 < need_hi && k0 + kKeys > need_lo;   // wave-uniform
     f32x4_t s[kKB][2];
@@ -334,8 +345,8 @@ attn_prefill_kernel(const PrefillArgs a) {
     // whose hi and lo parts leave no registers for it -- after the PV calls.
     constexpr bool kEarlyStash = !QF32;
     if (kEarlyStash) {
-      if (tile + 1 < ntiles) stash((tile + 1) & 1);
-      if (tile + 2 < ntiles) fetch(tile + 2);
+      if (tile + 1 < te) stash((tile + 1 - tb) & 1);
+      if (tile + 2 < te) fetch(tile + 2);
     }
     if (work) {
       const bool full = k0 >= free_lo && k0 + kKeys <= free_hi;
@@ -427,54 +438,158 @@ attn_prefill_kernel(const PrefillArgs a) {
         }
     }
     if (!kEarlyStash) {
-      if (tile + 1 < ntiles) stash((tile + 1) & 1);
-      if (tile + 2 < ntiles) fetch(tile + 2);
+      if (tile + 1 < te) stash((tile + 1 - tb) & 1);
+      if (tile + 2 < te) fetch(tile + 2);
     }
     __syncthreads();
   }
 
   // Normalise and store.  Lane (n, k4) holds, for row n of block j, columns
-  // 16 v + 4 k4 + i (i < 4) of block v.
+  // 16 v + 4 k4 + i (i < 4) of block v.  With key splits the normalised
+  // rows and their lse are this split's partial.
+  const int64_t team = (int64_t)pair * nrb + rb;
+  constexpr int kCoherent = 0x10;   // sc1: write through to / read from the coherence point
+  // this row block's partials (no records without splits)
+  const __amdgpu_buffer_rsrc_t ro =
+      SPLIT ? slab_rsrc(a.ws_o + team * splits * kRows * D, (uint32_t)(splits * kRows * D * 4))
+            : slab_rsrc(nullptr, 0u);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float lt = l[j];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    const int row = r0 + kRowsPerWave * wave + 16 * j + n;
+    const int rr = kRowsPerWave * wave + 16 * j + n;    // row within the block
+    const int row = r0 + rr;
     if (row >= SG) continue;
     const int t = row / G, h = row % G;
     const int64_t orow = ((int64_t)b * S + t) * Hq + (int64_t)g * G + h;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const float lse = lt > 0.0f ? (m[j] * qscale + log2f(lt)) * kLn2 : -INFINITY;
 #pragma unroll
     for (int v = 0; v < VB; ++v) {
       const int d0 = 16 * v + 4 * k4;
       const float y0 = o[j][v][0] * inv, y1 = o[j][v][1] * inv;
       const float y2 = o[j][v][2] * inv, y3 = o[j][v][3] * inv;
-      if (a.out_bf16) {
+      if constexpr (SPLIT) {
+        const uint32_t off = (uint32_t)(((sp * kRows + rr) * D + d0) * 4);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4_t, float4{y0, y1, y2, y3}), ro, off, 0, kCoherent);
+      } else if (a.out_bf16) {
         uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + orow * D + d0;
-        *reinterpret_cast<uint2*>(dst) =
-            uint2{(uint32_t)f32_to_bf16(y0) | ((uint32_t)f32_to_bf16(y1) << 16),
-                  (uint32_t)f32_to_bf16(y2) | ((uint32_t)f32_to_bf16(y3) << 16)};
+        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16(y0, y1), pack_bf16(y2, y3)};
       } else {
         float* dst = reinterpret_cast<float*>(a.out) + orow * D + d0;
         *reinterpret_cast<float4*>(dst) = float4{y0, y1, y2, y3};
       }
     }
-    if (a.lse_out != nullptr && k4 == 0)
-      a.lse_out[orow] = lt > 0.0f ? (m[j] * qscale + log2f(lt)) * kLn2 : -INFINITY;
+    if (k4 == 0) {
+      if constexpr (SPLIT)
+        __hip_atomic_store(a.ws_lse + (team * splits + sp) * kRows + rr, lse, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else if (a.lse_out != nullptr)
+        a.lse_out[orow] = lse;
+    }
   }
+  if constexpr (!SPLIT) return;
+
+  // Arrival ticket (one per row block): the last split to arrive merges the
+  // partials in split order, so reruns are bit-identical, and resets the
+  // ticket.  No workgroup waits for another.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // partial stores completed
+  __syncthreads();
+  __shared__ int s_last;
+  uint32_t* ticket = a.ws_cnt + team;
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == (uint32_t)(splits - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // Thread tid owns float4 groups tid + 256 i of the block's rows x D: row
+  // (tid + 256 i) / (D/4).  One memory round trip per split: M, W and A are
+  // the running maximum lse, weight sum and weighted sum.
+  constexpr int QD = D / 4;
+  constexpr int GPT = kRows * QD / (kWaves * 64);
+  const int nvalid = SG - r0 < kRows ? SG - r0 : kRows;
+  const float* lse_t = a.ws_lse + team * splits * kRows;
+  float Mx[GPT], Wx[GPT];
+  float4 Ax[GPT];
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    Mx[i] = -INFINITY;
+    Wx[i] = 0.0f;
+    Ax[i] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int q = 0; q < splits; ++q) {
+    float lk[GPT];
+    float4 ok[GPT];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int gi = tid + kWaves * 64 * i;
+      const int rr = gi / QD, d4 = gi % QD;
+      lk[i] = -INFINITY;
+      ok[i] = float4{0.f, 0.f, 0.f, 0.f};
+      if (rr < nvalid) {
+        lk[i] = __hip_atomic_load(lse_t + q * kRows + rr, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        ok[i] = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(
+                        ro, (uint32_t)(((q * kRows + rr) * D + 4 * d4) * 4), 0, kCoherent));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      if (lk[i] == -INFINITY) continue;           // no key of this split for the row
+      const float Mn = fmaxf(Mx[i], lk[i]);
+      const float sc = __expf(Mx[i] - Mn);        // 0 while nothing was seen
+      const float w = __expf(lk[i] - Mn);
+      Wx[i] = Wx[i] * sc + w;
+      Ax[i].x = fmaf(w, ok[i].x, Ax[i].x * sc);
+      Ax[i].y = fmaf(w, ok[i].y, Ax[i].y * sc);
+      Ax[i].z = fmaf(w, ok[i].z, Ax[i].z * sc);
+      Ax[i].w = fmaf(w, ok[i].w, Ax[i].w * sc);
+      Mx[i] = Mn;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < GPT; ++i) {
+    const int gi = tid + kWaves * 64 * i;
+    const int rr = gi / QD, d4 = gi % QD;
+    if (rr >= nvalid) continue;
+    const int row = r0 + rr;
+    const int t = row / G, h = row % G;
+    const int64_t orow = ((int64_t)b * S + t) * Hq + (int64_t)g * G + h;
+    const bool any = Wx[i] > 0.0f;
+    const float inv = any ? 1.0f / Wx[i] : 0.0f;
+    const float y0 = Ax[i].x * inv, y1 = Ax[i].y * inv, y2 = Ax[i].z * inv, y3 = Ax[i].w * inv;
+    if (a.out_bf16) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + orow * D + 4 * d4;
+      *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16(y0, y1), pack_bf16(y2, y3)};
+    } else {
+      float* dst = reinterpret_cast<float*>(a.out) + orow * D + 4 * d4;
+      *reinterpret_cast<float4*>(dst) = float4{y0, y1, y2, y3};
+    }
+    if (d4 == 0 && a.lse_out != nullptr) a.lse_out[orow] = any ? Mx[i] + logf(Wx[i]) : -INFINITY;
+  }
+  if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D, bool QF32, bool PLO>
+int launch_s(const PrefillArgs& a, hipStream_t s) {
+  const unsigned blocks = (unsigned)((int64_t)a.B * a.Hkv * a.row_blocks * a.splits);
+  if (a.splits > 1)
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QF32, PLO, true>), dim3(blocks),
+                       dim3(kWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QF32, PLO, false>), dim3(blocks),
+                       dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
 template <int D, bool QF32>
 int launch_t(const PrefillArgs& a, hipStream_t s) {
-  const unsigned blocks = (unsigned)((int64_t)a.B * a.Hkv * a.row_blocks);
-  if (a.out_bf16)
-    hipLaunchKernelGGL((attn_prefill_kernel<D, QF32, false>), dim3(blocks), dim3(kWaves * 64),
-                       0, s, a);
-  else
-    hipLaunchKernelGGL((attn_prefill_kernel<D, QF32, true>), dim3(blocks), dim3(kWaves * 64),
-                       0, s, a);
-  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
+  return a.out_bf16 ? launch_s<D, QF32, false>(a, s) : launch_s<D, QF32, true>(a, s);
 }
 
 }  // namespace

@@ -99,6 +99,14 @@ struct PrefillArgs {
   float* lse_out;              // [B,S,Hq] or null
   int B, Hq, Hkv, D, T;
   int row_blocks;              // ceil(S * G / prefill_rows_per_block())
+  // Key splits: each row block's tiles are shared out among `splits`
+  // workgroups whose partials (normalised o, natural-log lse) go to ws_o /
+  // ws_lse; the last of them to arrive (ticket ws_cnt, one per row block,
+  // zero between launches) merges them.  splits = 1: no workspace.
+  int splits;
+  float* ws_o;                 // [teams, splits, rows per block, D]
+  float* ws_lse;               // [teams, splits, rows per block]
+  uint32_t* ws_cnt;            // [teams]
 };
 
 // Arguments of the packed QKV projection y[M,N] = x[M,K] W^T, passed by

@@ -17,7 +17,8 @@ from . import attn_decode, attn_decode_merge, attn_decode_splitk, decode_step, q
 from . import decode_step_ex, qkv_prologue_ex, rope_table
 from . import attn_decode_merge_multi, attn_decode_multi, attn_decode_splitk_multi, attn_prefill
 from . import splitk_multi_workspace_bytes
-from . import decode_step_multi, decode_step_multi_workspace_bytes, qkv_gemv
+from . import decode_step_multi, decode_step_multi_workspace_bytes, prefill_workspace_bytes
+from . import qkv_gemv
 
 BF16_NAN = 0x7FC0
 
@@ -37,21 +38,23 @@ class DeviceStep:
     """One decode step of workload ``w`` with all inputs resident in HBM.
 
     ``mode``: "fused" runs the whole step as one launch (gqa_decode_step, or
-    gqa_decode_step_multi with several tokens);
-    "split" runs the prologue, the split-K partition pass over
-    ``part_tokens``-row partitions (default: the workload's own size) and the
-    merge as three launches; "unsplit" runs the prologue and the unsplit
-    kernel; "prefill" runs the prologue and the matrix-core prefill kernel
-    (any number of tokens, causal or bidirectional as the workload says).  ``split`` (bool) is the older spelling of split/unsplit.  ``q_dtype`` selects the dtype attention reads q in when the
-    workload has no prologue.  ``poison`` writes bf16 NaN into every cache
-    row outside each sequence's attended range [lo, n) (rows the step must
-    never read); rows written by the prologue are left alone.
+    gqa_decode_step_multi with several tokens); "split" runs the prologue,
+    the split-K partition pass over ``part_tokens``-row partitions (default:
+    the workload's own size) and the merge as three launches; "unsplit" runs
+    the prologue and the unsplit kernel; "prefill" runs the prologue and the
+    matrix-core prefill kernel (any number of tokens, causal or
+    bidirectional as the workload says; ``splits`` > 1 shares each row
+    block's keys among that many workgroups).  ``split`` (bool) is the older
+    spelling of split/unsplit.  ``q_dtype`` selects the dtype attention reads
+    q in when the workload has no prologue.  ``poison`` writes bf16 NaN into
+    every cache row outside each sequence's attended range [lo, n) (rows the
+    step must never read); rows written by the prologue are left alone.
     """
 
     def __init__(self, w, device="cuda", split: bool = True,
                  part_tokens: Optional[int] = None, out_dtype: Optional[str] = None,
                  q_dtype: str = "bf16", poison: bool = False, scale: float = 0.0,
-                 mode: Optional[str] = None):
+                 mode: Optional[str] = None, splits: int = 1):
         self.w = w
         self.dev = torch.device(device)
         self.S = int(getattr(w, "S", 1))     # query tokens per sequence
@@ -60,6 +63,7 @@ class DeviceStep:
         if not self.causal and self.mode != "prefill":
             raise NotImplementedError("bidirectional attention runs on the prefill kernel")
         self.split = self.mode == "split"
+        self.splits = int(splits)           # prefill: key splits per row block
         self.part_tokens = int(part_tokens or w.part_tokens)
         self.scale = float(scale)
         od = out_dtype or w.out_dtype
@@ -110,6 +114,10 @@ class DeviceStep:
         self.out = torch.empty((w.B,) + tok + (w.Hq, w.D), dtype=self.out_dtype, device=d)
         self.lse = torch.empty((w.B,) + tok + (w.Hq,), dtype=torch.float32, device=d)
         self.ws = None
+        self.pws = None
+        if self.mode == "prefill" and self.splits > 1:
+            nb = prefill_workspace_bytes(w.B, self.S, w.Hq, w.Hkv, w.D, self.splits)
+            self.pws = torch.zeros(nb, dtype=torch.uint8, device=d)   # tickets start at 0
         if self.mode == "split":
             nb = splitk_multi_workspace_bytes(w.B, self.S, w.Hq, w.D, w.T, w.window,
                                               self.part_tokens)
@@ -141,7 +149,8 @@ class DeviceStep:
             out = self.out if self.out.dim() == 4 else self.out.unsqueeze(1)
             attn_prefill(q, self.k_cache, self.v_cache, self.lens, causal=self.causal,
                          window=w.window, scale=self.scale, out=out,
-                         lse_out=self.lse.reshape(w.B, self.S, w.Hq))
+                         lse_out=self.lse.reshape(w.B, self.S, w.Hq), splits=self.splits,
+                         workspace=self.pws)
             return
         if self.S > 1:
             if self.split:

@@ -381,6 +381,36 @@ int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
                      int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
 
 /*
+ * gqa_attn_prefill with the keys of every 128-row block shared out among
+ * `splits` workgroups (1..16; gqa_attn_prefill is splits = 1): the
+ * flash-decoding split of the fusedtok README's attention_decode applied to
+ * the prefill, for launches whose row blocks are too few -- or, under the
+ * causal mask, too unequal -- to keep every CU busy.  Each split writes its
+ * rows' partial (normalised o, lse) to `workspace`; the last split of a row
+ * block to finish merges them in split order (bit-identical reruns) and
+ * writes out / lse_out.  Results equal gqa_attn_prefill's up to rounding.
+ *   workspace  256-byte aligned, gqa_attn_prefill_workspace_bytes() bytes
+ *              (0 for splits = 1, when it may be NULL): partial o, partial
+ *              lse, then uint32 tickets, one per row block, which must be
+ *              zero before the first call and are left zero by every call
+ *              that completes.  Calls sharing a workspace must not overlap.
+ * Errors as for gqa_attn_prefill, plus GQA_ERR_VALUE (splits outside 1..16),
+ * GQA_ERR_NULL (splits > 1 without a workspace), GQA_ERR_WORKSPACE (too
+ * small) and GQA_ERR_ALIGN (workspace not 256-byte aligned).
+ * gqa_attn_prefill_default_splits suggests a split count for the current
+ * device: 2 when the launch has fewer row blocks than two per CU, else 1;
+ * it reads device attributes only and returns 1 when they cannot be read.
+ */
+size_t gqa_attn_prefill_workspace_bytes(int B, int S, int Hq, int Hkv, int D, int splits);
+int gqa_attn_prefill_default_splits(int B, int S, int Hq, int Hkv);
+int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,
+                           const uint16_t* k_cache, const uint16_t* v_cache,
+                           const int32_t* lens, int S, int causal, int window, float scale,
+                           int splits, void* workspace, size_t workspace_bytes,
+                           void* out, gqa_dtype_t out_dtype, float* lse_out,
+                           int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
+/*
  * Packed QKV projection of the decode batch: y[m][n] = sum_k x[m][k] w[n][k]
  * for m < M, n < N (the projection ahead of the prologue in the cutileGPT
  * README's runtime list, "packed QKV ... projections"; the weight layout

@@ -1,7 +1,7 @@
 """Seeded random sweep over the whole surface: the decode step (split,
 unsplit and fused), several tokens per sequence (split, unsplit and in one
-launch), the prefill (causal and bidirectional) and the packed QKV
-projection.  Each case draws its sizes
+launch), the prefill (causal and bidirectional, with and without key
+splits) and the packed QKV projection.  Each case draws its sizes
 from a fixed-seed generator -- group size, head dim, batch, cache length,
 lengths (ragged, some zero), window, partition size, token count, output
 dtype -- and is checked against the fp64 oracle at the same bars as the
@@ -35,7 +35,7 @@ def _decode_cases(n=60, seed=1234):
     return out
 
 
-def _tokens_cases(n=60, seed=4321, prefill=False, fused=False):
+def _tokens_cases(n=60, seed=4321, prefill=False, fused=False, splits=False):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -57,6 +57,8 @@ def _tokens_cases(n=60, seed=4321, prefill=False, fused=False):
                         causal=bool(rng.random() < 0.7) if prefill else True,
                         out=str(rng.choice(["f32", "bf16"])), P=int(rng.integers(16, 600)),
                         zero=bool(rng.random() < 0.3), seed=int(rng.integers(1 << 30))))
+        if splits:
+            out[-1]["splits"] = int(rng.integers(2, 7))
     return out
 
 
@@ -69,7 +71,7 @@ def _gemv_cases(n=30, seed=99):
 
 
 def _cid(c):
-    keys = ("mode", "G", "Hkv", "D", "B", "S", "T", "window", "out")
+    keys = ("mode", "G", "Hkv", "D", "B", "S", "T", "window", "out", "splits")
     return "-".join(f"{k}{c[k]}" for k in keys if k in c)
 
 
@@ -103,7 +105,7 @@ def _run(c):
     w = _workload(c)
     print(f"\n[case] sweep {c}", flush=True)
     ref = O.decode_step(w)
-    step = runner.DeviceStep(w, mode=c["mode"], part_tokens=c["P"])
+    step = runner.DeviceStep(w, mode=c["mode"], part_tokens=c["P"], splits=c.get("splits", 1))
     step.run()
     got = step.results()
     check_attention(got, ref, w.out_dtype, _cid(c))
@@ -135,6 +137,13 @@ def test_gpu_sweep_tokens_one_launch(c):
 @pytest.mark.gpu
 @pytest.mark.parametrize("c", _tokens_cases(n=60, seed=777, prefill=True), ids=_cid)
 def test_gpu_sweep_prefill(c):
+    _run(c)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("c", _tokens_cases(n=30, seed=2468, prefill=True, splits=True),
+                         ids=_cid)
+def test_gpu_sweep_prefill_split(c):
     _run(c)
 
 

@@ -1,5 +1,6 @@
-"""Prefill on the matrix cores (gqa_attn_prefill): S query tokens per
-sequence over the cache, causal or bidirectional (the fusedtok README's
+"""Prefill on the matrix cores (gqa_attn_prefill, and gqa_attn_prefill_split
+with the keys of each row block shared out among workgroups): S query tokens
+per sequence over the cache, causal or bidirectional (the fusedtok README's
 attention_prefill row), any S and any group size.  CPU: host-side validation
 of the C ABI.  GPU: against the fp64 oracle on seeded workloads -- fresh
 sequences and chunks at the end of a longer cache, fp32 q from the prologue
@@ -39,6 +40,31 @@ def test_prefill_validation(G):
     assert call(q=A16 + 8) == -6
     assert call(lse=A16 + 2) == -6
     assert call(Hq=30, Hkv=8) == -2          # Hq not a multiple of Hkv
+
+
+def test_prefill_split_validation(G):
+    ws = G.prefill_workspace_bytes(1, 64, 32, 8, 128, 4)
+    def call(splits=4, wsp=A16 * 16, wsb=ws, S=64):
+        return G.lib.gqa_attn_prefill_split(A16, 1, A16, A16, A16, S, 1, 0, 0.0, splits, wsp,
+                                            wsb, A16, 0, None, 1, 32, 8, 128, 4096, None)
+    assert call(splits=0) == -7
+    assert call(splits=17) == -7
+    assert call(wsp=None) == -1                  # splits > 1 needs a workspace
+    assert call(wsb=ws - 1) == -4
+    assert call(wsp=A16 * 16 + 16) == -6         # workspace 256-byte aligned
+    assert call(S=0) == -2
+
+
+def test_prefill_split_workspace(G):
+    # rows per KV head = S * G = 300 * 4 -> 10 row blocks of 128; teams = B * Hkv * 10
+    B, S, Hq, Hkv, D, sp = 2, 300, 32, 8, 128, 4
+    teams = B * Hkv * 10
+    part = teams * sp * 128
+    r256 = lambda x: x + (-x) % 256
+    want = r256(part * D * 4) + r256(part * 4) + teams * 4
+    assert G.prefill_workspace_bytes(B, S, Hq, Hkv, D, sp) == want
+    assert G.prefill_workspace_bytes(B, S, Hq, Hkv, D, 1) == 0
+    assert 1 <= G.prefill_default_splits(1, 1024, 32, 8) <= 8
 
 
 def _step(w, **kw):
@@ -219,3 +245,72 @@ def test_gpu_prefill_full_size_sampled():
         err = float(np.max(np.abs(got["out"][:, s] - ro)))
         assert err <= OUT_TOL[w.out_dtype], (s, err)
         assert float(np.max(np.abs(got["lse"][:, s] - rl))) <= LSE_TOL, s
+
+
+# (config, overrides, key splits, what the case covers)
+SPLIT_CASES = [
+    ("7f", dict(S=1024, L=1024), 4, "fresh causal S=1024 (the fusedtok row's shape)"),
+    ("7f", dict(S=300, L=300), 3, "fresh, splits not a power of two, ragged row block"),
+    ("7f", dict(S=200, L=260, causal=False), 2, "fresh bidirectional, T > S"),
+    ("7", dict(B=2, L=700, S=300), 8, "chunk with bf16 q, bf16 out"),
+    ("7", dict(B=2, L=500, S=64, Hq=16, Hkv=2, out_dtype="f32"), 16,
+     "more splits than tiles for most row blocks, fp32 out"),
+    ("5", dict(B=2, L=2000, window=300, S=200), 4, "window per token, QK-norm, prologue"),
+    ("1", dict(S=50), 2, "D=64"),
+    ("3", dict(B=4, L=1200, S=96, lmin=96), 5, "ragged lengths"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over,splits,what", SPLIT_CASES,
+                         ids=[f"s{i}" for i in range(len(SPLIT_CASES))])
+def test_gpu_prefill_split(name, over, splits, what):
+    """Key splits with the last-arriver merge against the fp64 oracle; the
+    tickets are left at zero."""
+    _gpu()
+    from gqa_attention_kv_amd import runner
+    from test_gpu_parity import check_attention
+    w = W.make(name, **over)
+    print(f"\n[case] prefill split={splits} cfg={name} {over} ({what})", flush=True)
+    ref = O.decode_step(w)
+    step = runner.DeviceStep(w, mode="prefill", splits=splits)
+    step.run()
+    got = step.results()
+    check_attention(got, ref, w.out_dtype, f"prefill split {splits} {name} {over}")
+    import torch
+    teams = w.B * w.Hkv * ((w.S * (w.Hq // w.Hkv) + 127) // 128)
+    tickets = step.pws[-4 * teams:].view(torch.int32)    # the workspace's last words
+    assert int(tickets.abs().sum()) == 0, "tickets not reset"
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_split_poisoned_and_empty():
+    """Splits with NaN outside every token's rows and sequences whose first
+    tokens (or all tokens) see no row: out = 0, lse = -inf there."""
+    _gpu()
+    from test_gpu_parity import check_attention
+    w = W.make("7", B=3, L=600, S=128, window=200)
+    w.lens[:] = np.array([100, 0, 600], np.int32)
+    print("\n[case] prefill split poisoned / empty", flush=True)
+    ref = O.decode_step(w)
+    got = _step(w, poison=True, splits=4)
+    check_attention(got, ref, w.out_dtype, "prefill split poisoned")
+    assert np.all(got["out"][1] == 0) and np.all(got["lse"][1] == -math.inf)
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_split_reruns_and_unsplit():
+    """Reruns with splits are bit-identical; the split result matches the
+    unsplit kernel within the parity bar."""
+    _gpu()
+    from gqa_attention_kv_amd import runner
+    w = W.make("7f", S=512, L=512, out_dtype="f32")
+    step = runner.DeviceStep(w, mode="prefill", splits=4)
+    step.run()
+    r1 = step.results()
+    step.run()
+    r2 = step.results()
+    assert np.array_equal(r1["out"], r2["out"]) and np.array_equal(r1["lse"], r2["lse"])
+    one = _step(w)
+    assert float(np.max(np.abs(one["out"] - r1["out"]))) <= 1e-3
+    assert float(np.max(np.abs(one["lse"] - r1["lse"]))) <= 1e-3
