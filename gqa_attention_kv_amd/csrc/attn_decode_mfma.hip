@@ -1,10 +1,11 @@
-// Single-token GQA decode attention on gfx950 matrix cores, in three modes
-// that share one body:
+// GQA decode attention on gfx950 matrix cores, one token per sequence (or
+// a few: G * S <= 16 (token, head) rows per KV head), in three modes that
+// share one body:
 //   Final  one workgroup per (sequence, KV head) writes the output directly;
 //   Split  one workgroup per (partition, KV head, sequence) writes the
 //          partition's (o_k, lse_k) for the log-sum-exp merge;
 //   Step   the whole decode step in one launch: per-head QK-RMSNorm and NeoX
-//          RoPE of the new query, the K/V append, the split-K pass, and the
+//          RoPE of the new queries, the K/V append, the split-K pass, and the
 //          merge, done by the last workgroup of each (sequence, KV head) to
 //          finish.
 //
@@ -1036,42 +1037,63 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   }
   __syncthreads();
 
-  // Step with a single partition writes the final output like Final.
+  // Step with a single partition writes the final output like Final.  Each
+  // thread combines four consecutive d of one column (one 16-byte LDS read
+  // per wave, one 16-byte store).
   const bool write_final = MODE == Mode::Final || (MODE == Mode::Step && num_parts == 1);
-  for (int idx = threadIdx.x; idx < CT * D; idx += NW * 64) {
-    const int h = idx / D;          // column
-    const int d = idx % D;
+  constexpr int Q4 = D / 4;
+  // Step: this team's partials, rows head0 .. head0 + span - 1 of ws_o
+  // (column c is row head0 + (orow(c) - head0)), through one buffer
+  // resource; the host keeps them below 2 GiB.
+  const int64_t span = orow(NC - 1) - head0 + 1;
+  const __amdgpu_buffer_rsrc_t Wrs =
+      MODE == Mode::Step
+          ? make_rsrc(a.ws_o + head0 * num_parts * D, (uint32_t)((size_t)span * num_parts * D * 4))
+          : make_rsrc(nullptr, 0u);
+  for (int idx = threadIdx.x; idx < CT * Q4; idx += NW * 64) {
+    const int h = idx / Q4;         // column
+    const int d = 4 * (idx % Q4);
     if (h >= NC) break;             // columns only grow with idx
     const int64_t oh = orow(h);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
     const float Ms = (M == -INFINITY) ? 0.0f : M;
-    float L = 0.0f, A = 0.0f;
+    float L = 0.0f;
+    float4 A = float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - Ms);
+      const float4 ow = *reinterpret_cast<const float4*>(&sm_o[w][h][d]);
       L += sm_l[w][h] * f;
-      A += sm_o[w][h][d] * f;
+      A.x = fmaf(ow.x, f, A.x);
+      A.y = fmaf(ow.y, f, A.y);
+      A.z = fmaf(ow.z, f, A.z);
+      A.w = fmaf(ow.w, f, A.w);
     }
     const bool any = L > 0.0f;
-    const float ov = any ? A / L : 0.0f;
+    const float inv = any ? 1.0f / L : 0.0f;
+    const float4 ov = float4{A.x * inv, A.y * inv, A.z * inv, A.w * inv};
     const float lse = any ? (M + log2f(L)) * kLn2 : -INFINITY;
     if (write_final) {
       if (a.out_bf16)
-        reinterpret_cast<uint16_t*>(a.out)[oh * D + d] = __builtin_bit_cast(uint16_t, (__bf16)ov);
-      else reinterpret_cast<float*>(a.out)[oh * D + d] = ov;
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + oh * D + d) =
+            make_uint2(pack_bf16(ov.x, ov.y), pack_bf16(ov.z, ov.w));
+      else
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oh * D + d) = ov;
       if (d == 0 && a.lse_out != nullptr) a.lse_out[oh] = lse;
     } else if (MODE == Mode::Split) {
-      if (any) a.ws_o[(oh * num_parts + part) * D + d] = ov;
+      if (any) *reinterpret_cast<float4*>(a.ws_o + (oh * num_parts + part) * D + d) = ov;
       if (d == 0) a.ws_lse[oh * num_parts + part] = lse;
     } else {
-      // Agent-scope stores write through to the coherence point, so the
-      // merging workgroup (possibly on another XCD) can read them without
-      // any L2 writeback.
+      // Write-through (sc1) stores reach the coherence point, so the merging
+      // workgroup (possibly on another XCD) can read them without any L2
+      // writeback.
+      constexpr int kCoherent = 0x10;
       if (any)
-        __hip_atomic_store(a.ws_o + (oh * num_parts + part) * D + d, ov,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4_t, ov), Wrs,
+            (uint32_t)((((oh - head0) * num_parts + part) * D + d) * 4), 0, kCoherent);
       if (d == 0)
         __hip_atomic_store(a.ws_lse + oh * num_parts + part, lse, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);

@@ -35,7 +35,7 @@ struct PrologueArgs {
 // Arguments of the attention kernel in all three modes, passed by value.
 struct KernelArgs {
   // query [B,S,Hq,D]: sequences q_bstride elements apart, tokens q_sstride
-  // apart, heads dense (Step: S = 1)
+  // apart, heads dense
   const void* q;
   int64_t q_bstride;
   int64_t q_sstride;
@@ -48,15 +48,15 @@ struct KernelArgs {
   float qscale;                // softmax scale * log2(e)
   int part_tokens;             // Split / Step
   int num_parts;
-  float* ws_lse;               // [B,Hq,num_parts]
-  float* ws_o;                 // [B,Hq,num_parts,D]
+  float* ws_lse;               // [B,S,Hq,num_parts]
+  float* ws_o;                 // [B,S,Hq,num_parts,D]
   uint32_t* ws_cnt;            // Step: [B,Hkv] arrival tickets, zero between launches
   void* out;                   // Final / Step
   int out_bf16;
   float* lse_out;              // may be null
   int B, Hq, Hkv, D, T;
   // Step only: the fused prologue
-  const void* k_new;
+  const void* k_new;           // [B,S,Hkv,D]: sequences kv_bstride apart, tokens Hkv*D
   const void* v_new;
   int64_t kv_bstride;
   const float* wq;             // null: no QK-norm
@@ -65,8 +65,8 @@ struct KernelArgs {
   int rope;                    // 0: no RoPE
   int rope_interleaved;        // pairs (2i, 2i+1) instead of (i, i+D/2)
   float rope_mscale;           // magnitude factor of the rotated vectors
-  const int32_t* pos;
-  float* q_out;                // may be null
+  const int32_t* pos;          // token s at position (and cache row) pos[b] + s
+  float* q_out;                // [B,S,Hq,D] or null
   uint16_t* k_cache_w;         // same buffers as k_cache / v_cache
   uint16_t* v_cache_w;
   double inv_freq_rev[kMaxHalfDim];   // frequency of pair i / (2 pi), float64
