@@ -706,9 +706,13 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       for (int c = 0; c < KC; ++c) qraw[c].unpack(qf[c]);
       apply_qnorm();
       if (rope) {
+        // Entry e = thread + 64 NW k is pair e % HALF = this lane's pair fi
+        // (HALF divides 64), whose frequency was loaded before the tiles: a
+        // load here would wait behind them.
+        static_assert(64 % HALF == 0, "pair of a table entry");
         for (int e = threadIdx.x; e < S * HALF; e += NW * 64) {
           const int st = e / HALF, i = e % HALF;
-          const double rev = (double)((int64_t)p + st) * a.inv_freq_rev[i];
+          const double rev = (double)((int64_t)p + st) * inv_rev;
           double sd, cd;
           sincos_pi_f64((rev - rint(rev)) * 6.283185307179586, &sd, &cd);
           ang[st][i] = (float)cd * a.rope_mscale;
