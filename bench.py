@@ -87,11 +87,14 @@ def _parse():
                     help="also time a plain device copy of this many MiB")
     ap.add_argument("--part-tokens", type=int, default=0,
                     help="override the workload's split-K partition size")
-    ap.add_argument("--mode", default="fused", choices=["fused", "split", "prefill"],
+    ap.add_argument("--mode", default="fused",
+                    choices=["fused", "split", "prefill", "prefill_step"],
                     help="fused: the whole step as one launch (default); split: "
                          "prologue, split-K pass and merge as three launches; prefill: "
-                         "prologue and the matrix-core prefill kernel (the default "
-                         "for the prefill workloads)")
+                         "prologue and the matrix-core prefill kernel; prefill_step: "
+                         "the K/V append and the prefill kernel rotating q itself "
+                         "(gqa_prefill_step, two launches timed together; the default "
+                         "for the prefill workloads with a prologue)")
     ap.add_argument("--splits", type=int, default=0,
                     help="prefill: key splits per row block (0: the library's "
                          "suggestion for the device, gqa_attn_prefill_default_splits)")
@@ -485,7 +488,10 @@ def main():
     mode = args.mode
     splits = 1
     if args.workload in PREFILL_WORKLOADS:
-        mode = "prefill"
+        # with a prologue, the K/V append and the prefill kernel that rotates
+        # q itself (two launches) unless --mode prefill asks for the
+        # standalone prologue before it
+        mode = "prefill" if args.mode == "prefill" or w.pos is None else "prefill_step"
         # key splits: the library's suggestion for this device unless given
         splits = args.splits or prefill_default_splits(w.B, w.S, w.Hq, w.Hkv)
     step = DeviceStep(w, device=dev, mode=mode, splits=splits)
@@ -508,8 +514,8 @@ def main():
         sweep()
         rec = (lambda k: timer.record(4 * i + k, stream)) if i is not None else (lambda k: None)
         rec(0)
-        if mode == "fused":      # one launch: bracket it with one event pair only
-            step.fused()
+        if mode in ("fused", "prefill_step"):   # one call: one event pair
+            step.run()
             rec(3)
             return
         step.prologue()
@@ -529,7 +535,7 @@ def main():
     wall = time.perf_counter() - wall0
 
     step_ms = [timer.ms(4 * i, 4 * i + 3) for i in range(args.steps)]
-    if mode == "fused":      # one kernel: the step is the dominant kernel
+    if mode in ("fused", "prefill_step"):   # the call is the dominant kernel('s launches)
         pro_ms = merge_ms = [0.0]
         attn_ms = step_ms
     else:
@@ -541,8 +547,8 @@ def main():
     mean_attn = statistics.fmean(attn_ms)
 
     def run_once():
-        if mode == "fused":
-            step.fused()
+        if mode in ("fused", "prefill_step"):
+            step.run()
         else:
             step.prologue()
             step.attention()
@@ -557,18 +563,19 @@ def main():
 
     if args.no_cpu_baseline:
         cpu = None
-    elif mode == "prefill":
+    elif mode in ("prefill", "prefill_step"):
         cpu = _cpu_baseline_prefill(w, args.cpu_seconds)
     else:
         cpu = _cpu_baseline(w, args.cpu_seconds)
 
     traffic = _traffic(args.workload)
-    if mode == "prefill":
+    if mode in ("prefill", "prefill_step"):
         flops = workloads.attention_flops(w)
         tflops = flops / (mean_attn * 1e-3) / 1e12
         roofline = {
             "bound": "mfma",
-            "kernel": PREFILL_KERNEL,
+            "kernel": PREFILL_KERNEL + (" (with the K/V append launch)"
+                                        if mode == "prefill_step" else ""),
             "achieved": round(tflops, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
@@ -599,7 +606,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if mode == "prefill" else "f32",
+        "dtype": "bf16" if mode in ("prefill", "prefill_step") else "f32",
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_NAMES[args.workload],
@@ -607,7 +614,7 @@ def main():
             "query_tokens": w.S,
             "window": w.window, "part_tokens": w.part_tokens, "out_dtype": w.out_dtype,
             "path": mode,
-            **({"key_splits": splits} if mode == "prefill" else {}),
+            **({"key_splits": splits} if mode in ("prefill", "prefill_step") else {}),
             "prologue": ("qk_rmsnorm+rope+append" if w.w_q is not None else
                          "rope+append") if w.pos is not None else "none",
             "kv_bytes_per_step": kvb,

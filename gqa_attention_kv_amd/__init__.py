@@ -11,7 +11,8 @@ Functions follow the C entry points' names without the ``gqa_`` prefix:
 ``attn_decode_splitk``, ``attn_decode_merge``, ``attn_decode_multi``,
 ``attn_decode_splitk_multi``, ``attn_decode_merge_multi``, ``decode_step``,
 ``decode_step_ex``, ``decode_step_multi``, ``attn_prefill`` (with key
-``splits``: ``prefill_workspace_bytes``, ``prefill_default_splits``), ``qkv_gemv``,
+``splits``: ``prefill_workspace_bytes``, ``prefill_default_splits``),
+``prefill_step``, ``qkv_gemv``,
 ``rope_table``, ``splitk_workspace_bytes``, ``splitk_multi_workspace_bytes``,
 ``decode_step_workspace_bytes``, ``decode_step_multi_workspace_bytes``,
 ``num_partitions``.
@@ -33,6 +34,7 @@ __all__ = [
     "attn_decode_multi", "attn_decode_splitk_multi", "attn_decode_merge_multi",
     "splitk_multi_workspace_bytes", "decode_step_multi", "decode_step_multi_workspace_bytes",
     "attn_prefill", "qkv_gemv", "prefill_workspace_bytes", "prefill_default_splits",
+    "prefill_step",
     "F32", "BF16", "SYMBOLS", "ROPE_NEOX", "ROPE_INTERLEAVED", "ROPE_KINDS",
 ]
 
@@ -88,6 +90,9 @@ SYMBOLS = {
                               _i, _p]),
     "gqa_qkv_gemv": (_i, [_p, _i64, _p, _i64, _p, _i, _i64, _i, _i, _i, _p]),
     "gqa_attn_prefill_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "gqa_prefill_step": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p, _i,
+                              _p, _p, _p, _i, _i, _f, _i, _p, _sz, _p, _i, _p, _p,
+                              _i, _i, _i, _i, _i, _p]),
     "gqa_attn_prefill_default_splits": (_i, [_i, _i, _i, _i]),
     "gqa_attn_prefill_split": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _f, _i, _p, _sz, _p, _i,
                                     _p, _i, _i, _i, _i, _i, _p]),
@@ -430,6 +435,71 @@ def attn_prefill(q, k_cache, v_cache, lens, causal: bool = True, window: int = 0
         1 if causal else 0, int(window), float(scale), int(splits),
         _ptr(workspace) if splits > 1 else None, nbytes, _ptr(out), _dtype_code(out, "out"),
         _ptr(lse_out), B, Hq, Hkv, D, T, _stream(dev)))
+    return out
+
+
+def prefill_step(q, k_new, v_new, pos, k_cache, v_cache, lens, causal: bool = True,
+                 window: int = 0, scale: float = 0.0, inv_freq=None, rope_mscale: float = 1.0,
+                 rope_layout="neox", q_norm_w=None, k_norm_w=None, eps: float = 1e-6,
+                 splits: int = 1, workspace=None, out=None, out_dtype=torch.float32,
+                 lse_out=None, q_out=None):
+    """The prefill with its prologue (gqa_prefill_step): q [B,S,Hq,D], k_new
+    and v_new [B,S,Hkv,D] (tokens and heads dense, a batch stride of their
+    own) in float32 or bfloat16; token s is appended at row pos[b] + s and
+    the attention kernel normalises and rotates q itself.  ``inv_freq``:
+    host float64 [D/2] rotary table or None.  Returns out [B,S,Hq,D]."""
+    dev, B, S, Hq, Hkv, D, T = _multi_common(q, k_cache, v_cache, lens)
+    code = _dtype_code(q, "q")
+    for t, w, h in ((q, "q", Hq), (k_new, "k_new", Hkv), (v_new, "v_new", Hkv)):
+        _dev(t, w, dev)
+        if t.dtype != q.dtype:
+            raise TypeError("q, k_new and v_new must share a dtype")
+        if (tuple(t.shape) != (B, S, h, D) or t.stride(3) != 1 or t.stride(2) != D
+                or t.stride(1) != h * D):
+            raise ValueError(f"{w}: expected [B,S,{h},D] with contiguous tokens and heads")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must share a batch stride")
+    for t, w in ((pos, "pos"),):
+        _dev(t, w, dev)
+        if t.dtype != torch.int32 or tuple(t.shape) != (B,):
+            raise ValueError("pos must be int32 [B]")
+        _contig(t, w)
+    for w, nm in ((q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if w is not None:
+            _dev(w, nm, dev)
+            if w.dtype != torch.float32 or tuple(w.shape) != (D,):
+                raise ValueError(f"{nm} must be float32 [D]")
+            _contig(w, nm)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=dev)
+    _dev(out, "out", dev)
+    _contig(out, "out")
+    if tuple(out.shape) != (B, S, Hq, D):
+        raise ValueError("out must be [B,S,Hq,D]")
+    if lse_out is not None:
+        _lse_check(lse_out.reshape(B, S * Hq), B, S * Hq, dev)
+    if q_out is not None:
+        _dev(q_out, "q_out", dev)
+        _contig(q_out, "q_out")
+        if q_out.dtype != torch.float32 or tuple(q_out.shape) != (B, S, Hq, D):
+            raise ValueError("q_out must be float32 [B,S,Hq,D]")
+    nbytes = 0
+    if splits > 1:
+        need = prefill_workspace_bytes(B, S, Hq, Hkv, D, splits)
+        if workspace is None:
+            workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+        _dev(workspace, "workspace", dev)
+        _contig(workspace, "workspace")
+        nbytes = workspace.numel() * workspace.element_size()
+    f = _host_table(inv_freq, D)
+    _check(lib.gqa_prefill_step(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0), k_new.stride(0),
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), None if f is None else f.ctypes.data,
+        float(rope_mscale), _layout_code(rope_layout), _ptr(pos), int(S),
+        _ptr(k_cache), _ptr(v_cache), _ptr(lens), 1 if causal else 0, int(window),
+        float(scale), int(splits), _ptr(workspace) if splits > 1 else None, nbytes,
+        _ptr(out), _dtype_code(out, "out"), _ptr(lse_out), _ptr(q_out), B, Hq, Hkv, D, T,
+        _stream(dev)))
     return out
 
 

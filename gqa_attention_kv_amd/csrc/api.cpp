@@ -295,7 +295,7 @@ int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,
       workspace_bytes < gqa_attn_prefill_workspace_bytes(B, S, Hq, Hkv, D, splits))
     return GQA_ERR_WORKSPACE;
   gqa::PrefillArgs a{};
-  a.q = q; a.in_bf16 = q_dtype == GQA_BF16;
+  a.q = q; a.q_bstride = (int64_t)S * Hq * D; a.in_bf16 = q_dtype == GQA_BF16;
   a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens;
   a.S = S; a.causal = causal; a.window = window;
   a.qscale = softmax_qscale(scale, D);
@@ -311,6 +311,88 @@ int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,
     a.ws_cnt = reinterpret_cast<uint32_t*>(ws + align256(part * D * sizeof(float)) +
                                            align256(part * sizeof(float)));
   }
+  return gqa::launch_attn_prefill(a, stream);
+}
+
+int gqa_prefill_step(const void* q, const void* k_new, const void* v_new,
+                     gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                     const float* q_norm_w, const float* k_norm_w, float eps,
+                     const double* inv_freq, double rope_mscale, int rope_layout,
+                     const int32_t* pos, int S,
+                     uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                     int causal, int window, float scale, int splits,
+                     void* workspace, size_t workspace_bytes,
+                     void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
+  if (!q || !k_new || !v_new || !pos || !k_cache || !v_cache || !lens || !out)
+    return GQA_ERR_NULL;
+  if ((q_norm_w == nullptr) != (k_norm_w == nullptr)) return GQA_ERR_NULL;
+  int rc = check_shapes(B, Hq, Hkv, D, T);
+  if (rc) return rc;
+  if (S < 1) return GQA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return GQA_ERR_VALUE;
+  if (splits < 1 || splits > 16) return GQA_ERR_VALUE;
+  if (splits > 1 && !workspace) return GQA_ERR_NULL;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
+  if ((rc = check_rope(inv_freq, rope_mscale, rope_layout, D))) return rc;
+  if (q_bstride < (int64_t)S * Hq * D || kv_bstride < (int64_t)S * Hkv * D) return GQA_ERR_SHAPE;
+  if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
+  if ((int64_t)B * S > kMaxWorkgroups) return GQA_ERR_SHAPE;
+  const uintptr_t ea = in_dtype == GQA_BF16 ? 2 : 4;
+  // q rows are read as 16-byte vectors: the batch stride keeps that alignment
+  if (!aligned(q, 16) || (q_bstride * (int64_t)ea) % 16 != 0 || !aligned(k_new, ea) ||
+      !aligned(v_new, ea) || !aligned(q_norm_w, 16) || !aligned(k_norm_w, 4) ||
+      !aligned(pos, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(lens, 4) || !aligned(out, 16) || !aligned(lse_out, 4) || !aligned(q_out, 16) ||
+      !aligned(workspace, 256))
+    return GQA_ERR_ALIGN;
+  const int64_t rows = (int64_t)S * (Hq / Hkv);
+  if (rows > INT32_MAX / 2 || (int64_t)B * S * Hq > kMaxIndex / D) return GQA_ERR_SHAPE;
+  const int per = gqa::prefill_rows_per_block();
+  const int64_t row_blocks = (rows + per - 1) / per;
+  if ((int64_t)B * Hkv * row_blocks * splits > kMaxWorkgroups) return GQA_ERR_SHAPE;
+  if (splits > 1 &&
+      workspace_bytes < gqa_attn_prefill_workspace_bytes(B, S, Hq, Hkv, D, splits))
+    return GQA_ERR_WORKSPACE;
+  // 1: the K/V append of the S tokens (the prologue kernel on the K/V head
+  // vectors only)
+  gqa::PrologueArgs pa{};
+  pa.q = q; pa.k_new = k_new; pa.v_new = v_new; pa.in_bf16 = in_dtype == GQA_BF16;
+  pa.q_bstride = q_bstride; pa.kv_bstride = kv_bstride;
+  pa.q_norm_w = q_norm_w; pa.k_norm_w = k_norm_w; pa.eps = eps;
+  pa.rope = inv_freq != nullptr;
+  pa.rope_interleaved = rope_layout == GQA_ROPE_INTERLEAVED;
+  pa.rope_mscale = (float)rope_mscale;
+  pa.pos = pos; pa.S = S; pa.q_out = nullptr; pa.k_cache = k_cache; pa.v_cache = v_cache;
+  pa.B = B; pa.Hq = Hq; pa.Hkv = Hkv; pa.D = D; pa.T = T; pa.kv_only = 1;
+  if (pa.rope)
+    for (int i = 0; i < D / 2; ++i) pa.inv_freq_rev[i] = inv_freq[i] / 6.283185307179586476925;
+  if ((rc = gqa::launch_prologue(pa, stream))) return rc;
+  // 2: the attention, which normalises and rotates q itself
+  gqa::PrefillArgs a{};
+  a.q = q; a.q_bstride = q_bstride; a.in_bf16 = in_dtype == GQA_BF16;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.lens = lens;
+  a.S = S; a.causal = causal; a.window = window;
+  a.qscale = softmax_qscale(scale, D);
+  a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
+  a.row_blocks = (int)row_blocks;
+  a.splits = splits;
+  if (splits > 1) {
+    const size_t part = (size_t)B * Hkv * row_blocks * splits * per;
+    char* ws = static_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(ws);
+    a.ws_lse = reinterpret_cast<float*>(ws + align256(part * D * sizeof(float)));
+    a.ws_cnt = reinterpret_cast<uint32_t*>(ws + align256(part * D * sizeof(float)) +
+                                           align256(part * sizeof(float)));
+  }
+  a.pro = 1;
+  a.wq = q_norm_w; a.eps = eps;
+  a.rope = pa.rope; a.rope_interleaved = pa.rope_interleaved; a.rope_mscale = pa.rope_mscale;
+  a.pos = pos; a.q_out = q_out;
+  for (int i = 0; i < D / 2; ++i) a.inv_freq_rev[i] = pa.inv_freq_rev[i];
   return gqa::launch_attn_prefill(a, stream);
 }
 

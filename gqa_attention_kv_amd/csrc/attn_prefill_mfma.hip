@@ -97,11 +97,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// SPLIT: the launch shares each row block's keys among a.splits > 1
-// workgroups (the instances without it keep the plain loop and epilogue).
-template <int D, bool QF32, bool PLO, bool SPLIT>
+// QM: how q arrives -- 0 bf16 as given, 1 float32 as given, 2 / 3 raw
+// bf16 / float32 that the kernel normalises and rotates itself (the q half
+// of the prologue).  SPLIT: the launch shares each row block's keys among
+// a.splits > 1 workgroups (the instances without it keep the plain loop and
+// epilogue).
+template <int D, int QM, bool PLO, bool SPLIT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void
 attn_prefill_kernel(const PrefillArgs a) {
+  constexpr bool QF32 = QM != 0;       // q carried as bf16 hi + lo
+  constexpr bool PRO = QM >= 2;
   constexpr int KC = D / 32;            // QK slices
   constexpr int VB = D / 16;            // PV column blocks
   constexpr int KROW = D * 2 + 16;      // K row pitch in LDS (conflict-free operand reads)
@@ -187,35 +192,156 @@ attn_prefill_kernel(const PrefillArgs a) {
   // q operands (B of the QK calls): lane holds row n of block j, elements
   // 32c + 8 k4 .. + 8.
   u32x4_t qh[2][KC], ql[2][KC];
+  if constexpr (!PRO) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = r0 + kRowsPerWave * wave + 16 * j + n;
-    const bool ok = row < SG;
-    const int t = ok ? row / G : 0, h = ok ? row % G : 0;
-    const int64_t qoff = (((int64_t)b * S + t) * Hq + (int64_t)g * G + h) * D;
+    for (int j = 0; j < 2; ++j) {
+      const int row = r0 + kRowsPerWave * wave + 16 * j + n;
+      const bool ok = row < SG;
+      const int t = ok ? row / G : 0, h = ok ? row % G : 0;
+      const int64_t qoff = (int64_t)b * a.q_bstride + ((int64_t)t * Hq + (int64_t)g * G + h) * D;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int e = 32 * c + 8 * k4;
-      if constexpr (QF32) {
-        const float* p = reinterpret_cast<const float*>(a.q) + qoff + e;
-        float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (ok) {
+      for (int c = 0; c < KC; ++c) {
+        const int e = 32 * c + 8 * k4;
+        if constexpr (QF32) {
+          const float* p = reinterpret_cast<const float*>(a.q) + qoff + e;
+          float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (ok) {
+            const float4 u = *reinterpret_cast<const float4*>(p);
+            const float4 v = *reinterpret_cast<const float4*>(p + 4);
+            f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+            f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+          }
+          bf16x8_t hv, lv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            hv[i] = (__bf16)f[i];
+            lv[i] = (__bf16)(f[i] - (float)hv[i]);
+          }
+          qh[j][c] = __builtin_bit_cast(u32x4_t, hv);
+          ql[j][c] = __builtin_bit_cast(u32x4_t, lv);
+        } else {
+          const uint16_t* p = reinterpret_cast<const uint16_t*>(a.q) + qoff + e;
+          qh[j][c] = ok ? *reinterpret_cast<const u32x4_t*>(p) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  } else {
+    // The q half of the prologue for this lane's rows: RMSNorm over D (the
+    // row's four lanes k4 hold a quarter each), then RoPE of token t at
+    // position pos[b] + t -- the phase formed and reduced to [-1/2, 1/2]
+    // turns in float64, sin and cos from v_sin_f32 / v_cos_f32, which take
+    // turns.  NeoX pairs (i, i + D/2) sit in slices c and c + KC/2 of the
+    // same lane; interleaved pairs (2i, 2i + 1) side by side in one slice.
+    float f[2][KC][8];
+    bool ok[2];
+    int tk[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = r0 + kRowsPerWave * wave + 16 * j + n;
+      ok[j] = row < SG;
+      tk[j] = ok[j] ? row / G : 0;
+      const int h = ok[j] ? row % G : 0;
+      const int64_t qoff =
+          (int64_t)b * a.q_bstride + ((int64_t)tk[j] * Hq + (int64_t)g * G + h) * D;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int e = 32 * c + 8 * k4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[j][c][i] = 0.0f;
+        if (!ok[j]) continue;
+        if constexpr (QM == 3) {
+          const float* p = reinterpret_cast<const float*>(a.q) + qoff + e;
           const float4 u = *reinterpret_cast<const float4*>(p);
           const float4 v = *reinterpret_cast<const float4*>(p + 4);
-          f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
-          f[4] = v.x; f[5] = v.y; f[6] = v.z; f[7] = v.w;
+          f[j][c][0] = u.x; f[j][c][1] = u.y; f[j][c][2] = u.z; f[j][c][3] = u.w;
+          f[j][c][4] = v.x; f[j][c][5] = v.y; f[j][c][6] = v.z; f[j][c][7] = v.w;
+        } else {
+          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(
+              reinterpret_cast<const uint16_t*>(a.q) + qoff + e);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[j][c][2 * i] = __uint_as_float(w[i] << 16);
+            f[j][c][2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+          }
         }
+      }
+    }
+    if (a.wq != nullptr) {
+      float rs[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ss = fmaf(f[j][c][i], f[j][c][i], ss);
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        rs[j] = ok[j] ? 1.0f / sqrtf(ss / (float)D + a.eps) : 0.0f;
+      }
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const float4 u = *reinterpret_cast<const float4*>(a.wq + 32 * c + 8 * k4);
+        const float4 v = *reinterpret_cast<const float4*>(a.wq + 32 * c + 8 * k4 + 4);
+        const float wv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[j][c][i] = f[j][c][i] * rs[j] * wv[i];
+      }
+    }
+    if (a.rope) {
+      const float ms = a.rope_mscale;
+      const int64_t p0 = a.pos[b];
+      // element (c, i) of row j and its partner (c2, i2) rotate by pair
+      // `pair` (indices stay compile-time: one loop per layout)
+      auto rotate = [&](int c, int i, int c2, int i2, int pair) {
+        const double fr_pair = a.inv_freq_rev[pair];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const double rev = (double)(p0 + tk[j]) * fr_pair;
+          const float fr = (float)(rev - rint(rev));
+          const float cs = __builtin_amdgcn_cosf(fr) * ms, sn = __builtin_amdgcn_sinf(fr) * ms;
+          const float a1 = f[j][c][i], a2 = f[j][c2][i2];
+          f[j][c][i] = a1 * cs - a2 * sn;
+          f[j][c2][i2] = a2 * cs + a1 * sn;
+        }
+      };
+      if (a.rope_interleaved) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) rotate(c, i, c, i + 1, 16 * c + 4 * k4 + i / 2);
+      } else {
+#pragma unroll
+        for (int c = 0; c < KC / 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) rotate(c, i, c + KC / 2, i, 32 * c + 8 * k4 + i);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (a.q_out != nullptr && sp == 0 && ok[j]) {
+        const int row = r0 + kRowsPerWave * wave + 16 * j + n;
+        float* qo = a.q_out + (((int64_t)b * S + tk[j]) * Hq + (int64_t)g * G + row % G) * D;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          *reinterpret_cast<float4*>(qo + 32 * c + 8 * k4) =
+              float4{f[j][c][0], f[j][c][1], f[j][c][2], f[j][c][3]};
+          *reinterpret_cast<float4*>(qo + 32 * c + 8 * k4 + 4) =
+              float4{f[j][c][4], f[j][c][5], f[j][c][6], f[j][c][7]};
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
         bf16x8_t hv, lv;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          hv[i] = (__bf16)f[i];
-          lv[i] = (__bf16)(f[i] - (float)hv[i]);
+          hv[i] = (__bf16)f[j][c][i];
+          lv[i] = (__bf16)(f[j][c][i] - (float)hv[i]);
         }
         qh[j][c] = __builtin_bit_cast(u32x4_t, hv);
         ql[j][c] = __builtin_bit_cast(u32x4_t, lv);
-      } else {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(a.q) + qoff + e;
-        qh[j][c] = ok ? *reinterpret_cast<const u32x4_t*>(p) : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
   }
@@ -575,21 +701,27 @@ attn_prefill_kernel(const PrefillArgs a) {
   if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D, bool QF32, bool PLO>
+template <int D, int QM, bool PLO>
 int launch_s(const PrefillArgs& a, hipStream_t s) {
   const unsigned blocks = (unsigned)((int64_t)a.B * a.Hkv * a.row_blocks * a.splits);
   if (a.splits > 1)
-    hipLaunchKernelGGL((attn_prefill_kernel<D, QF32, PLO, true>), dim3(blocks),
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QM, PLO, true>), dim3(blocks),
                        dim3(kWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_prefill_kernel<D, QF32, PLO, false>), dim3(blocks),
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QM, PLO, false>), dim3(blocks),
                        dim3(kWaves * 64), 0, s, a);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
-template <int D, bool QF32>
+template <int D, int QM>
 int launch_t(const PrefillArgs& a, hipStream_t s) {
-  return a.out_bf16 ? launch_s<D, QF32, false>(a, s) : launch_s<D, QF32, true>(a, s);
+  return a.out_bf16 ? launch_s<D, QM, false>(a, s) : launch_s<D, QM, true>(a, s);
+}
+
+template <int D>
+int launch_d(const PrefillArgs& a, hipStream_t s) {
+  if (a.pro) return a.in_bf16 ? launch_t<D, 2>(a, s) : launch_t<D, 3>(a, s);
+  return a.in_bf16 ? launch_t<D, 0>(a, s) : launch_t<D, 1>(a, s);
 }
 
 }  // namespace
@@ -597,8 +729,8 @@ int launch_t(const PrefillArgs& a, hipStream_t s) {
 int prefill_rows_per_block() { return kRows; }
 
 int launch_attn_prefill(const PrefillArgs& a, hipStream_t s) {
-  if (a.D == 128) return a.in_bf16 ? launch_t<128, false>(a, s) : launch_t<128, true>(a, s);
-  if (a.D == 64) return a.in_bf16 ? launch_t<64, false>(a, s) : launch_t<64, true>(a, s);
+  if (a.D == 128) return launch_d<128>(a, s);
+  if (a.D == 64) return launch_d<64>(a, s);
   return GQA_ERR_UNSUPPORTED;
 }
 

@@ -29,6 +29,7 @@ struct PrologueArgs {
   uint16_t* k_cache;
   uint16_t* v_cache;
   int B, Hq, Hkv, D, T;
+  int kv_only;                 // only the K/V append (q is rotated elsewhere; q_out unused)
   double inv_freq_rev[kMaxHalfDim];   // rotary frequency of pair i / (2 pi), float64
 };
 
@@ -85,7 +86,8 @@ struct MergeArgs {
 // Arguments of the prefill kernel (S query tokens per sequence over the
 // cache, causal or bidirectional), passed by value.
 struct PrefillArgs {
-  const void* q;               // [B,S,Hq,D] dense
+  const void* q;               // [B,S,Hq,D]: sequences q_bstride apart, tokens and heads dense
+  int64_t q_bstride;
   int in_bf16;
   const uint16_t* k_cache;     // [B,Hkv,T,D]
   const uint16_t* v_cache;
@@ -107,6 +109,17 @@ struct PrefillArgs {
   float* ws_o;                 // [teams, splits, rows per block, D]
   float* ws_lse;               // [teams, splits, rows per block]
   uint32_t* ws_cnt;            // [teams]
+  // q prologue in the kernel (q raw): RMSNorm with wq (or none), then RoPE
+  // of token s at pos[b] + s; q_out [B,S,Hq,D] float32 or null
+  int pro;
+  const float* wq;
+  float eps;
+  int rope;
+  int rope_interleaved;
+  float rope_mscale;
+  const int32_t* pos;
+  float* q_out;
+  double inv_freq_rev[kMaxHalfDim];   // rotary frequency of pair i / (2 pi), float64
 };
 
 // Arguments of the packed QKV projection y[M,N] = x[M,K] W^T, passed by

@@ -46,7 +46,8 @@ constexpr int kProVecs = 8;
 constexpr int64_t kManyVecs = 16384;
 
 // Grid: x = sequence * S + token, y = a chunk of VPB * R of the token's
-// Hq + Hkv head vectors (query heads first); lane group k of the workgroup
+// Hq + Hkv head vectors (query heads first; only the Hkv K/V vectors when
+// the queries are rotated by the attention kernel); lane group k of the workgroup
 // takes vectors r * VPB + k of the chunk.  Index arithmetic is per
 // workgroup, and every input of the R vectors is loaded before any math.
 template <int D, typename IT, int R>
@@ -55,6 +56,7 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
   constexpr int VPB = 256 / HALF;    // lane groups per workgroup
   const int Hq = a.Hq, Hkv = a.Hkv, T = a.T, S = a.S;
   const int H = Hq + Hkv;
+  const int vfirst = a.kv_only ? Hq : 0;   // first head vector of the launch
   const int b = blockIdx.x / S;
   const int st = blockIdx.x - b * S;  // token
   const int grp = threadIdx.x / HALF;
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
   IT v0[R], v1[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int vh = (blockIdx.y * R + r) * VPB + grp;
+    const int vh = vfirst + (blockIdx.y * R + r) * VPB + grp;
     x0[r] = x1[r] = 0.0f;
     v0[r] = v1[r] = IT(0);
     if (vh >= H) continue;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int vh = (blockIdx.y * R + r) * VPB + grp;
+    const int vh = vfirst + (blockIdx.y * R + r) * VPB + grp;
     if (vh >= H) continue;             // uniform within the lane group
     const bool is_q = vh < Hq;
     // Weights and rotation act on the exact inputs in float64 and the RMS
@@ -142,14 +144,15 @@ __global__ __launch_bounds__(256) void qkv_prologue_kernel(const PrologueArgs a)
 template <int D, typename IT, int R>
 static int launch_prologue_r(const PrologueArgs& a, hipStream_t s) {
   constexpr int per = 256 / (D / 2) * R;   // head vectors per workgroup
-  const dim3 grid((unsigned)((int64_t)a.B * a.S), (unsigned)((a.Hq + a.Hkv + per - 1) / per));
+  const int nv = a.kv_only ? a.Hkv : a.Hq + a.Hkv;   // head vectors per token
+  const dim3 grid((unsigned)((int64_t)a.B * a.S), (unsigned)((nv + per - 1) / per));
   hipLaunchKernelGGL((qkv_prologue_kernel<D, IT, R>), grid, dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
 template <int D, typename IT>
 static int launch_prologue_t(const PrologueArgs& a, hipStream_t s) {
-  const int64_t vecs = (int64_t)a.B * a.S * (a.Hq + a.Hkv);
+  const int64_t vecs = (int64_t)a.B * a.S * (a.kv_only ? a.Hkv : a.Hq + a.Hkv);
   return vecs >= kManyVecs ? launch_prologue_r<D, IT, kProVecs>(a, s)
                            : launch_prologue_r<D, IT, 1>(a, s);
 }

@@ -18,7 +18,7 @@ from . import decode_step_ex, qkv_prologue_ex, rope_table
 from . import attn_decode_merge_multi, attn_decode_multi, attn_decode_splitk_multi, attn_prefill
 from . import splitk_multi_workspace_bytes
 from . import decode_step_multi, decode_step_multi_workspace_bytes, prefill_workspace_bytes
-from . import qkv_gemv
+from . import prefill_step, qkv_gemv
 
 BF16_NAN = 0x7FC0
 
@@ -44,11 +44,13 @@ class DeviceStep:
     the prologue and the unsplit kernel; "prefill" runs the prologue and the
     matrix-core prefill kernel (any number of tokens, causal or
     bidirectional as the workload says; ``splits`` > 1 shares each row
-    block's keys among that many workgroups).  ``split`` (bool) is the older
-    spelling of split/unsplit.  ``q_dtype`` selects the dtype attention reads
-    q in when the workload has no prologue.  ``poison`` writes bf16 NaN into
-    every cache row outside each sequence's attended range [lo, n) (rows the
-    step must never read); rows written by the prologue are left alone.
+    block's keys among that many workgroups); "prefill_step" runs the K/V
+    append and the prefill kernel, which rotates q itself
+    (gqa_prefill_step).  ``split`` (bool) is the older spelling of
+    split/unsplit.  ``q_dtype`` selects the dtype attention reads q in when
+    the workload has no prologue.  ``poison`` writes bf16 NaN into every
+    cache row outside each sequence's attended range [lo, n) (rows the step
+    must never read); rows written by the prologue are left alone.
     """
 
     def __init__(self, w, device="cuda", split: bool = True,
@@ -60,7 +62,9 @@ class DeviceStep:
         self.S = int(getattr(w, "S", 1))     # query tokens per sequence
         self.mode = mode or ("split" if split else "unsplit")
         self.causal = bool(getattr(w, "causal", True))
-        if not self.causal and self.mode != "prefill":
+        if self.mode == "prefill_step" and w.pos is None:
+            raise ValueError("prefill_step needs a workload with a prologue")
+        if not self.causal and self.mode not in ("prefill", "prefill_step"):
             raise NotImplementedError("bidirectional attention runs on the prefill kernel")
         self.split = self.mode == "split"
         self.splits = int(splits)           # prefill: key splits per row block
@@ -115,7 +119,9 @@ class DeviceStep:
         self.lse = torch.empty((w.B,) + tok + (w.Hq,), dtype=torch.float32, device=d)
         self.ws = None
         self.pws = None
-        if self.mode == "prefill" and self.splits > 1:
+        if self.mode == "prefill_step" and self.inv_freq is None and w.theta > 0:
+            self.inv_freq, self.rope_mscale = rope_table("default", w.D, w.theta)
+        if self.mode in ("prefill", "prefill_step") and self.splits > 1:
             nb = prefill_workspace_bytes(w.B, self.S, w.Hq, w.Hkv, w.D, self.splits)
             self.pws = torch.zeros(nb, dtype=torch.uint8, device=d)   # tickets start at 0
         if self.mode == "split":
@@ -221,9 +227,26 @@ class DeviceStep:
         off = base + (-base) % 256
         return self.ws[off:off + 4 * w.B * w.Hkv].view(torch.int32)
 
+    def prefill_step(self):
+        w = self.w
+        q = self.q_in if self.q_in.dim() == 4 else self.q_in.unsqueeze(1)
+        kn = self.k_new if self.k_new.dim() == 4 else self.k_new.unsqueeze(1)
+        vn = self.v_new if self.v_new.dim() == 4 else self.v_new.unsqueeze(1)
+        out = self.out if self.out.dim() == 4 else self.out.unsqueeze(1)
+        qo = self.q if self.q.dim() == 4 else self.q.unsqueeze(1)
+        prefill_step(q, kn, vn, self.pos, self.k_cache, self.v_cache, self.lens,
+                     causal=self.causal, window=w.window, scale=self.scale,
+                     inv_freq=self.inv_freq, rope_mscale=self.rope_mscale,
+                     rope_layout=self.rope_layout, q_norm_w=self.w_q, k_norm_w=self.w_k,
+                     eps=w.eps, splits=self.splits, workspace=self.pws, out=out,
+                     lse_out=self.lse.reshape(w.B, self.S, w.Hq), q_out=qo)
+
     def run(self):
         if self.mode == "fused":
             self.fused()
+            return
+        if self.mode == "prefill_step":
+            self.prefill_step()
             return
         self.prologue()
         self.attention()

@@ -401,6 +401,33 @@ int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
  * device: 2 when the launch has fewer row blocks than two per CU, else 1;
  * it reads device attributes only and returns 1 when they cannot be read.
  */
+/*
+ * The prefill with its prologue, in two launches: the effect of
+ * gqa_qkv_prologue_ex over S tokens followed by gqa_attn_prefill_split.
+ * The first launch appends the S tokens' K/V rows (rows pos[b] + s inside
+ * [0, T)); the second is the attention kernel, which normalises and rotates
+ * its own rows of q as it loads them, so the rotated q never goes through
+ * memory (q_out, float32 [B,S,Hq,D], is written only when not NULL).  q's
+ * rotary sin and cos come from the float64-reduced phase through the
+ * hardware sine and cosine (which take turns), so q_out can differ from
+ * gqa_qkv_prologue_ex's float64 rotation in the last bits; the appended K
+ * rows are those of gqa_qkv_prologue_ex.  Arguments as for
+ * gqa_qkv_prologue_ex (q [B,S,Hq,D] and k_new, v_new [B,S,Hkv,D] with batch
+ * strides, tokens and heads dense; pos, k_new, v_new required) and
+ * gqa_attn_prefill_split (causal, window, scale, splits, workspace, out,
+ * out_dtype, lse_out); the same errors.
+ */
+int gqa_prefill_step(const void* q, const void* k_new, const void* v_new,
+                     gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                     const float* q_norm_w, const float* k_norm_w, float eps,
+                     const double* inv_freq, double rope_mscale, int rope_layout,
+                     const int32_t* pos, int S,
+                     uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                     int causal, int window, float scale, int splits,
+                     void* workspace, size_t workspace_bytes,
+                     void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                     int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
+
 size_t gqa_attn_prefill_workspace_bytes(int B, int S, int Hq, int Hkv, int D, int splits);
 int gqa_attn_prefill_default_splits(int B, int S, int Hq, int Hkv);
 int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,

@@ -1,7 +1,7 @@
 """Seeded random sweep over the whole surface: the decode step (split,
 unsplit and fused), several tokens per sequence (split, unsplit and in one
 launch), the prefill (causal and bidirectional, with and without key
-splits) and the packed QKV projection.  Each case draws its sizes
+splits, with the q prologue in the kernel) and the packed QKV projection.  Each case draws its sizes
 from a fixed-seed generator -- group size, head dim, batch, cache length,
 lengths (ragged, some zero), window, partition size, token count, output
 dtype -- and is checked against the fp64 oracle at the same bars as the
@@ -35,7 +35,7 @@ def _decode_cases(n=60, seed=1234):
     return out
 
 
-def _tokens_cases(n=60, seed=4321, prefill=False, fused=False, splits=False):
+def _tokens_cases(n=60, seed=4321, prefill=False, fused=False, splits=False, step=False):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -59,6 +59,9 @@ def _tokens_cases(n=60, seed=4321, prefill=False, fused=False, splits=False):
                         zero=bool(rng.random() < 0.3), seed=int(rng.integers(1 << 30))))
         if splits:
             out[-1]["splits"] = int(rng.integers(2, 7))
+        if step:                       # the prefill with its prologue in the kernel
+            out[-1]["mode"] = "prefill_step"
+            out[-1]["prologue"] = True
     return out
 
 
@@ -144,6 +147,13 @@ def test_gpu_sweep_prefill(c):
 @pytest.mark.parametrize("c", _tokens_cases(n=30, seed=2468, prefill=True, splits=True),
                          ids=_cid)
 def test_gpu_sweep_prefill_split(c):
+    _run(c)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("c", _tokens_cases(n=30, seed=1357, prefill=True, splits=True,
+                                            step=True), ids=_cid)
+def test_gpu_sweep_prefill_step(c):
     _run(c)
 
 

@@ -55,6 +55,23 @@ def test_prefill_split_validation(G):
     assert call(S=0) == -2
 
 
+def test_prefill_step_validation(G):
+    def call(q=A16, kn=A16, pos=A16, S=64, splits=1, qbs=None, eps=1e-6, layout=0):
+        qbs = S * 32 * 128 if qbs is None else qbs
+        return G.lib.gqa_prefill_step(q, kn, A16, 1, qbs, S * 8 * 128, None, None, eps, None,
+                                      1.0, layout, pos, S, A16, A16, A16, 1, 0, 0.0, splits,
+                                      None, 0, A16, 0, None, None, 1, 32, 8, 128, 4096, None)
+    assert call(q=None) == -1
+    assert call(kn=None) == -1
+    assert call(pos=None) == -1
+    assert call(S=0) == -2
+    assert call(splits=2) == -1                  # splits > 1 needs a workspace
+    assert call(qbs=100) == -2                   # batch stride below S * Hq * D
+    assert call(eps=-1.0) == -7
+    assert call(layout=5) == -7
+    assert call(q=A16 + 8) == -6
+
+
 def test_prefill_split_workspace(G):
     # rows per KV head = S * G = 300 * 4 -> 10 row blocks of 128; teams = B * Hkv * 10
     B, S, Hq, Hkv, D, sp = 2, 300, 32, 8, 128, 4
@@ -314,3 +331,64 @@ def test_gpu_prefill_split_reruns_and_unsplit():
     one = _step(w)
     assert float(np.max(np.abs(one["out"] - r1["out"]))) <= 1e-3
     assert float(np.max(np.abs(one["lse"] - r1["lse"]))) <= 1e-3
+
+
+# (config, overrides, key splits, what the case covers): the prefill with
+# its prologue (gqa_prefill_step), q normalised and rotated in the kernel
+STEP_CASES = [
+    ("7f", dict(S=1024, L=1024), 2, "fresh causal S=1024, the fusedtok row's shape"),
+    ("7f", dict(S=300, L=300), 1, "fresh, ragged row block"),
+    ("7f", dict(S=200, L=260, causal=False), 1, "fresh bidirectional"),
+    ("6", dict(B=2, L=300, S=64), 1, "chunk after 300 rows"),
+    ("5", dict(B=2, L=2000, window=300, S=200), 3, "QK-norm, window per token, splits"),
+    ("5", dict(B=2, L=900, S=100, rope_layout="interleaved"), 1, "interleaved pairs"),
+    ("6", dict(B=2, L=900, S=40, Hq=16, Hkv=2,
+               rope_scaling=dict(kind="yarn", factor=4.0, orig_ctx=512)), 1,
+     "G=8, YaRN table and magnitude factor"),
+    ("1", dict(S=50), 1, "D=64"),
+    ("3", dict(B=4, L=1200, S=96, lmin=96, out_dtype="f32"), 2, "ragged lengths, fp32 out"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over,splits,what", STEP_CASES,
+                         ids=[f"p{i}" for i in range(len(STEP_CASES))])
+def test_gpu_prefill_step(name, over, splits, what):
+    """The K/V append and the attention with the q prologue inside the kernel
+    against the oracle: outputs, the rotated q (q_out) and the appended rows."""
+    _gpu()
+    from gqa_attention_kv_amd import runner
+    from test_gpu_parity import check_attention
+    from test_multi_token import check_prologue_multi
+    w = W.make(name, **over)
+    print(f"\n[case] prefill step splits={splits} cfg={name} {over} ({what})", flush=True)
+    ref = O.decode_step(w)
+    step = runner.DeviceStep(w, mode="prefill_step", splits=splits)
+    step.run()
+    got = step.results()
+    check_attention(got, ref, w.out_dtype, f"prefill step {name} {over}")
+    check_prologue_multi(w, got, ref, f"prefill step {name} {over}")
+
+
+@pytest.mark.gpu
+def test_gpu_prefill_step_matches_two_calls():
+    """gqa_prefill_step against gqa_qkv_prologue_ex + gqa_attn_prefill on the
+    same inputs: identical caches, outputs within the parity bar, reruns
+    bit-identical."""
+    _gpu()
+    from gqa_attention_kv_amd import runner
+    w = W.make("7f", S=512, L=600, out_dtype="f32")
+    a = runner.DeviceStep(w, mode="prefill")
+    a.run()
+    ra = a.results()
+    b = runner.DeviceStep(w, mode="prefill_step")
+    b.run()
+    rb = b.results()
+    b.run()
+    rb2 = b.results()
+    assert np.array_equal(ra["k_cache"], rb["k_cache"])
+    assert np.array_equal(ra["v_cache"], rb["v_cache"])
+    assert float(np.max(np.abs(ra["out"] - rb["out"]))) <= 1e-3
+    assert float(np.max(np.abs(ra["q"] - rb["q"]))) <= 1e-4
+    for k in ("out", "lse", "q", "k_cache"):
+        assert np.array_equal(rb[k], rb2[k]), k
