@@ -1,7 +1,8 @@
 // extern "C" entry points declared in include/gqa_decode.h: host-side
-// argument checks, then one launcher call.  Nothing is enqueued when a check
-// fails, and no entry point allocates, frees, synchronises or reads device
-// memory.
+// argument checks, then the launcher calls (one, or two for
+// gqa_prefill_step).  Nothing is enqueued when a check fails, and no entry
+// point allocates, frees, synchronises or reads device memory
+// (gqa_attn_prefill_default_splits only reads a device attribute).
 #include <math.h>
 #include <stdint.h>
 
