@@ -246,6 +246,17 @@ static int64_t prefill_teams(int B, int S, int Hq, int Hkv) {
   return (int64_t)B * Hkv * ((rows + per - 1) / per);
 }
 
+// Point the key-split buffers of `a` (sizes and splits set) into `workspace`.
+static void prefill_workspace_layout(gqa::PrefillArgs& a, void* workspace) {
+  const size_t part =
+      (size_t)a.B * a.Hkv * a.row_blocks * a.splits * gqa::prefill_rows_per_block();
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_lse = reinterpret_cast<float*>(ws + align256(part * a.D * sizeof(float)));
+  a.ws_cnt = reinterpret_cast<uint32_t*>(ws + align256(part * a.D * sizeof(float)) +
+                                         align256(part * sizeof(float)));
+}
+
 size_t gqa_attn_prefill_workspace_bytes(int B, int S, int Hq, int Hkv, int D, int splits) {
   if (B < 1 || S < 1 || Hq < 1 || Hkv < 1 || D < 1 || splits < 1 || Hq % Hkv != 0) return 0;
   if (splits == 1) return 0;
@@ -304,14 +315,7 @@ int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   a.row_blocks = (int)row_blocks;
   a.splits = splits;
-  if (splits > 1) {
-    const size_t part = (size_t)B * Hkv * row_blocks * splits * per;
-    char* ws = static_cast<char*>(workspace);
-    a.ws_o = reinterpret_cast<float*>(ws);
-    a.ws_lse = reinterpret_cast<float*>(ws + align256(part * D * sizeof(float)));
-    a.ws_cnt = reinterpret_cast<uint32_t*>(ws + align256(part * D * sizeof(float)) +
-                                           align256(part * sizeof(float)));
-  }
+  if (splits > 1) prefill_workspace_layout(a, workspace);
   return gqa::launch_attn_prefill(a, stream);
 }
 
@@ -381,14 +385,7 @@ int gqa_prefill_step(const void* q, const void* k_new, const void* v_new,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
   a.row_blocks = (int)row_blocks;
   a.splits = splits;
-  if (splits > 1) {
-    const size_t part = (size_t)B * Hkv * row_blocks * splits * per;
-    char* ws = static_cast<char*>(workspace);
-    a.ws_o = reinterpret_cast<float*>(ws);
-    a.ws_lse = reinterpret_cast<float*>(ws + align256(part * D * sizeof(float)));
-    a.ws_cnt = reinterpret_cast<uint32_t*>(ws + align256(part * D * sizeof(float)) +
-                                           align256(part * sizeof(float)));
-  }
+  if (splits > 1) prefill_workspace_layout(a, workspace);
   a.pro = 1;
   a.wq = q_norm_w; a.eps = eps;
   a.rope = pa.rope; a.rope_interleaved = pa.rope_interleaved; a.rope_mscale = pa.rope_mscale;
