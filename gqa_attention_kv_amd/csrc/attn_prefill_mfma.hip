@@ -443,15 +443,26 @@ attn_prefill_kernel(const PrefillArgs a) {
     const bool work = wave_live && k0 < need_hi && k0 + kKeys > need_lo;   // wave-uniform
     f32x4_t s[kKB][2];
     if (work) {
-      // QK for every 16-key block and both row blocks.
+      // QK for every 16-key block and both row blocks.  The K operands of
+      // block kb + 1 are read from LDS while block kb's calls run (two
+      // register sets; the scheduling barriers keep the reads ahead).
+      u32x4_t kbuf[2][KC];
+      auto kread = [&](int kb, u32x4_t* dst) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          dst[c] =
+              *reinterpret_cast<const u32x4_t*>(cur + (16 * kb + n) * KROW + 64 * c + 16 * k4);
+      };
+      kread(0, kbuf[0]);
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
         s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (kb + 1 < kKB) kread(kb + 1, kbuf[(kb + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          const u32x4_t ka =
-              *reinterpret_cast<const u32x4_t*>(cur + (16 * kb + n) * KROW + 64 * c + 16 * k4);
+          const u32x4_t ka = kbuf[kb & 1][c];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             s[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -463,6 +474,7 @@ attn_prefill_kernel(const PrefillArgs a) {
                   s[kb][j], 0, 0, 0);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // Stash the next tile into the other stage (every wave finished reading
@@ -544,13 +556,23 @@ attn_prefill_kernel(const PrefillArgs a) {
           }
       }
 
-      // PV: column block v, lane row n is column 16 v + n of V.
+      // PV: column block v, lane row n is column 16 v + n of V.  The V
+      // operand of step (hh, v) + 1 is read while step (hh, v) runs.
+      auto vread = [&](int it) {
+        const int hh = it / VB, v = it % VB;
+        return *reinterpret_cast<const u32x4_t*>(cur + KBYTES + (16 * v + n) * VROW + 64 * hh +
+                                                 16 * k4);
+      };
+      u32x4_t vbuf[2];
+      vbuf[0] = vread(0);
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
         for (int v = 0; v < VB; ++v) {
-          const u32x4_t va = *reinterpret_cast<const u32x4_t*>(
-              cur + KBYTES + (16 * v + n) * VROW + 64 * hh + 16 * k4);
+          const int it = hh * VB + v;
+          if (it + 1 < NH * VB) vbuf[(it + 1) & 1] = vread(it + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const u32x4_t va = vbuf[it & 1];
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -561,6 +583,7 @@ attn_prefill_kernel(const PrefillArgs a) {
                   __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pl[hh][j]),
                   o[j][v], 0, 0, 0);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
     }
     if (!kEarlyStash) {
