@@ -371,6 +371,32 @@ def test_gpu_prefill_step(name, over, splits, what):
 
 
 @pytest.mark.gpu
+def test_gpu_prefill_step_edges():
+    """gqa_prefill_step with tokens past the cache end (sequence 0: rows
+    pos + s >= T are not written), an empty sequence (no row attended:
+    out = 0, lse = -inf) and a sequence whose first tokens see no row."""
+    _gpu()
+    from gqa_attention_kv_amd import runner
+    from test_gpu_parity import check_attention
+    from test_multi_token import check_prologue_multi
+    w = W.make("6", B=3, L=400, S=96, Hq=16, Hkv=4)
+    T = w.T
+    w.pos = w.pos.copy()
+    w.lens = w.lens.copy()
+    w.pos[0], w.lens[0] = T - 40, T            # 56 of the 96 new rows fall past T
+    w.pos[1], w.lens[1] = -96, 0               # empty sequence
+    w.pos[2], w.lens[2] = 0, 50                # tokens 0..45 see no row
+    print(f"\n[case] prefill step edges pos={w.pos.tolist()} lens={w.lens.tolist()}", flush=True)
+    ref = O.decode_step(w)
+    step = runner.DeviceStep(w, mode="prefill_step", splits=2)
+    step.run()
+    got = step.results()
+    check_attention(got, ref, w.out_dtype, "prefill step edges")
+    check_prologue_multi(w, got, ref, "prefill step edges")
+    assert np.all(got["out"][1] == 0) and np.all(got["lse"][1] == -math.inf)
+
+
+@pytest.mark.gpu
 def test_gpu_prefill_step_matches_two_calls():
     """gqa_prefill_step against gqa_qkv_prologue_ex + gqa_attn_prefill on the
     same inputs: identical caches, outputs within the parity bar, reruns
