@@ -192,6 +192,9 @@ struct TileBuf {
 // spills to scratch inside the tile loop.
 constexpr int kWavesPerEU = 3;
 
+// Lazy-rescale threshold of the online softmax, in exp2 units.
+constexpr float kRescaleLog2 = 8.0f;
+
 // The last workgroup of a (sequence, KV head) team merges the team's
 // partitions (one per member): M = max_k lse_k, w_k = e^(lse_k - M),
 // out = sum_k w_k o_k / sum_k w_k, lse = M + log sum_k w_k.  Thread t owns
@@ -952,30 +955,45 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       p[r] = ok ? s[r] * qscale : -INFINITY;
       tmax = fmaxf(tmax, p[r]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    // With several tokens a column may have seen no valid row yet (m = mnew
-    // = -inf): exponents are then taken against 0, which keeps alpha and p
-    // at 0 instead of NaN.  With one token the unit's first tile always
-    // holds a valid row, so mnew is finite.
-    const float mnew = fmaxf(m, tmax);
-    const float mref = MT && mnew == -INFINITY ? 0.0f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - mref);
-    m = mnew;
+    // The maximum over the four lane groups (rows) of head n, in VALU
+    // permutes rather than LDS round trips.
+    {
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
+                                                      __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+      const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax),
+                                                      __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+    }
+    // Lazy rescale: the reference maximum m moves only when the tile's
+    // maximum exceeds it by more than 2^8 (exp2 units), so p stays below 256
+    // and, in most tiles, O is not rescaled at all (no cross-lane exchange
+    // of the factors).  m = -inf (no valid row yet) always moves to a finite
+    // maximum.
+    const bool need = tmax > m + kRescaleLog2;
+    if (__any(need)) {
+      const float mnew = need ? tmax : m;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;   // 0 from -inf
+      m = mnew;
+      l *= alpha;
+      // Rescale O rows: row 4lg + r belongs to the head held by lane 4lg + r.
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float al = __shfl(alpha, 4 * lg + r, 64);
+#pragma unroll
+        for (int blk = 0; blk < VB; ++blk) o[blk][r] *= al;
+      }
+    }
+    // A column that has seen no valid row yet (m = -inf, several tokens)
+    // takes its exponents against 0, which keeps p at 0 instead of NaN.
+    const float mref = m == -INFINITY ? 0.0f : m;
     float psum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       p[r] = __builtin_amdgcn_exp2f(p[r] - mref);
       psum += p[r];
     }
-    l = l * alpha + psum;
-    // Rescale O rows: row 4lg + r belongs to the head held by lane 4lg + r.
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float al = __shfl(alpha, 4 * lg + r, 64);
-#pragma unroll
-      for (int blk = 0; blk < VB; ++blk) o[blk][r] *= al;
-    }
+    l += psum;
     // PV on one bf16 call per column block, with the 16 tile rows as 32
     // k-indices: k = 8lg + 2r + x stands for tile row 4r + lg, x = 0 taking
     // the bf16 hi part of P and x = 1 its lo part, so V (exact in bf16) is
