@@ -79,16 +79,25 @@ __device__ __forceinline__ int vpos(int key) {
   return (key & ~31) + 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
 }
 
+// Maximum that propagates NaN (IEEE 754-2019 maximum, v_maximum3_f32 on
+// gfx950).  Unlike fmaxf it needs no canonicalised inputs, which saves an
+// instruction per matrix-core result.  The scores it sees are finite or
+// -inf (masked); a NaN could only come from a NaN in an attended row, and
+// that reaches the output through the exponential either way.
+__device__ __forceinline__ float fmax_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 of a wave, in every lane:
 // v_permlane32_swap exchanges the wave's halves and v_permlane16_swap the
 // odd and even 16-lane rows (VALU ops, no LDS round trip).
 __device__ __forceinline__ float max_over_rows(float t) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t),
                                                   false, false);
-  t = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  t = fmax_nan(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t),
                                                   false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Two floats as packed bf16 (round to nearest even), a in the low half.
@@ -150,7 +159,10 @@ attn_prefill_kernel(const PrefillArgs a) {
   const int b = pair / Hkv, g = pair % Hkv;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // wave index in a scalar register, so tests on the wave's rows (which
+  // tiles it works on, which need masks) are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, k4 = lane >> 4;
 
   const int len = a.lens[b];
@@ -381,8 +393,38 @@ attn_prefill_kernel(const PrefillArgs a) {
   const bool vthread = VITEMS >= kWaves * 64 || tid < VITEMS;
   u32x4_t fk[KFILL], fv0[VFILL], fv1[VFILL];
   auto clamp_key = [&](int key) { return key < kend ? key : kend - 1; };
+  // A tile wholly inside [kbeg, kend) needs no clamp: each load's offset is
+  // then the lane's fixed part plus the tile's (scalar) row offset.
+  uint32_t kofs[KFILL], vofs[VFILL];
+#pragma unroll
+  for (int f = 0; f < KFILL; ++f) {
+    const int ci = tid + kWaves * 64 * f;
+    kofs[f] = (uint32_t)(ci / CPR) * (uint32_t)(D * 2) + 16u * (ci % CPR);
+  }
+#pragma unroll
+  for (int f = 0; f < VFILL; ++f) {
+    const int it = tid + kWaves * 64 * f;
+    vofs[f] = (uint32_t)(2 * (it % PAIRS)) * (uint32_t)(D * 2) + 16u * (it / PAIRS);
+  }
   auto fetch = [&](int tile) {
     const int base = kbeg + kKeys * tile;
+    if (base + kKeys <= kend) {
+      const uint32_t so = (uint32_t)base * (uint32_t)(D * 2);
+#pragma unroll
+      for (int f = 0; f < KFILL; ++f)
+        fk[f] = __builtin_bit_cast(u32x4_t,
+                                   __builtin_amdgcn_raw_buffer_load_b128(rk, kofs[f], so, 0));
+      if (vthread) {
+#pragma unroll
+        for (int f = 0; f < VFILL; ++f) {
+          fv0[f] = __builtin_bit_cast(u32x4_t,
+                                      __builtin_amdgcn_raw_buffer_load_b128(rv, vofs[f], so, 0));
+          fv1[f] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, vofs[f] + D * 2, so, 0));
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int f = 0; f < KFILL; ++f) {
       const int ci = tid + kWaves * 64 * f;
@@ -491,9 +533,9 @@ attn_prefill_kernel(const PrefillArgs a) {
       // Masks and the tile maximum of each row (raw scores; qscale > 0).
       float mnew[2];
       bool need[2];
+      if (!full) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (!full) {
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
@@ -501,13 +543,16 @@ attn_prefill_kernel(const PrefillArgs a) {
               const int key = k0 + 16 * kb + 4 * k4 + i;
               if (key < rlo[j] || key >= rhi[j]) s[kb][j][i] = -INFINITY;
             }
-        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
         float t = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
-          t = fmaxf(t, fmaxf(fmaxf(s[kb][j][0], s[kb][j][1]), fmaxf(s[kb][j][2], s[kb][j][3])));
+          t = fmax_nan(t, fmax_nan(fmax_nan(s[kb][j][0], s[kb][j][1]),
+                                   fmax_nan(s[kb][j][2], s[kb][j][3])));
         t = max_over_rows(t);
-        mnew[j] = fmaxf(m[j], t);
+        mnew[j] = fmax_nan(m[j], t);
         // m = -inf with a finite maximum gives +inf (rescale); both -inf give
         // NaN (no rescale: the row has seen no key yet).
         need[j] = (mnew[j] - m[j]) * qscale > kRescaleLog2;
