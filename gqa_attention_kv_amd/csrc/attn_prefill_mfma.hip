@@ -495,6 +495,11 @@ attn_prefill_kernel(const PrefillArgs a) {
           dst[c] =
               *reinterpret_cast<const u32x4_t*>(cur + (16 * kb + n) * KROW + 64 * c + 16 * k4);
       };
+      // The two waves on a SIMD belong to different workgroups and each
+      // alternates matrix-core blocks with VALU softmax work: the one in a
+      // matrix-core block issues first, so the other's VALU work fills the
+      // gaps instead of competing for the same slots.
+      __builtin_amdgcn_s_setprio(1);
       kread(0, kbuf[0]);
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
@@ -518,6 +523,7 @@ attn_prefill_kernel(const PrefillArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     // Stash the next tile into the other stage (every wave finished reading
     // that stage before the barrier that ended the previous trip), then
@@ -609,6 +615,7 @@ attn_prefill_kernel(const PrefillArgs a) {
                                                  16 * k4);
       };
       u32x4_t vbuf[2];
+      __builtin_amdgcn_s_setprio(1);
       vbuf[0] = vread(0);
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
@@ -630,6 +637,7 @@ attn_prefill_kernel(const PrefillArgs a) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (!kEarlyStash) {
       if (tile + 1 < te) stash((tile + 1 - tb) & 1);
