@@ -369,6 +369,9 @@ attn_prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int v = 0; v < VB; ++v) o[j][v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY};
+  // the exponent's reference: m * qscale, or 0 while m = -inf; it changes
+  // only with m, so it is kept rather than rebuilt every tile
+  float mq[2] = {0.f, 0.f};
   float l[2] = {0.f, 0.f};
   const float qscale = a.qscale;
 
@@ -567,7 +570,10 @@ attn_prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const float alpha = need[j] ? __builtin_amdgcn_exp2f((m[j] - mnew[j]) * qscale) : 1.0f;
-          if (need[j]) m[j] = mnew[j];
+          if (need[j]) {
+            m[j] = mnew[j];
+            mq[j] = m[j] * qscale;
+          }
           l[j] *= alpha;
 #pragma unroll
           for (int v = 0; v < VB; ++v) o[j][v] *= alpha;
@@ -582,15 +588,15 @@ attn_prefill_kernel(const PrefillArgs a) {
       u32x4_t ph[NH][2], pl[NH][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float mref = m[j] == -INFINITY ? 0.0f : m[j] * qscale;
+        const float mref = mq[j];
         float p[kKB][4];
-        float ps = 0.0f;
+        float ps;
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j][i], qscale, -mref));
-            ps += p[kb][i];
+            ps = kb == 0 && i == 0 ? p[0][0] : ps + p[kb][i];
           }
         l[j] += ps;
 #pragma unroll
