@@ -1125,13 +1125,19 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   if constexpr (MODE == Mode::Step) {
     if (num_parts == 1) return;
     // Arrival ticket: every workgroup of this (sequence, KV head) publishes
-    // its partial, waits until those write-through stores have completed,
-    // and takes a ticket; the last one reads the partials back with
-    // agent-scope loads (which do not hit stale L2 lines), merges them, and
-    // resets the ticket for the next launch.  No
-    // workgroup waits on another.  Agent-scope fences would write back or
-    // invalidate a whole L2 per workgroup, which costs more than the step.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // stores completed
+    // its partial and takes a ticket; the last one reads the partials back,
+    // merges them, and resets the ticket for the next launch.  No workgroup
+    // waits on another.
+    //  * Release: every wave waits until its own write-through partial
+    //    stores are complete (wait_vmem), then the workgroup meets at the
+    //    barrier, and only then does thread 0 take the ticket.  So every
+    //    partial of this workgroup is visible device-wide before the ticket
+    //    moves.  (An agent-scope release fence would also write back the
+    //    whole L2 of the XCD, per workgroup; the partials are write-through
+    //    and need only the wait.)
+    //  * Acquire: the last arriver alone takes an agent-scope acquire fence
+    //    before it reads, and reads the partials with device-coherent loads.
+    wait_vmem();
     __syncthreads();
     __shared__ int s_last;
     uint32_t* ticket = a.ws_cnt + (int64_t)b * Hkv + g;
@@ -1142,6 +1148,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     merge_partials<D, CT, NW, MT>(a, head0, G, NC);
     if (threadIdx.x == 0)
       __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -361,7 +361,7 @@ attn_prefill_kernel(const PrefillArgs a) {
   // The q operands are complete before the loop: without this, the first
   // use inside the loop would wait for every load in flight (on each trip,
   // the prefetch of the tile after next as well).
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); lgkmcnt, expcnt unrestricted
+  wait_vmem();
 
   f32x4_t o[2][VB];
 #pragma unroll
@@ -702,8 +702,11 @@ attn_prefill_kernel(const PrefillArgs a) {
 
   // Arrival ticket (one per row block): the last split to arrive merges the
   // partials in split order, so reruns are bit-identical, and resets the
-  // ticket.  No workgroup waits for another.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // partial stores completed
+  // ticket.  No workgroup waits for another.  Every wave waits until its
+  // write-through partial stores are complete before the barrier that
+  // precedes the ticket (release), and the last arriver takes an
+  // agent-scope acquire fence before it reads the partials back.
+  wait_vmem();
   __syncthreads();
   __shared__ int s_last;
   uint32_t* ticket = a.ws_cnt + team;
@@ -714,6 +717,7 @@ attn_prefill_kernel(const PrefillArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // Thread tid owns float4 groups tid + 256 i of the block's rows x D: row
   // (tid + 256 i) / (D/4).  One memory round trip per split: M, W and A are
   // the running maximum lse, weight sum and weighted sum.

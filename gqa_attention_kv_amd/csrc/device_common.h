@@ -105,4 +105,13 @@ __device__ __forceinline__ void sincos_pi_f64(double x, double* s, double* c) {
   *c = (q == 1 || q == 2) ? -cv : cv;
 }
 
+// Waits until every vector-memory access this wave has issued is complete
+// (s_waitcnt vmcnt(0); the LDS and export counters are left unrestricted).
+// A store's counter drops only once the store is acknowledged at the level
+// its scope bits name, so after this wait a device-scope (write-through)
+// store has reached the point where every XCD reads it.  A workgroup-scope
+// release fence does not give this on gfx950: all waves of a workgroup share
+// one CU, so it waits only for LDS traffic.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace gqa
