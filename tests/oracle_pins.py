@@ -730,4 +730,133 @@ def pin_prologue_multi_matches_bruteforce(O):
                 assert np.array_equal(vc2[b, :, t], vc[b, :, t])
 
 
+# ---------------------------------------------------------------------------
+# The whole decode step: prologue, then attention over the appended cache
+# ---------------------------------------------------------------------------
+def _bf16_rne_scalar(x: float) -> int:
+    """One round-to-nearest-even of a Python float to bf16 bits, by hand:
+    8 significant bits from frexp, Python's round() (ties to even)."""
+    if x == 0.0:
+        return 0x8000 if math.copysign(1.0, x) < 0 else 0
+    m, e = math.frexp(x)                       # x = m 2^e, 0.5 <= |m| < 1
+    r = round(m * 256.0)                       # exact product; ties to even
+    y = math.ldexp(r, e - 8)
+    u = int.from_bytes(np.float32(y).tobytes(), "little")
+    return u >> 16
+
+
+def _bf16_value(bits: int) -> float:
+    return float(np.frombuffer((bits << 16).to_bytes(4, "little"), np.float32)[0])
+
+
+def _step_bruteforce(O, w, scale):
+    """The decode step composed by hand from the scalar brute force: each
+    token's q and k normalised (if the workload has weights), rotated at its
+    own position with the workload's pair layout, table and magnitude
+    factor, the k row rounded once to bf16 and written with the raw v row at
+    that position, then attention of the rotated q over the appended cache
+    (token s attends lens - (S-1-s) rows when causal, lens rows otherwise)."""
+    S = w.S
+    B, Hq, Hkv, D, T = w.B, w.Hq, w.Hkv, w.D, w.T
+    q = O.bf16_to_f64(w.q).reshape(B, S, Hq, D)
+    kc = w.k_cache.copy()
+    vc = w.v_cache.copy()
+    if w.theta > 0:
+        if w.rope_scaling is not None:
+            inv, msc = O.rope_inv_freq_scaled(D, w.theta, **w.rope_scaling)
+            inv = [float(f) for f in inv]
+        else:
+            inv, msc = [w.theta ** (-2.0 * i / D) for i in range(D // 2)], 1.0
+    qh = np.array(q)
+    if w.pos is not None:
+        kn = O.bf16_to_f64(w.k_new).reshape(B, S, Hkv, D)
+        vbits = np.asarray(w.v_new).reshape(B, S, Hkv, D)
+
+        def pro(x, wt, p):
+            x = list(x)
+            if wt is not None:
+                x = BF.rmsnorm(x, [float(v) for v in wt], w.eps)
+            if w.theta > 0:
+                x = BF.rope_pairs(x, p, inv, w.rope_layout, msc)
+            return x
+        for b in range(B):
+            for s in range(S):
+                p = int(w.pos[b]) + s
+                for h in range(Hq):
+                    qh[b, s, h] = pro(q[b, s, h], w.w_q, p)
+                if not 0 <= p < T:
+                    continue
+                for g in range(Hkv):
+                    kx = pro(kn[b, s, g], w.w_k, p)
+                    kc[b, g, p] = [_bf16_rne_scalar(v) for v in kx]
+                    vc[b, g, p] = vbits[b, s, g]
+    Kf = O.bf16_to_f64(kc).tolist()
+    Vf = O.bf16_to_f64(vc).tolist()
+    out = np.zeros((B, S, Hq, D))
+    lse = np.zeros((B, S, Hq))
+    for s in range(S):
+        back = (S - 1 - s) if w.causal else 0
+        lens_s = [int(n) - back for n in w.lens]
+        o_s, l_s = BF.attend(qh[:, s].tolist(), Kf, Vf, lens_s, w.window, scale)
+        out[:, s], lse[:, s] = np.array(o_s), np.array(l_s)
+    if S == 1:
+        qh, out, lse = qh[:, 0], out[:, 0], lse[:, 0]
+    return qh, kc, vc, out, lse
+
+
+def pin_decode_step_composition(O):
+    """oracle.decode_step (the reference of every GPU parity test) against the
+    step composed by hand from the brute force: rotated q, appended caches
+    (bit for bit), output and lse; with split=True also every partition's
+    (o_k, lse_k) against the brute force over that partition's rows alone."""
+    import workloads as WL
+    cases = [
+        # QK-norm + NeoX RoPE + window, split over partitions of 5 rows
+        ("5", dict(B=2, Hq=8, Hkv=2, D=8, L=23, window=11, part_tokens=5), 0.0),
+        # QK-norm + interleaved pairs + YaRN table (magnitude factor), explicit scale
+        ("2a", dict(B=2, Hq=4, Hkv=2, D=8, L=13, part_tokens=4, rope_layout="interleaved",
+                    rope_scaling=dict(kind="yarn", factor=4.0, orig_ctx=8)), 0.37),
+        # RoPE only, ragged lengths
+        ("3", dict(B=3, Hq=4, Hkv=1, D=8, L=17, lmin=2, part_tokens=6), 0.0),
+        # no prologue: q as given
+        ("4", dict(B=1, Hq=4, Hkv=2, D=8, L=19, peaky=0.2, part_tokens=7), 0.0),
+        # several causal tokens with QK-norm, NTK table, interleaved pairs, window
+        ("6", dict(B=2, Hq=4, Hkv=2, D=8, L=9, S=3, norm=True, window=6,
+                   rope_layout="interleaved", rope_scaling=dict(kind="ntk", factor=2.0)), 0.0),
+        # several bidirectional tokens of a fresh sequence, YaRN magnitude factor
+        ("7f", dict(B=1, Hq=4, Hkv=1, D=8, L=6, S=5, causal=False, norm=True,
+                    rope_scaling=dict(kind="yarn", factor=2.0, orig_ctx=4)), 0.0),
+    ]
+    for name, over, scale in cases:
+        w = WL.make(name, **over)
+        qh, kc, vc, out, lse = _step_bruteforce(O, w, scale)
+        for split in ((False, True) if w.S == 1 else (False,)):
+            res = O.decode_step(w, split=split, scale=scale)
+            what = f"decode_step {name} split={split}"
+            _close(res["q_hat"], qh, 1e-12, what + " q_hat")
+            assert np.array_equal(res["k_cache"], kc), what + " k_cache"
+            assert np.array_equal(res["v_cache"], vc), what + " v_cache"
+            _close(res["out"], out, 1e-12, what + " out")
+            fin = np.isfinite(lse)
+            assert np.array_equal(np.isfinite(res["lse"]), fin), what + " lse finiteness"
+            _close(res["lse"][fin], lse[fin], 1e-12, what + " lse")
+            if not split:
+                continue
+            # each partition alone: rows [lo + kP, lo + (k+1)P) of the window
+            Kf = O.bf16_to_f64(kc).tolist()
+            Vf = O.bf16_to_f64(vc).tolist()
+            P = w.part_tokens
+            for b in range(w.B):
+                n = min(max(int(w.lens[b]), 0), w.T)
+                lo = max(0, n - w.window) if w.window > 0 else 0
+                for k in range(res["lse_parts"].shape[-1]):
+                    a, e = min(lo + k * P, n), min(lo + (k + 1) * P, n)
+                    if a == e:
+                        assert np.all(res["lse_parts"][b, :, k] == -math.inf), what
+                        continue
+                    o_k, l_k = BF.attend([qh[b].tolist()], [Kf[b]], [Vf[b]], [e], e - a, scale)
+                    _close(res["o_parts"][b, :, k], o_k[0], 1e-12, what + " o_k")
+                    _close(res["lse_parts"][b, :, k], l_k[0], 1e-12, what + " lse_k")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

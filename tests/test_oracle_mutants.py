@@ -356,6 +356,45 @@ def _split_qkv_k_v_swapped(y, Hq, Hkv, D):
     return q, v, k
 
 
+# --- the whole step (decode_step composes the pieces above) ------------------------
+def _decode_step_variant(kind):
+    """decode_step with one composition slip; everything else as written."""
+    def f(w, split=False, scale=0.0):
+        q = R.bf16_to_f64(w.q)
+        S = getattr(w, "S", 1)
+        inv_freq, mscale = None, 1.0
+        if w.rope_scaling is not None and w.theta > 0:
+            inv_freq, mscale = R.rope_inv_freq_scaled(w.D, w.theta, **w.rope_scaling)
+        if kind == "drops_mscale":
+            mscale = 1.0
+        layout = "neox" if kind == "drops_layout" else w.rope_layout
+        if kind == "ignores_scale":
+            scale = 0.0
+        pro = R.qkv_prologue_multi if S > 1 else R.qkv_prologue
+        if w.pos is not None and not (kind == "multi_skips_prologue" and S > 1):
+            q_hat, kc, vc = pro(q, R.bf16_to_f64(w.k_new), R.bf16_to_f64(w.v_new), w.w_q,
+                                w.w_k, w.eps, w.theta, w.pos, w.k_cache, w.v_cache,
+                                inv_freq=inv_freq, layout=layout, mscale=mscale)
+        else:
+            q_hat, kc, vc = q, w.k_cache, w.v_cache
+        res = dict(q_hat=q_hat, k_cache=kc, v_cache=vc)
+        qa = q if kind == "attends_raw_q" else q_hat
+        ka, va = (w.k_cache, w.v_cache) if kind == "attends_pre_append_cache" else (kc, vc)
+        if S > 1:
+            causal = True if kind == "drops_causal" else w.causal
+            res["out"], res["lse"] = R.attend_multi(qa, ka, va, w.lens, w.window, scale,
+                                                    causal=causal)
+            return res
+        if split:
+            o, l = R.attend_partials(qa, ka, va, w.lens, w.window, scale, w.part_tokens)
+            res["o_parts"], res["lse_parts"] = o, l
+            res["out"], res["lse"] = R.lse_merge(o, l)
+        else:
+            res["out"], res["lse"] = R.attend(qa, ka, va, w.lens, w.window, scale)
+        return res
+    return f
+
+
 MUTANTS = {
     "bf16_truncate": {"f64_to_bf16": _bf16_truncate},
     "bf16_double_round": {"f64_to_bf16": _bf16_double_round},
@@ -403,6 +442,13 @@ MUTANTS = {
     "linear_drops_a_column": {"linear": _linear_drops_last_column},
     "split_qkv_k_v_swapped": {"split_qkv": _split_qkv_k_v_swapped},
     "prefill_bidirectional_first_token_rows": {"attend_multi": _multi_bidirectional_first_token_rows},
+    "step_attends_raw_q": {"decode_step": _decode_step_variant("attends_raw_q")},
+    "step_attends_pre_append_cache": {"decode_step": _decode_step_variant("attends_pre_append_cache")},
+    "step_drops_mscale": {"decode_step": _decode_step_variant("drops_mscale")},
+    "step_drops_layout": {"decode_step": _decode_step_variant("drops_layout")},
+    "step_drops_causal": {"decode_step": _decode_step_variant("drops_causal")},
+    "step_ignores_scale": {"decode_step": _decode_step_variant("ignores_scale")},
+    "step_multi_skips_prologue": {"decode_step": _decode_step_variant("multi_skips_prologue")},
 }
 
 
