@@ -1,14 +1,22 @@
 """Decode-attention benchmark on one MI355X.
 
 One step = one pass of the whole decode hot path over one batch: the fused
-prologue (QK-RMSNorm + NeoX RoPE + K/V append), the split-K attention pass
-and the log-sum-exp merge.  By default (--mode fused) that is one C-ABI call,
-gqa_decode_step (gqa_decode_step_multi with several query tokens per
-sequence), i.e. one kernel launch; --mode split makes it three calls
-(prologue, split-K pass, merge).  Every launch goes to torch's current
-stream and every input is already resident in HBM.  Before each timed step,
-a read-only sweep of a 1 GiB buffer evicts the KV window from the L2s and the
-256 MB Infinity Cache so it is read from HBM (outside the timed region).
+prologue (QK-RMSNorm + NeoX RoPE + K/V append, when the workload has one),
+the split-K attention pass and the log-sum-exp merge.  By default (--mode
+fused) that is one C-ABI call, gqa_decode_step (gqa_decode_step_multi with
+several query tokens per sequence), i.e. one kernel launch; --mode split
+makes it three calls (prologue, split-K pass, merge).  Every launch goes to
+torch's current stream and every input is already resident in HBM.  Before
+each timed step, a read-only sweep of a 1 GiB buffer evicts the KV rows from
+the L2s and the 256 MB Infinity Cache so they are read from HBM (outside the
+timed region).  --graph captures one step in a HIP graph and times its
+replays instead of eager launches.
+
+The default workload is the largest single-GPU one: long-context
+flash-decoding, L = 131072 rows, 64 partitions of 2048 rows merged by
+log-sum-exp (537 MB of K/V per step).  Timing runs in --rounds independent
+rounds of --steps steps each; ``ms_per_step`` is the mean of the round
+medians.
 
 Prints ONE JSON line.  ``value`` is the step's KV-read throughput: KV-cache
 bytes the step must read (K and V rows of every attended window, bf16) per
@@ -18,9 +26,14 @@ MI355X's 8 TB/s HBM peak, with its duration from HIP events (created without
 the system-scope fence) recorded on the launch stream around the kernel;
 ``traffic`` is the measured HBM bytes per launch from committed rocprofv3
 counters when they were taken on the current kernel source.
-``cpu_baseline`` times the fp64 CPU oracle on the same workload on this host.
+``context.read_ceiling`` is a plain streaming read of exactly the step's KV
+bytes (gqa_probe_stream_read, best of a few launch shapes) timed in the same
+run after the same sweep: what the part streams for that many bytes.
+``cpu_baseline`` times the fp64 CPU oracle on the same workload on this host,
+with all the host's BLAS threads and with one.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--rounds R]
+                       [--workload 4] [--mode fused|split] [--graph]
 """
 from __future__ import annotations
 
@@ -73,7 +86,13 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="5", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workload", default="4", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--rounds", type=int, default=3,
+                    help="independent timing rounds of --steps steps each")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the same-run streaming-read ceiling")
     ap.add_argument("--flush", default="read", choices=["read", "rmw", "none"],
                     help="cache sweep between steps: read a 1 GiB buffer (default), "
                          "read-modify-write it, or none (warm-cache figure)")
@@ -231,21 +250,29 @@ class _HipEvents:
         self.ev = []
 
 
+def _timed_reps(fn, min_seconds: float):
+    """(repetitions, seconds): call fn until min_seconds have passed (once at least)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            return reps, el
+
+
 def _cpu_baseline(w, min_seconds: float):
-    """Time the fp64 oracle's decode step on this host (a baseline, not a target)."""
+    """Time the fp64 oracle's decode step on this host (a baseline, not a
+    target): with every BLAS thread numpy has, then with one thread."""
     import threadpoolctl
     import workloads
     from oracle import reference as oracle
 
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode_step(w, split=False)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
+    reps, el = _timed_reps(lambda: oracle.decode_step(w, split=False), min_seconds)
+    with threadpoolctl.threadpool_limits(1):
+        reps1, el1 = _timed_reps(lambda: oracle.decode_step(w, split=False), min_seconds)
     kvb = workloads.kv_bytes(w)
     return {
         "value": round(kvb * reps / el / 1e9, 4),
@@ -253,10 +280,57 @@ def _cpu_baseline(w, min_seconds: float):
         "cores": threads,
         "kind": "oracle",
         "cpu_model": _cpu_model(),
+        "us_per_step": round(1e6 * el / reps),
+        "single_thread": {"value": round(kvb * reps1 / el1 / 1e9, 4), "unit": "GB/s",
+                          "cores": 1, "us_per_step": round(1e6 * el1 / reps1)},
         "sample": (f"{reps} full decode step(s) of the same workload (prologue + unsplit "
-                   f"attention, float64 numpy), {el:.1f} s wall, "
-                   f"{1e6 * el / reps:.0f} us/step"),
+                   f"attention, float64 numpy) on {threads} threads, {el:.1f} s wall, "
+                   f"{1e6 * el / reps:.0f} us/step; {reps1} on one thread, {el1:.1f} s, "
+                   f"{1e6 * el1 / reps1:.0f} us/step"),
     }
+
+
+# Launch shapes (workgroups, threads, loads in flight per thread) tried for
+# the streaming-read ceiling; the best median is reported.
+_CEILING_SHAPES = [(256, 256, 8), (256, 512, 8), (256, 1024, 4), (256, 256, 16),
+                   (512, 256, 8), (512, 512, 4), (1024, 256, 4), (2048, 256, 4)]
+
+
+def _read_ceiling(dev, nbytes: int, sweep, reps: int = 5):
+    """A plain streaming read of exactly ``nbytes`` bytes (one contiguous
+    buffer, each byte read once) after the same cache sweep as the timed
+    steps: the median over ``reps`` launches for each launch shape, best
+    shape reported."""
+    import torch
+    from gqa_attention_kv_amd import probe_stream_read
+
+    nb = nbytes - nbytes % 16
+    buf = torch.ones(nb // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(max(wg * th for wg, th, _ in _CEILING_SHAPES), dtype=torch.int32,
+                       device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = _HipEvents(2 * reps)
+    best = None
+    for wg, th, un in _CEILING_SHAPES:
+        probe_stream_read(buf, wg, th, un, sink=sink)       # warm the shape
+        ts = []
+        for i in range(reps):
+            sweep()
+            ev.record(2 * i, stream)
+            probe_stream_read(buf, wg, th, un, sink=sink)
+            ev.record(2 * i + 1, stream)
+        torch.cuda.synchronize()
+        ts = [ev.ms(2 * i, 2 * i + 1) for i in range(reps)]
+        med = statistics.median(ts)
+        if best is None or med < best[0]:
+            best = (med, wg, th, un)
+    ev.close()
+    med, wg, th, un = best
+    gbps = nb / (med * 1e-3) / 1e9
+    return {"bytes": nb, "us": round(1e3 * med, 2), "GBps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4),
+            "shape": {"workgroups": wg, "threads": th, "loads_in_flight": un},
+            "kernel": "stream_read_kernel"}
 
 
 def _cpu_baseline_prefill(w, min_seconds: float):
@@ -507,6 +581,32 @@ def main():
         elif args.flush == "rmw":
             flush.add_(1)
 
+    one_call = mode in ("fused", "prefill_step") or args.graph
+
+    def run_once():
+        if mode in ("fused", "prefill_step"):
+            step.run()
+        else:
+            step.prologue()
+            step.attention()
+            step.merge()
+
+    graph = None
+    if args.graph:
+        # capture one whole step (all of its launches); warm up on a side
+        # stream first, as capture requires
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                run_once()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_once()
+        torch.cuda.synchronize()
+
     stream = torch.cuda.current_stream(dev).cuda_stream   # every launch goes here
     timer = _HipEvents(4 * args.steps)
 
@@ -514,7 +614,11 @@ def main():
         sweep()
         rec = (lambda k: timer.record(4 * i + k, stream)) if i is not None else (lambda k: None)
         rec(0)
-        if mode in ("fused", "prefill_step"):   # one call: one event pair
+        if graph is not None:
+            graph.replay()
+            rec(3)
+            return
+        if one_call:                           # one call: one event pair
             step.run()
             rec(3)
             return
@@ -528,34 +632,48 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    step_ms = [timer.ms(4 * i, 4 * i + 3) for i in range(args.steps)]
-    if mode in ("fused", "prefill_step"):   # the call is the dominant kernel('s launches)
-        pro_ms = merge_ms = [0.0]
-        attn_ms = step_ms
-    else:
-        pro_ms = [timer.ms(4 * i, 4 * i + 1) for i in range(args.steps)]
-        attn_ms = [timer.ms(4 * i + 1, 4 * i + 2) for i in range(args.steps)]
-        merge_ms = [timer.ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]
-    timer.close()
-    mean_step = statistics.fmean(step_ms)
-    mean_attn = statistics.fmean(attn_ms)
-
-    def run_once():
-        if mode in ("fused", "prefill_step"):
-            step.run()
+    rounds, step_all, attn_all, pro_all, merge_all = [], [], [], [], []
+    wall = 0.0
+    for r in range(args.rounds):
+        wall0 = time.perf_counter()
+        for i in range(args.steps):
+            one_step(i)
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - wall0
+        st = [timer.ms(4 * i, 4 * i + 3) for i in range(args.steps)]
+        if one_call:
+            at, pr, mg = st, [0.0], [0.0]
         else:
-            step.prologue()
-            step.attention()
-            step.merge()
-    context = None if args.no_context else _context(dev, run_once)
+            pr = [timer.ms(4 * i, 4 * i + 1) for i in range(args.steps)]
+            at = [timer.ms(4 * i + 1, 4 * i + 2) for i in range(args.steps)]
+            mg = [timer.ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)]
+        ss = sorted(st)
+        rounds.append({"median_us": round(1e3 * statistics.median(st), 2),
+                       "mean_us": round(1e3 * statistics.fmean(st), 2),
+                       "p10_us": round(1e3 * ss[len(ss) // 10], 2),
+                       "p90_us": round(1e3 * ss[(9 * len(ss)) // 10], 2),
+                       "attn_median_us": round(1e3 * statistics.median(at), 2)})
+        step_all += st
+        attn_all.append(statistics.median(at))
+        pro_all += pr
+        merge_all += mg
+    timer.close()
+    # the mean of the round medians
+    mean_step = statistics.fmean(statistics.median(step_all[r * args.steps:(r + 1) * args.steps])
+                                 for r in range(args.rounds))
+    mean_attn = statistics.fmean(attn_all)
+
+    context = {}
+    if not args.no_context:
+        context.update(_context(dev, graph.replay if graph is not None else run_once))
+    ceiling = None
+    if not args.no_ceiling and mode not in ("prefill", "prefill_step"):
+        ceiling = _read_ceiling(dev, kvb, sweep)
+        context["read_ceiling"] = ceiling
     value = kvb / (mean_step * 1e-3) / 1e9
     achieved = kvb / (mean_attn * 1e-3) / 1e9
+    if ceiling:
+        ceiling["step_frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
 
     finite = bool(torch.isfinite(step.out.float()).all().item())
 
@@ -583,6 +701,9 @@ def main():
             "traffic": traffic,
             "flops_per_launch": flops,
         }
+        dtype = ("bf16 MFMA (bf16 q and P), fp32 accumulate and softmax"
+                 if w.out_dtype == "bf16" else
+                 "bf16 MFMA (P as a bf16 hi+lo pair), fp32 accumulate and softmax")
     else:
         roofline = {
             "bound": "hbm",
@@ -593,7 +714,10 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "bytes_per_launch": kvb,
         }
+        dtype = ("bf16 K/V on bf16 MFMA with q and P as bf16 hi+lo pairs (~16 significant "
+                 "bits), fp32 accumulate, softmax and merge")
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -601,19 +725,20 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "rounds": args.rounds,
         "ms_per_step": round(mean_step, 5),
         "us_per_step": round(1e3 * mean_step, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if mode in ("prefill", "prefill_step") else "f32",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {
             "workload": WORKLOAD_NAMES[args.workload],
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D, "T": w.T,
             "query_tokens": w.S,
             "window": w.window, "part_tokens": w.part_tokens, "out_dtype": w.out_dtype,
-            "path": mode,
+            "path": mode + (" (HIP graph replay)" if args.graph else ""),
             **({"key_splits": splits} if mode in ("prefill", "prefill_step") else {}),
             "prologue": ("qk_rmsnorm+rope+append" if w.w_q is not None else
                          "rope+append") if w.pos is not None else "none",
@@ -624,14 +749,13 @@ def main():
         "roofline": roofline,
         "kernels_us": {
             "mode": mode,
-            "prologue": round(1e3 * statistics.fmean(pro_ms), 2),
+            "graph": bool(args.graph),
+            "prologue": round(1e3 * statistics.fmean(pro_all), 2),
             "attn": round(1e3 * mean_attn, 2),
-            "merge": round(1e3 * statistics.fmean(merge_ms), 2),
-            "step_median": round(1e3 * statistics.median(step_ms), 2),
-            "step_p10": round(1e3 * sorted(step_ms)[len(step_ms) // 10], 2),
-            "step_p90": round(1e3 * sorted(step_ms)[(9 * len(step_ms)) // 10], 2),
+            "merge": round(1e3 * statistics.fmean(merge_all), 2),
+            "rounds": rounds,
         },
-        "context": context,
+        "context": context or None,
         "wall_s_timed_loop": round(wall, 4),
         "output_finite": finite,
         "cpu_baseline": cpu,

@@ -15,7 +15,7 @@ Functions follow the C entry points' names without the ``gqa_`` prefix:
 ``prefill_step``, ``qkv_gemv``,
 ``rope_table``, ``splitk_workspace_bytes``, ``splitk_multi_workspace_bytes``,
 ``decode_step_workspace_bytes``, ``decode_step_multi_workspace_bytes``,
-``num_partitions``.
+``num_partitions``; and the measurement helper ``probe_stream_read``.
 """
 from __future__ import annotations
 
@@ -34,7 +34,7 @@ __all__ = [
     "attn_decode_multi", "attn_decode_splitk_multi", "attn_decode_merge_multi",
     "splitk_multi_workspace_bytes", "decode_step_multi", "decode_step_multi_workspace_bytes",
     "attn_prefill", "qkv_gemv", "prefill_workspace_bytes", "prefill_default_splits",
-    "prefill_step",
+    "prefill_step", "probe_stream_read",
     "F32", "BF16", "SYMBOLS", "ROPE_NEOX", "ROPE_INTERLEAVED", "ROPE_KINDS",
 ]
 
@@ -96,6 +96,7 @@ SYMBOLS = {
     "gqa_attn_prefill_default_splits": (_i, [_i, _i, _i, _i]),
     "gqa_attn_prefill_split": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _f, _i, _p, _sz, _p, _i,
                                     _p, _i, _i, _i, _i, _i, _p]),
+    "gqa_probe_stream_read": (_i, [_p, _sz, _i, _i, _i, _p, _p]),
 }
 for _name, (_res, _args) in SYMBOLS.items():
     _fn = getattr(lib, _name)
@@ -536,6 +537,29 @@ def qkv_gemv(x, w, out=None, out_dtype=torch.bfloat16):
     _check(lib.gqa_qkv_gemv(_ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(out),
                             _dtype_code(out, "out"), out.stride(0), M, N, K, _stream(dev)))
     return out
+
+
+def probe_stream_read(buf, workgroups: int = 256, threads: int = 256, unroll: int = 8,
+                      sink=None, nbytes: Optional[int] = None):
+    """Measurement helper (not part of the attention path): read the first
+    ``nbytes`` bytes (default: all) of the contiguous device tensor ``buf``
+    once, one contiguous share per workgroup, ``unroll`` 16-byte loads in
+    flight per thread.  ``sink`` is a device uint32/int32 tensor of at least
+    workgroups * threads elements (allocated when None)."""
+    _dev(buf, "buf")
+    _contig(buf, "buf")
+    dev = buf.device
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if n > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    if sink is None:
+        sink = torch.empty(workgroups * threads, dtype=torch.int32, device=dev)
+    _dev(sink, "sink", dev)
+    if sink.numel() * sink.element_size() < 4 * workgroups * threads:
+        raise ValueError("sink must hold workgroups * threads uint32")
+    _check(lib.gqa_probe_stream_read(_ptr(buf), n, workgroups, threads, unroll, _ptr(sink),
+                                     _stream(dev)))
+    return sink
 
 
 def splitk_multi_workspace_bytes(B: int, S: int, Hq: int, D: int, T: int, window: int,

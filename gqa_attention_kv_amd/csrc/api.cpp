@@ -416,6 +416,17 @@ int gqa_qkv_gemv(const uint16_t* x, int64_t x_stride, const uint16_t* w, int64_t
   return gqa::launch_qkv_gemv(a, stream);
 }
 
+int gqa_probe_stream_read(const void* buf, size_t bytes, int workgroups, int threads, int unroll,
+                          uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink) return GQA_ERR_NULL;
+  if (bytes < 16 || bytes > ((size_t)1 << 31) || workgroups < 1 || workgroups > 65536)
+    return GQA_ERR_SHAPE;
+  if (bytes % 16 != 0 || !aligned(buf, 16) || !aligned(sink, 4)) return GQA_ERR_ALIGN;
+  if (threads < 64 || threads > 1024 || threads % 64 != 0) return GQA_ERR_VALUE;
+  if (unroll != 4 && unroll != 8 && unroll != 16) return GQA_ERR_UNSUPPORTED;
+  return gqa::launch_stream_read(buf, (uint32_t)bytes, workgroups, threads, unroll, sink, stream);
+}
+
 int gqa_num_partitions(int T, int window, int part_tokens) {
   if (T < 1 || part_tokens < 1) return 0;
   return num_parts(T, window, part_tokens);

@@ -143,5 +143,7 @@ int launch_merge(const MergeArgs& a, hipStream_t s);
 int prefill_rows_per_block();                                 // (token, head) rows per workgroup
 int launch_attn_prefill(const PrefillArgs& a, hipStream_t s);
 int launch_qkv_gemv(const GemvArgs& a, hipStream_t s);
+int launch_stream_read(const void* buf, uint32_t bytes, int workgroups, int threads, int unroll,
+                       uint32_t* sink, hipStream_t s);   // read-ceiling probe
 
 }  // namespace gqa

@@ -457,6 +457,24 @@ int gqa_qkv_gemv(const uint16_t* x, int64_t x_stride, const uint16_t* w, int64_t
                  void* y, gqa_dtype_t y_dtype, int64_t y_stride, int M, int N, int K,
                  hipStream_t stream);
 
+/* Measurement helper, not part of the attention path: reads `bytes` bytes
+ * of the device buffer `buf` once, as one contiguous share per workgroup
+ * (`workgroups` workgroups of `threads` threads, `unroll` 16-byte
+ * non-temporal loads in flight per thread), and does nothing with them.
+ * Timed around the launch it gives the streaming-read rate the part reaches
+ * for that many bytes: the ceiling a decode step that reads each K/V row
+ * once can approach.  The fusedtok README ("Benchmarks") rates its decode
+ * kernel by the cache-streaming bandwidth it reaches; this is the bare
+ * stream it is measured against.
+ * buf 16-byte aligned, 16 <= bytes <= 2^31 and a multiple of 16, else
+ * GQA_ERR_SHAPE / GQA_ERR_ALIGN; 1 <= workgroups <= 65536; threads a
+ * multiple of 64 in [64, 1024] (GQA_ERR_VALUE); unroll 4, 8 or 16
+ * (GQA_ERR_UNSUPPORTED).  `sink` is caller-owned device memory of
+ * workgroups * threads uint32 that the kernel may write (in practice it
+ * never does).  Nothing is allocated. */
+int gqa_probe_stream_read(const void* buf, size_t bytes, int workgroups, int threads, int unroll,
+                          uint32_t* sink, hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char* gqa_status_string(int status);
 

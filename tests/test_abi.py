@@ -166,3 +166,22 @@ def test_status_strings(G):
     for s in range(-7, 1):
         assert G.lib.gqa_status_string(s)
     assert G.lib.gqa_status_string(-99) == b"unknown status"
+
+
+def test_probe_validation(G):
+    f = G.lib.gqa_probe_stream_read
+
+    def call(**kw):
+        a = dict(buf=A16, n=1 << 20, wg=256, th=256, u=8, sink=A16)
+        a.update(kw)
+        return f(a["buf"], a["n"], a["wg"], a["th"], a["u"], a["sink"], None)
+    assert call(buf=None) == -1
+    assert call(sink=None) == -1
+    assert call(n=8) == -2
+    assert call(n=(1 << 31) + 16) == -2
+    assert call(wg=0) == -2
+    assert call(n=(1 << 20) + 8) == -6
+    assert call(buf=A16 + 8) == -6
+    assert call(th=96) == -7
+    assert call(th=2048) == -7
+    assert call(u=5) == -3
