@@ -15,7 +15,8 @@ Functions follow the C entry points' names without the ``gqa_`` prefix:
 ``prefill_step``, ``qkv_gemv``,
 ``rope_table``, ``splitk_workspace_bytes``, ``splitk_multi_workspace_bytes``,
 ``decode_step_workspace_bytes``, ``decode_step_multi_workspace_bytes``,
-``num_partitions``; and the measurement helper ``probe_stream_read``.
+``num_partitions``, ``decode_step_noalloc`` (no workspace: the library's
+static scratch); and the measurement helper ``probe_stream_read``.
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ __all__ = [
     "attn_decode_multi", "attn_decode_splitk_multi", "attn_decode_merge_multi",
     "splitk_multi_workspace_bytes", "decode_step_multi", "decode_step_multi_workspace_bytes",
     "attn_prefill", "qkv_gemv", "prefill_workspace_bytes", "prefill_default_splits",
-    "prefill_step", "probe_stream_read",
+    "prefill_step", "probe_stream_read", "decode_step_noalloc",
     "F32", "BF16", "SYMBOLS", "ROPE_NEOX", "ROPE_INTERLEAVED", "ROPE_KINDS",
 ]
 
@@ -97,6 +98,9 @@ SYMBOLS = {
     "gqa_attn_prefill_split": (_i, [_p, _i, _p, _p, _p, _i, _i, _i, _f, _i, _p, _sz, _p, _i,
                                     _p, _i, _i, _i, _i, _i, _p]),
     "gqa_probe_stream_read": (_i, [_p, _sz, _i, _i, _i, _p, _p]),
+    "gqa_decode_step_noalloc": (_i, [_p, _p, _p, _i, _i64, _i64, _p, _p, _f, _p, _d, _i, _p,
+                                     _i, _p, _p, _p, _i, _f, _i, _p, _i, _p, _p, _i, _i, _i,
+                                     _i, _i, _p]),
 }
 for _name, (_res, _args) in SYMBOLS.items():
     _fn = getattr(lib, _name)
@@ -686,10 +690,40 @@ def decode_step_multi(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens:
     return out, workspace
 
 
+def decode_step_noalloc(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens: int,
+                        inv_freq=None, rope_mscale: float = 1.0, rope_layout="neox",
+                        q_norm_w=None, k_norm_w=None, eps: float = 1e-6, window: int = 0,
+                        scale: float = 0.0, out=None, out_dtype=torch.float32, lse_out=None,
+                        q_out=None):
+    """``decode_step_multi`` without a workspace: the library's static
+    per-device scratch holds the tickets and partials (for callers that
+    cannot allocate; ``out`` must then be given, since allocating it here
+    would defeat the purpose).  Calls that overlap in time on one GPU race.
+    Returns ``out``."""
+    if out is None:
+        raise ValueError("decode_step_noalloc needs a preallocated out")
+    a = _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, None,
+                     q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out, multi=True,
+                     no_workspace=True)
+    dev, B, S, Hq, Hkv, D, T, code, _, out, _, pro = a
+    f = _host_table(inv_freq, D)
+    _check(lib.gqa_decode_step_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), code, q.stride(0),
+        k_new.stride(0) if pro else S * Hkv * D,
+        _ptr(q_norm_w), _ptr(k_norm_w), float(eps), None if f is None else f.ctypes.data,
+        float(rope_mscale), _layout_code(rope_layout), _ptr(pos), S,
+        _ptr(k_cache), _ptr(v_cache), _ptr(lens), int(window), float(scale), int(part_tokens),
+        _ptr(out), _dtype_code(out, "out"), _ptr(lse_out), _ptr(q_out), B, Hq, Hkv, D, T,
+        _stream(dev)))
+    return out
+
+
 def _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, workspace,
-                 q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out, multi=False):
+                 q_norm_w, k_norm_w, window, out, out_dtype, lse_out, q_out, multi=False,
+                 no_workspace=False):
     """Checks of the one-launch step.  ``multi``: q, k_new, v_new, out and
-    q_out carry a token axis ([B,S,H,D], tokens and heads dense)."""
+    q_out carry a token axis ([B,S,H,D], tokens and heads dense).
+    ``no_workspace``: the call takes no workspace (none is allocated)."""
     dev = k_cache.device
     pro = pos is not None
     if (k_new is None) == pro or (v_new is None) == pro:
@@ -735,12 +769,13 @@ def _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, work
             if w.dtype != torch.float32 or tuple(w.shape) != (D,):
                 raise ValueError(f"{nm} must be float32 [D]")
             _contig(w, nm)
-    need = (decode_step_multi_workspace_bytes(B, S, Hq, Hkv, D, T, window, part_tokens) if multi
-            else decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens))
-    if workspace is None:
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
-    _dev(workspace, "workspace", dev)
-    _contig(workspace, "workspace")
+    if not no_workspace:
+        need = (decode_step_multi_workspace_bytes(B, S, Hq, Hkv, D, T, window, part_tokens)
+                if multi else decode_step_workspace_bytes(B, Hq, Hkv, D, T, window, part_tokens))
+        if workspace is None:
+            workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+        _dev(workspace, "workspace", dev)
+        _contig(workspace, "workspace")
     rows = (B, S, Hq) if multi else (B, Hq)
     if out is None:
         out = torch.empty(rows + (D,), dtype=out_dtype, device=dev)
@@ -761,7 +796,7 @@ def _step_checks(q, k_new, v_new, pos, k_cache, v_cache, lens, part_tokens, work
         _contig(q_out, "q_out")
         if q_out.dtype != torch.float32 or tuple(q_out.shape) != rows + (D,):
             raise ValueError(f"q_out must be float32 {list(rows + (D,))}")
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if multi:
         return dev, B, S, Hq, Hkv, D, T, code, workspace, out, nbytes, pro
     return dev, B, Hq, Hkv, D, T, code, workspace, out, nbytes, pro

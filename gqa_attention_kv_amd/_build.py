@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.cpp", "prologue.hip", "attn_decode_mfma.hip", "merge.hip", "attn_prefill_mfma.hip",
-           "qkv_gemv.hip", "probe.hip"]
+           "qkv_gemv.hip", "probe.hip", "step_noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -82,6 +82,72 @@ float softmax_qscale(float scale, int D) {
 
 }  // namespace
 
+namespace gqa {
+
+size_t step_lse_bytes(int B, int S, int Hq, int num_parts) {
+  return align256((size_t)B * S * Hq * num_parts * sizeof(float));
+}
+
+int decode_step_args(const void* q, const void* k_new, const void* v_new,
+                     gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                     const float* q_norm_w, const float* k_norm_w, float eps,
+                     const double* inv_freq, double rope_mscale, int rope_layout,
+                     const int32_t* pos, int S,
+                     uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                     int window, float scale, int part_tokens,
+                     void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                     int B, int Hq, int Hkv, int D, int T, KernelArgs* args) {
+  if (!q || !k_cache || !v_cache || !lens || !out) return GQA_ERR_NULL;
+  // the prologue inputs come all together or not at all
+  const bool pro = pos != nullptr;
+  if ((k_new != nullptr) != pro || (v_new != nullptr) != pro) return GQA_ERR_NULL;
+  if ((q_norm_w == nullptr) != (k_norm_w == nullptr)) return GQA_ERR_NULL;
+  if (!pro && (q_norm_w != nullptr || q_out != nullptr || inv_freq != nullptr))
+    return GQA_ERR_NULL;
+  int rc = check_shapes(B, Hq, Hkv, D, T);
+  if (rc) return rc;
+  if ((rc = check_tokens(S, B, Hq, Hkv))) return rc;
+  if ((rc = check_split(B, Hkv, T, window, part_tokens, S))) return rc;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
+  if (q_bstride < (int64_t)S * Hq * D || kv_bstride < (int64_t)S * Hkv * D) return GQA_ERR_SHAPE;
+  if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
+  if ((rc = check_rope(inv_freq, rope_mscale, rope_layout, D))) return rc;
+  if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
+  const uintptr_t ea = in_dtype == GQA_BF16 ? 2 : 4;
+  // q rows are read as 16-byte vectors: the batch stride must keep that alignment
+  if (!aligned(q, 16) || (q_bstride * (int64_t)ea) % 16 != 0 || !aligned(k_new, ea) ||
+      !aligned(v_new, ea) || !aligned(q_norm_w, 16) || !aligned(k_norm_w, 4) ||
+      !aligned(pos, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(lens, 4) ||
+      !aligned(out, 16) || !aligned(lse_out, 4) || !aligned(q_out, 16))
+    return GQA_ERR_ALIGN;
+  const int np = num_parts(T, window, part_tokens, S);
+  // the merge reads one (sequence, KV head)'s partials -- rows of S tokens,
+  // Hq apart -- with 32-bit offsets
+  const int64_t team_rows = (int64_t)(S - 1) * Hq + Hq / Hkv;
+  if (team_rows * np * D * 4 >= (INT64_C(1) << 31)) return GQA_ERR_SHAPE;
+  KernelArgs& a = *args;
+  a = KernelArgs{};
+  a.q = q; a.q_bstride = q_bstride; a.in_bf16 = in_dtype == GQA_BF16;
+  a.S = S; a.q_sstride = (int64_t)Hq * D;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.k_cache_w = k_cache; a.v_cache_w = v_cache;
+  a.lens = lens; a.window = window; a.qscale = softmax_qscale(scale, D);
+  a.part_tokens = part_tokens; a.num_parts = np;
+  a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
+  a.k_new = k_new; a.v_new = v_new; a.kv_bstride = kv_bstride;
+  a.wq = q_norm_w; a.wk = k_norm_w; a.eps = eps;
+  a.rope = pro && inv_freq != nullptr;
+  a.rope_interleaved = rope_layout == GQA_ROPE_INTERLEAVED;
+  a.rope_mscale = (float)rope_mscale;
+  a.pos = pos; a.q_out = q_out;
+  if (a.rope)
+    for (int i = 0; i < D / 2; ++i) a.inv_freq_rev[i] = inv_freq[i] / 6.283185307179586476925;
+  return GQA_OK;
+}
+
+}  // namespace gqa
+
 extern "C" {
 
 const char* gqa_status_string(int status) {
@@ -94,6 +160,7 @@ const char* gqa_status_string(int status) {
     case GQA_ERR_LAUNCH: return "HIP kernel launch failed";
     case GQA_ERR_ALIGN: return "pointer not aligned as required";
     case GQA_ERR_VALUE: return "scalar argument out of range";
+    case GQA_ERR_SCRATCH: return "shape too large for the static scratch of the no-allocation step";
     default: return "unknown status";
   }
 }
@@ -559,60 +626,22 @@ int gqa_decode_step_multi(const void* q, const void* k_new, const void* v_new,
                           void* workspace, size_t workspace_bytes,
                           void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
                           int B, int Hq, int Hkv, int D, int T, hipStream_t stream) {
-  if (!q || !k_cache || !v_cache || !lens || !workspace || !out) return GQA_ERR_NULL;
-  // the prologue inputs come all together or not at all
-  const bool pro = pos != nullptr;
-  if ((k_new != nullptr) != pro || (v_new != nullptr) != pro) return GQA_ERR_NULL;
-  if ((q_norm_w == nullptr) != (k_norm_w == nullptr)) return GQA_ERR_NULL;
-  if (!pro && (q_norm_w != nullptr || q_out != nullptr || inv_freq != nullptr))
-    return GQA_ERR_NULL;
-  int rc = check_shapes(B, Hq, Hkv, D, T);
+  if (!workspace) return GQA_ERR_NULL;
+  gqa::KernelArgs a{};
+  int rc = gqa::decode_step_args(q, k_new, v_new, in_dtype, q_bstride, kv_bstride, q_norm_w,
+                                 k_norm_w, eps, inv_freq, rope_mscale, rope_layout, pos, S,
+                                 k_cache, v_cache, lens, window, scale, part_tokens, out,
+                                 out_dtype, lse_out, q_out, B, Hq, Hkv, D, T, &a);
   if (rc) return rc;
-  if ((rc = check_tokens(S, B, Hq, Hkv))) return rc;
-  if ((rc = check_split(B, Hkv, T, window, part_tokens, S))) return rc;
-  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GQA_ERR_UNSUPPORTED;
-  if (q_bstride < (int64_t)S * Hq * D || kv_bstride < (int64_t)S * Hkv * D) return GQA_ERR_SHAPE;
-  if (q_bstride > kMaxIndex / B || kv_bstride > kMaxIndex / B) return GQA_ERR_SHAPE;
-  if (!(eps >= 0.0f) || !isfinite(eps)) return GQA_ERR_VALUE;
-  if ((rc = check_rope(inv_freq, rope_mscale, rope_layout, D))) return rc;
-  if (isnan(scale) || isinf(scale)) return GQA_ERR_VALUE;
-  const uintptr_t ea = in_dtype == GQA_BF16 ? 2 : 4;
-  // q rows are read as 16-byte vectors: the batch stride must keep that alignment
-  if (!aligned(q, 16) || (q_bstride * (int64_t)ea) % 16 != 0 || !aligned(k_new, ea) ||
-      !aligned(v_new, ea) || !aligned(q_norm_w, 16) || !aligned(k_norm_w, 4) ||
-      !aligned(pos, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(lens, 4) ||
-      !aligned(workspace, 256) || !aligned(out, 16) || !aligned(lse_out, 4) ||
-      !aligned(q_out, 16))
-    return GQA_ERR_ALIGN;
+  if (!aligned(workspace, 256)) return GQA_ERR_ALIGN;
   if (workspace_bytes <
       gqa_decode_step_multi_workspace_bytes(B, S, Hq, Hkv, D, T, window, part_tokens))
     return GQA_ERR_WORKSPACE;
-  const int np = num_parts(T, window, part_tokens, S);
-  // the merge reads one (sequence, KV head)'s partials -- rows of S tokens,
-  // Hq apart -- with 32-bit offsets
-  const int64_t team_rows = (int64_t)(S - 1) * Hq + Hq / Hkv;
-  if (team_rows * np * D * 4 >= (INT64_C(1) << 31)) return GQA_ERR_SHAPE;
-  gqa::KernelArgs a{};
-  a.q = q; a.q_bstride = q_bstride; a.in_bf16 = in_dtype == GQA_BF16;
-  a.S = S; a.q_sstride = (int64_t)Hq * D;
-  a.k_cache = k_cache; a.v_cache = v_cache; a.k_cache_w = k_cache; a.v_cache_w = v_cache;
-  a.lens = lens; a.window = window; a.qscale = softmax_qscale(scale, D);
-  a.part_tokens = part_tokens; a.num_parts = np;
   char* ws = static_cast<char*>(workspace);
   a.ws_lse = reinterpret_cast<float*>(ws);
-  a.ws_o = reinterpret_cast<float*>(ws + align256(lse_bytes((size_t)B * S * Hq, np)));
+  a.ws_o = reinterpret_cast<float*>(ws + gqa::step_lse_bytes(B, S, Hq, a.num_parts));
   a.ws_cnt = reinterpret_cast<uint32_t*>(
       ws + align256(gqa_splitk_multi_workspace_bytes(B, S, Hq, D, T, window, part_tokens)));
-  a.out = out; a.out_bf16 = out_dtype == GQA_BF16; a.lse_out = lse_out;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.T = T;
-  a.k_new = k_new; a.v_new = v_new; a.kv_bstride = kv_bstride;
-  a.wq = q_norm_w; a.wk = k_norm_w; a.eps = eps;
-  a.rope = pro && inv_freq != nullptr;
-  a.rope_interleaved = rope_layout == GQA_ROPE_INTERLEAVED;
-  a.rope_mscale = (float)rope_mscale;
-  a.pos = pos; a.q_out = q_out;
-  if (a.rope)
-    for (int i = 0; i < D / 2; ++i) a.inv_freq_rev[i] = inv_freq[i] / 6.283185307179586476925;
   return gqa::launch_decode_step(a, stream);
 }
 

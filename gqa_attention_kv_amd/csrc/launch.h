@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/gqa_decode.h"
+
 namespace gqa {
 
 constexpr int kMaxHalfDim = 64;   // D/2 for the largest supported head dim
@@ -143,6 +145,20 @@ int launch_merge(const MergeArgs& a, hipStream_t s);
 int prefill_rows_per_block();                                 // (token, head) rows per workgroup
 int launch_attn_prefill(const PrefillArgs& a, hipStream_t s);
 int launch_qkv_gemv(const GemvArgs& a, hipStream_t s);
+// Host checks of a fused decode step's arguments (all but its workspace),
+// shared by gqa_decode_step_multi and gqa_decode_step_noalloc: fills `a`
+// except ws_lse / ws_o / ws_cnt and returns GQA_OK, or a negative status.
+int decode_step_args(const void* q, const void* k_new, const void* v_new,
+                     gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                     const float* q_norm_w, const float* k_norm_w, float eps,
+                     const double* inv_freq, double rope_mscale, int rope_layout,
+                     const int32_t* pos, int S,
+                     uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                     int window, float scale, int part_tokens,
+                     void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                     int B, int Hq, int Hkv, int D, int T, KernelArgs* a);
+// Bytes of the step's lse partials [B,S,Hq,num_parts] fp32, rounded up to 256.
+size_t step_lse_bytes(int B, int S, int Hq, int num_parts);
 int launch_stream_read(const void* buf, uint32_t bytes, int workgroups, int threads, int unroll,
                        uint32_t* sink, hipStream_t s);   // read-ceiling probe
 

@@ -61,7 +61,9 @@ enum {
   GQA_ERR_WORKSPACE = -4,   /* split-K workspace too small                 */
   GQA_ERR_LAUNCH = -5,      /* HIP reported an error for the launch        */
   GQA_ERR_ALIGN = -6,       /* a pointer lacks the required alignment      */
-  GQA_ERR_VALUE = -7        /* a scalar argument is out of its range       */
+  GQA_ERR_VALUE = -7,       /* a scalar argument is out of its range       */
+  GQA_ERR_SCRATCH = -8      /* the shape needs more than the library's
+                               static scratch (gqa_decode_step_noalloc)     */
 };
 
 /*
@@ -456,6 +458,39 @@ int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,
 int gqa_qkv_gemv(const uint16_t* x, int64_t x_stride, const uint16_t* w, int64_t w_stride,
                  void* y, gqa_dtype_t y_dtype, int64_t y_stride, int M, int N, int K,
                  hipStream_t stream);
+
+/*
+ * gqa_decode_step_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): gqa_decode_step_multi with the same arguments except
+ * the workspace, which is instead a file-scope device array of the library,
+ * 8 MiB on each device it runs on, held until the process ends.  The call
+ * allocates nothing and calls no allocating routine.
+ *   Limits: B * Hkv <= 4096 arrival tickets, and the split-K partials,
+ *   256-byte-rounded B*S*Hq*NP*4 bytes of lse plus B*S*Hq*NP*D*4 bytes of o
+ *   (NP = partitions, as for gqa_splitk_multi_workspace_bytes), within
+ *   8 MiB - 16 KiB; beyond them it returns GQA_ERR_SCRATCH and enqueues
+ *   nothing.  (For example B=1, Hq=32, L=131072, P=2048 needs 1.01 MiB, as
+ *   does B=8, Hq=64, window 4096, P=1024.)
+ *   The step runs on the current device; `stream` must belong to it.  The
+ *   first call on a device also enqueues, ahead of the step, one small
+ *   kernel that zeroes the tickets.
+ *   Every call on a device shares that device's array: calls that overlap
+ *   in time on one device (on different streams, or from several host
+ *   threads without ordering) race and give wrong results.  Calls ordered
+ *   on one stream are safe; each completed call leaves the tickets at zero,
+ *   the partials are rewritten by every call.
+ * Other arguments, results and errors as for gqa_decode_step_multi.
+ */
+int gqa_decode_step_noalloc(const void* q, const void* k_new, const void* v_new,
+                            gqa_dtype_t in_dtype, int64_t q_bstride, int64_t kv_bstride,
+                            const float* q_norm_w, const float* k_norm_w, float eps,
+                            const double* inv_freq, double rope_mscale, int rope_layout,
+                            const int32_t* pos, int S,
+                            uint16_t* k_cache, uint16_t* v_cache, const int32_t* lens,
+                            int window, float scale, int part_tokens,
+                            void* out, gqa_dtype_t out_dtype, float* lse_out, float* q_out,
+                            int B, int Hq, int Hkv, int D, int T, hipStream_t stream);
 
 /* Measurement helper, not part of the attention path: reads `bytes` bytes
  * of the device buffer `buf` once, as one contiguous share per workgroup
