@@ -311,6 +311,7 @@ def _read_ceiling(dev, nbytes: int, sweep, reps: int = 5):
     stream = torch.cuda.current_stream(dev).cuda_stream
     ev = _HipEvents(2 * reps)
     best = None
+    every = {}
     for wg, th, un in _CEILING_SHAPES:
         probe_stream_read(buf, wg, th, un, sink=sink)       # warm the shape
         ts = []
@@ -322,6 +323,7 @@ def _read_ceiling(dev, nbytes: int, sweep, reps: int = 5):
         torch.cuda.synchronize()
         ts = [ev.ms(2 * i, 2 * i + 1) for i in range(reps)]
         med = statistics.median(ts)
+        every[f"{wg}x{th}x{un}"] = round(1e3 * med, 2)
         if best is None or med < best[0]:
             best = (med, wg, th, un)
     ev.close()
@@ -330,7 +332,7 @@ def _read_ceiling(dev, nbytes: int, sweep, reps: int = 5):
     return {"bytes": nb, "us": round(1e3 * med, 2), "GBps": round(gbps, 1),
             "frac_of_peak": round(gbps / HBM_PEAK_GBS, 4),
             "shape": {"workgroups": wg, "threads": th, "loads_in_flight": un},
-            "kernel": "stream_read_kernel"}
+            "us_by_shape": every, "kernel": "stream_read_kernel"}
 
 
 def _cpu_baseline_prefill(w, min_seconds: float):
@@ -373,11 +375,17 @@ def _cpu_baseline_prefill(w, min_seconds: float):
     }
 
 
-def _context(dev, run_once, warm_steps: int = 20):
-    """A context figure outside the K timed steps: the step with warm caches
-    (no sweep in between; the mean of ``warm_steps`` runs, HIP events)."""
+def _context(dev, run_once, warm_steps: int = 20, capture=None):
+    """Context figures outside the timed rounds, all with warm caches (no
+    sweep in between), HIP events on the launch stream:
+    ``warm_us_per_step`` -- the mean of ``warm_steps`` event pairs, one
+    around each step; ``warm_back_to_back_us_per_step`` -- ``warm_steps``
+    steps between one event pair (the host enqueues ahead, unless its own
+    per-call cost is the larger); with ``capture`` (a function returning a
+    HIP graph of n consecutive steps), ``graph_of_steps_us_per_step`` -- one
+    replay of a graph of ``warm_steps`` steps between one event pair."""
     import torch
-    ev = _HipEvents(2 * warm_steps)
+    ev = _HipEvents(2 * warm_steps + 4)
     stream = torch.cuda.current_stream(dev).cuda_stream
     run_once()
     torch.cuda.synchronize()
@@ -387,8 +395,26 @@ def _context(dev, run_once, warm_steps: int = 20):
         ev.record(2 * i + 1, stream)
     torch.cuda.synchronize()
     warm = statistics.fmean(ev.ms(2 * i, 2 * i + 1) for i in range(warm_steps))
+    k = 2 * warm_steps
+    ev.record(k, stream)
+    for _ in range(warm_steps):
+        run_once()
+    ev.record(k + 1, stream)
+    torch.cuda.synchronize()
+    out = {"warm_us_per_step": round(1e3 * warm, 2),
+           "warm_back_to_back_us_per_step": round(1e3 * ev.ms(k, k + 1) / warm_steps, 2)}
+    if capture is not None:
+        g = capture(warm_steps)
+        g.replay()
+        torch.cuda.synchronize()
+        ev.record(k + 2, stream)
+        g.replay()
+        ev.record(k + 3, stream)
+        torch.cuda.synchronize()
+        out["graph_of_steps_us_per_step"] = round(1e3 * ev.ms(k + 2, k + 3) / warm_steps, 2)
+        del g
     ev.close()
-    return {"warm_us_per_step": round(1e3 * warm, 2)}
+    return out
 
 
 def _cpu_model() -> str:
@@ -591,10 +617,9 @@ def main():
             step.attention()
             step.merge()
 
-    graph = None
-    if args.graph:
-        # capture one whole step (all of its launches); warm up on a side
-        # stream first, as capture requires
+    def capture(nsteps: int):
+        """A HIP graph of nsteps consecutive steps (all of their launches);
+        warmed up on a side stream first, as capture requires."""
         side = torch.cuda.Stream(dev)
         side.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(side):
@@ -602,10 +627,14 @@ def main():
                 run_once()
         torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            run_once()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(nsteps):
+                run_once()
         torch.cuda.synchronize()
+        return g
+
+    graph = capture(1) if args.graph else None
 
     stream = torch.cuda.current_stream(dev).cuda_stream   # every launch goes here
     timer = _HipEvents(4 * args.steps)
@@ -665,7 +694,8 @@ def main():
 
     context = {}
     if not args.no_context:
-        context.update(_context(dev, graph.replay if graph is not None else run_once))
+        context.update(_context(dev, graph.replay if graph is not None else run_once,
+                                capture=capture if args.graph else None))
     ceiling = None
     if not args.no_ceiling and mode not in ("prefill", "prefill_step"):
         ceiling = _read_ceiling(dev, kvb, sweep)

@@ -346,7 +346,7 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
 // columns of the 16-column MFMA tile; column c is token c / G, head c % G.
 // MT: several tokens (S > 1), whose columns attend different row ranges;
 // the single-token instances keep the plainer inner loop.
-template <int D, int CT, int NW, typename IT, Mode MODE, bool MT>
+template <int D, int CT, int NW, int PPW, typename IT, Mode MODE, bool MT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(CT >= 16 ? 2 : kWavesPerEU))) void
 attn_decode_mfma_kernel(const KernelArgs a) {
   static_assert(CT <= 16, "one 16-column MFMA tile holds at most 16 query rows");
@@ -373,20 +373,32 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   // many partitions puts partitions of every sequence in flight at once,
   // streams 32 MiB or more apart, and measured slower and sensitive to where
   // the K and V caches sit relative to each other.)
+  //
+  // Partitions per workgroup (ppw = PPW, Split and Step with one token):
+  // with ppw = 2 a workgroup takes two consecutive partitions of one
+  // (sequence, KV head) and its NW waves split into two groups of NW/2, one
+  // per partition.  The long-context launches use it with NW = 8, so each
+  // partition keeps four waves while the two partitions that share a CU are
+  // one workgroup (see the launcher).  The grid's unit is then the pair.
+  constexpr int ppw = (kPartial && !MT) ? PPW : 1;
+  constexpr int wpp = NW / ppw;       // waves per partition
+  static_assert(PPW == 1 || PPW == 2, "one or two partitions per workgroup");
   const int nbg = a.B * a.Hkv;
-  const int npg = MODE == Mode::Final ? 1 : a.num_parts;
-  int part, bg;
+  const int npg = MODE == Mode::Final ? 1 : (a.num_parts + ppw - 1) / ppw;
+  int pgrp, bg;
   if (npg >= 8) {
     bg = (int)blockIdx.x / npg;
-    part = (int)blockIdx.x - bg * npg;
+    pgrp = (int)blockIdx.x - bg * npg;
   } else {
-    part = (int)blockIdx.x / nbg;
-    bg = (int)blockIdx.x - part * nbg;
+    pgrp = (int)blockIdx.x / nbg;
+    bg = (int)blockIdx.x - pgrp * nbg;
   }
   const int g = bg % a.Hkv;
   const int b = bg / a.Hkv;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int lw = ppw == 1 ? wave : wave % wpp;   // wave within its partition's group
+  const int part = ppw == 1 ? pgrp : pgrp * ppw + wave / wpp;   // this wave's partition
   const int n = lane & 15;
   const int lg = lane >> 4;
   const int T = a.T;
@@ -406,7 +418,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   auto tok_lo = [&](int st) { return a.window > 0 ? max(0, tok_end(st) - a.window) : 0; };
   const int nrow = MT ? tok_end(S - 1) : min(max(a.lens[b], 0), T);
   const int lo = MT ? tok_lo(0) : (a.window > 0 ? max(0, nrow - a.window) : 0);
-  // Rows this workgroup attends: the whole range, or its partition.
+  // Rows this wave attends: the whole range, or its partition.
   int t0 = lo, t1 = nrow;
   if (kPartial) {
     t0 = min(lo + part * a.part_tokens, nrow);
@@ -420,7 +432,9 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   };
 
   if constexpr (MODE != Mode::Step) {
-    if (t0 >= t1) {   // nothing to attend in this range (uniform over the workgroup)
+    // nothing to attend in this range (uniform over the workgroup when it
+    // holds one partition)
+    if (ppw == 1 && t0 >= t1) {
       if (MODE == Mode::Split) {
         for (int c = threadIdx.x; c < NC; c += NW * 64)
           a.ws_lse[orow(c) * num_parts + part] = -INFINITY;
@@ -485,12 +499,13 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
   };
 
-  // Units of UR rows: wave w takes units w, w + NW, w + 2 NW, ... of the
-  // workgroup's range.
+  // Units of UR rows: the wave with index lw in its partition's group of
+  // wpp waves takes units lw, lw + wpp, lw + 2 wpp, ... of the partition's
+  // range (the whole workgroup's range when it holds one partition).
   auto unit_row = [&](int64_t u) -> int {
     return (int)min((int64_t)t0 + (int64_t)UR * u, (int64_t)t1);
   };
-  int64_t ustep = wave;
+  int64_t ustep = lw;
   int rcur = unit_row(ustep);
 
   TileBuf<D> bf[2];
@@ -608,7 +623,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       const bool in_range = has_pro && p >= 0 && p < T;
       const bool attended = has_pro && p >= t0 && p < t1;
       const bool outside = in_range && (p < lo || p >= nrow);
-      const bool kwrite = wave == 0 && (attended || (part == 0 && outside));
+      const bool kwrite = lw == 0 && (attended || (part == 0 && outside));
       const bool need_k = attended || kwrite;
       // raw values: converted only after the tiles are issued
       IT rx0 = 0, rx1 = 0, rv0 = 0, rv1 = 0;
@@ -1023,7 +1038,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   // meant to overlap; the scheduling barriers keep the machine scheduler
   // from doing the same.
   while (rcur < t1) {
-    ustep += NW;
+    ustep += wpp;
     const int rnext = unit_row(ustep);
     __builtin_amdgcn_sched_barrier(0);
     compute(bf[0], rcur);
@@ -1060,8 +1075,9 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   __syncthreads();
 
   // Step with a single partition writes the final output like Final.  Each
-  // thread combines four consecutive d of one column (one 16-byte LDS read
-  // per wave, one 16-byte store).
+  // thread combines four consecutive d of one column over the waves of one
+  // partition (one 16-byte LDS read per wave, one 16-byte store); with two
+  // partitions per workgroup the index runs over both.
   const bool write_final = MODE == Mode::Final || (MODE == Mode::Step && num_parts == 1);
   constexpr int Q4 = D / 4;
   // Step: this team's partials, rows head0 .. head0 + span - 1 of ws_o
@@ -1072,19 +1088,27 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       MODE == Mode::Step
           ? make_rsrc(a.ws_o + head0 * num_parts * D, (uint32_t)((size_t)span * num_parts * D * 4))
           : make_rsrc(nullptr, 0u);
-  for (int idx = threadIdx.x; idx < CT * Q4; idx += NW * 64) {
-    const int h = idx / Q4;         // column
+  for (int idx = threadIdx.x; idx < ppw * CT * Q4; idx += NW * 64) {
+    const int pp = ppw == 1 ? 0 : idx / (CT * Q4);   // partition of the pair
+    const int h = (idx / Q4) % CT;    // column
     const int d = 4 * (idx % Q4);
-    if (h >= NC) break;             // columns only grow with idx
+    const int pout = pgrp * ppw + pp;
+    if (h >= NC) {                    // columns only grow with idx within a partition
+      if (ppw == 1) break;
+      continue;
+    }
+    if (ppw > 1 && pout >= num_parts) continue;
     const int64_t oh = orow(h);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 0; w < NW; ++w)
+      if (w / wpp == pp) M = fmaxf(M, sm_m[w][h]);
     const float Ms = (M == -INFINITY) ? 0.0f : M;
     float L = 0.0f;
     float4 A = float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
+      if (w / wpp != pp) continue;
       const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - Ms);
       const float4 ow = *reinterpret_cast<const float4*>(&sm_o[w][h][d]);
       L += sm_l[w][h] * f;
@@ -1105,8 +1129,8 @@ attn_decode_mfma_kernel(const KernelArgs a) {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + oh * D + d) = ov;
       if (d == 0 && a.lse_out != nullptr) a.lse_out[oh] = lse;
     } else if (MODE == Mode::Split) {
-      if (any) *reinterpret_cast<float4*>(a.ws_o + (oh * num_parts + part) * D + d) = ov;
-      if (d == 0) a.ws_lse[oh * num_parts + part] = lse;
+      if (any) *reinterpret_cast<float4*>(a.ws_o + (oh * num_parts + pout) * D + d) = ov;
+      if (d == 0) a.ws_lse[oh * num_parts + pout] = lse;
     } else {
       // Write-through (sc1) stores reach the coherence point, so the merging
       // workgroup (possibly on another XCD) can read them without any L2
@@ -1115,9 +1139,9 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       if (any)
         __builtin_amdgcn_raw_buffer_store_b128(
             __builtin_bit_cast(u32x4_t, ov), Wrs,
-            (uint32_t)((((oh - head0) * num_parts + part) * D + d) * 4), 0, kCoherent);
+            (uint32_t)((((oh - head0) * num_parts + pout) * D + d) * 4), 0, kCoherent);
       if (d == 0)
-        __hip_atomic_store(a.ws_lse + oh * num_parts + part, lse, __ATOMIC_RELAXED,
+        __hip_atomic_store(a.ws_lse + oh * num_parts + pout, lse, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -1142,34 +1166,66 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     __shared__ int s_last;
     uint32_t* ticket = a.ws_cnt + (int64_t)b * Hkv + g;
     if (threadIdx.x == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+      // one arrival per partition this workgroup holds
+      const uint32_t cnt = ppw == 1 ? 1u : (uint32_t)min(ppw, num_parts - pgrp * ppw);
+      const uint32_t old = __hip_atomic_fetch_add(ticket, cnt, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
-      s_last = old == (uint32_t)(num_parts - 1);
+      const bool last = old + cnt == (uint32_t)num_parts;
+      // the acquire: one wave invalidates the CU's and the XCD's caches
+      // before the barrier that the other waves' reads follow (an
+      // invalidation per wave cost up to 3 us on an eight-wave workgroup)
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      s_last = last;
     }
     __syncthreads();
     if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     merge_partials<D, CT, NW, MT>(a, head0, G, NC);
     if (threadIdx.x == 0)
       __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Waves per workgroup: four, one per SIMD of the CU.
+// Waves per partition: four, one per SIMD of the CU (eight per workgroup
+// when a workgroup holds two partitions).
 constexpr int kWavesPerGroup = 4;
+
+// Long-context launches (single token, Split or Step, at least kPairParts
+// partitions per (sequence, KV head) and kPairFrom partitions in all) run
+// two partitions per workgroup on eight waves: one workgroup per CU with
+// four waves per partition.  Measured on the 64-partition long-context
+// step (537 MB): 91.8 -> 87.0 us, the slowest XCD's loop ending earlier
+// than with two four-wave workgroups per CU, of which the one dispatched
+// first takes most of the CU's bandwidth.  Ragged batches (few partitions
+// per sequence, many of them short or empty) keep one partition per
+// workgroup, whose finer grain the dispatcher balances (pairs cost 6 us on
+// the ragged Llama-3-8B batch).
+constexpr int kPairParts = 16;
+constexpr int64_t kPairFrom = 512;
 
 template <int D, int CT, typename IT, Mode MODE>
 static int launch_mode(const KernelArgs& a, hipStream_t s) {
-  constexpr int NW = kWavesPerGroup;
-  const dim3 grid((MODE == Mode::Final ? 1 : a.num_parts) * a.B * a.Hkv);
   bool multi = false;
   if constexpr (CT > 1) multi = a.S > 1;   // one column holds one token
-  if (multi)
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, IT, MODE, CT != 1>), grid,
-                       dim3(NW * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, IT, MODE, false>), grid,
-                       dim3(NW * 64), 0, s, a);
+  const int64_t total = (int64_t)a.num_parts * a.B * a.Hkv;
+  const bool pair = MODE != Mode::Final && !multi && a.num_parts >= kPairParts &&
+                    total >= kPairFrom;
+  if (pair) {
+    if constexpr (MODE != Mode::Final) {
+      constexpr int NW = 2 * kWavesPerGroup;
+      const dim3 grid((a.num_parts + 1) / 2 * a.B * a.Hkv);
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, 2, IT, MODE, false>), grid,
+                         dim3(NW * 64), 0, s, a);
+    }
+  } else {
+    constexpr int NW = kWavesPerGroup;
+    const dim3 grid((MODE == Mode::Final ? 1 : a.num_parts) * a.B * a.Hkv);
+    if (multi)
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, 1, IT, MODE, CT != 1>), grid,
+                         dim3(NW * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_decode_mfma_kernel<D, CT, NW, 1, IT, MODE, false>), grid,
+                         dim3(NW * 64), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 

@@ -713,11 +713,13 @@ attn_prefill_kernel(const PrefillArgs a) {
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == (uint32_t)(splits - 1);
+    const bool last = old == (uint32_t)(splits - 1);
+    // one wave invalidates before the barrier that the other waves' reads follow
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
   }
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // Thread tid owns float4 groups tid + 256 i of the block's rows x D: row
   // (tid + 256 i) / (D/4).  One memory round trip per split: M, W and A are
   // the running maximum lse, weight sum and weighted sum.

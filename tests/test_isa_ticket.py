@@ -12,8 +12,9 @@ every instance that takes a ticket:
 
 * between the last device-scope store and the barrier ahead of the ticket
   there is a wait for the vector-memory counter to reach zero;
-* the merging path after the ticket starts with a device-scope cache
-  invalidation (the acquire).
+* the wave that draws the last ticket takes a device-scope cache
+  invalidation (the acquire) right after it, before the barrier that the
+  merging reads follow.
 """
 import concurrent.futures as cf
 import os
@@ -76,12 +77,13 @@ def _check(lines):
     stores = [j for j in range(ib) if "store" in lines[j] and "sc1" in lines[j]]
     assert stores, "no device-scope partial store ahead of the ticket"
     waits = [j for j in range(stores[-1] + 1, ib) if "vmcnt(0)" in lines[j]]
-    acquire = any("buffer_inv sc1" in ln for ln in lines[ia:ia + 80])
+    acquire = any("buffer_inv sc1" in ln for ln in lines[ia:ia + 40])
     return bool(waits), acquire
 
 
 @pytest.mark.parametrize("src,pattern,expected", [
-    ("attn_decode_mfma.hip", "attn_decode_mfma_kernel", 36),   # Step: 2 D x 2 q types x (1 + 4 x 2) column/token instances
+    # Step: 2 D x 2 q types x ((1 + 4 x 2) column/token instances + 5 pair instances)
+    ("attn_decode_mfma.hip", "attn_decode_mfma_kernel", 56),
     ("attn_prefill_mfma.hip", "attn_prefill_kernel", 16),      # key splits: 2 D x 4 q modes x 2 P forms
 ], ids=["decode_step", "prefill_split"])
 def test_ticket_release_and_acquire(assembly, src, pattern, expected):
