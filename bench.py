@@ -461,13 +461,16 @@ def _bench_gemv(args, dev):
     g = workloads.make_gemv(args.workload)
     nbytes = workloads.gemv_bytes(g)
     run = DeviceGemv(g, device=dev)
-    flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
+    # 1 GiB of int64, summed as int64: summing an int32 buffer into an int64
+    # result made torch widen the whole buffer first (a 2 GiB temporary
+    # written before every step, dirty lines included)
+    flush = None if args.flush == "none" else torch.ones(1 << 27, dtype=torch.int64,
                                                           device=dev)
     flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
 
     def sweep():
         if args.flush == "read":
-            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink)
+            torch.sum(flush, dim=0, out=flush_sink)
         elif args.flush == "rmw":
             flush.add_(1)
 
@@ -595,7 +598,10 @@ def main():
         # key splits: the library's suggestion for this device unless given
         splits = args.splits or prefill_default_splits(w.B, w.S, w.Hq, w.Hkv)
     step = DeviceStep(w, device=dev, mode=mode, splits=splits)
-    flush = None if args.flush == "none" else torch.ones(1 << 28, dtype=torch.int32,
+    # 1 GiB of int64, summed as int64: summing an int32 buffer into an int64
+    # result made torch widen the whole buffer first (a 2 GiB temporary
+    # written before every step, dirty lines included)
+    flush = None if args.flush == "none" else torch.ones(1 << 27, dtype=torch.int64,
                                                           device=dev)
     flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
 
@@ -603,7 +609,7 @@ def main():
         # A read-only sweep leaves the caches full of clean lines, so the timed
         # kernels pay no write-back of somebody else's dirty data.
         if args.flush == "read":
-            torch.sum(flush, dim=0, dtype=torch.int64, out=flush_sink)
+            torch.sum(flush, dim=0, out=flush_sink)
         elif args.flush == "rmw":
             flush.add_(1)
 
