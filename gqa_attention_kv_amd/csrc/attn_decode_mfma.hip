@@ -29,8 +29,9 @@
 //       which streams at only ~4.1 TB/s on MI355X against ~5.2 TB/s for
 //       instructions that read whole 256-byte rows.  So K is loaded like V,
 //       whole rows, and passes through a wave-private LDS slab (rows padded
-//       to D*2+16 bytes: conflict-free for both the row writes and the
-//       operand reads).  An fp32 q is split into bf16 hi + lo parts so the
+//       to D*2+16 bytes; the counters still report bank conflicts at about
+//       0.6 of the LDS-active cycles, small against the HBM-bound loop).
+//       An fp32 q is split into bf16 hi + lo parts so the
 //       scores keep ~16 mantissa bits: with G <= 8 the lo parts fill columns
 //       8..15 of the same operand and one DPP step adds column n + 8 to
 //       column n; with G = 16 they take a second call.  A bf16 q needs the

@@ -15,7 +15,7 @@
 // not by HBM.  Work split: a workgroup of 4 waves owns 128 consecutive
 // (token, head) rows of one (sequence, KV head) -- row r is token r / G,
 // head r % G of the group, so the G heads of a token sit side by side -- and
-// streams the K/V rows they need through LDS in tiles of 32 rows, shared by
+// streams the K/V rows they need through LDS in tiles of 64 rows, shared by
 // all 4 waves; each wave owns 32 rows (two blocks of 16).
 //
 // Lane l, with n = l % 16 and k4 = l / 16, per 16-row block (columns = query
