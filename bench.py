@@ -492,7 +492,12 @@ def _bench_gemv(args, dev):
     timer.close()
     mean = statistics.fmean(ms)
     gbps = nbytes / (mean * 1e-3) / 1e9
-    context = None if args.no_context else _context(dev, run.run)
+    context = {} if args.no_context else _context(dev, run.run)
+    if not args.no_ceiling:
+        context["read_ceiling"] = _read_ceiling(dev, nbytes, sweep)
+        context["read_ceiling"]["step_frac_of_ceiling"] = round(
+            gbps / context["read_ceiling"]["GBps"], 4)
+    context = context or None
     copy_probe = _copy_probe(args.copy_probe_mib, dev, sweep)
     cpu = None
     if not args.no_cpu_baseline:
