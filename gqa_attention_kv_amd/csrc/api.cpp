@@ -471,8 +471,9 @@ int gqa_qkv_gemv(const uint16_t* x, int64_t x_stride, const uint16_t* w, int64_t
   if (x_stride % 8 != 0 || w_stride % 8 != 0) return GQA_ERR_ALIGN;
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, y_dtype == GQA_BF16 ? 2 : 4))
     return GQA_ERR_ALIGN;
-  // a workgroup addresses its 16 weight rows with 32-bit byte offsets
-  if ((15 * w_stride + K) * 2 > (int64_t)UINT32_MAX) return GQA_ERR_SHAPE;
+  // a workgroup addresses its share of up to 64 weight rows with 32-bit
+  // byte offsets
+  if ((63 * w_stride + K) * 2 > (int64_t)UINT32_MAX) return GQA_ERR_SHAPE;
   if ((int64_t)N > kMaxWorkgroups * 16 || (int64_t)M * y_stride > kMaxIndex ||
       (int64_t)N * w_stride > kMaxIndex || (int64_t)M * x_stride > kMaxIndex)
     return GQA_ERR_SHAPE;

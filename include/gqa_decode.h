@@ -452,7 +452,7 @@ int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,
  * (round to nearest even).  bf16 products, float32 accumulation in a fixed
  * order (bit-identical reruns).  1 <= M <= 16 and K a multiple of 128, else
  * GQA_ERR_UNSUPPORTED; GQA_ERR_SHAPE for strides below the sizes or
- * 15 * w_stride + K >= 2^31 elements; GQA_ERR_ALIGN for misaligned
+ * 63 * w_stride + K >= 2^31 elements; GQA_ERR_ALIGN for misaligned
  * pointers or strides.  Nothing is allocated; y must not alias x or w.
  */
 int gqa_qkv_gemv(const uint16_t* x, int64_t x_stride, const uint16_t* w, int64_t w_stride,

@@ -35,7 +35,8 @@ def test_gemv_validation(G):
     assert call(xs=1028) == -6                       # stride not a multiple of 8
     assert call(w=A16 + 8) == -6
     assert call(y=A16 + 2, yd=0) == -6               # fp32 output needs 4-byte alignment
-    assert call(ws=1 << 28) == -2                    # 16 rows exceed 32-bit byte offsets
+    assert call(ws=1 << 28) == -2                    # a share of rows exceeds 32-bit byte offsets
+    assert call(ws=1 << 26) == -2                    # 64 rows of 2^26 elements do too
 
 
 def check_gemv(got, ref64, out_dtype, what=""):
@@ -84,6 +85,9 @@ CASES = [  # (overrides, output dtype, x pad, y pad)
     (dict(M=16, K=512, N=272), "f32", 0, 0),
     (dict(M=5, K=640, N=33), "bf16", 16, 8),         # five 128-column steps over 4 waves
     (dict(M=2, K=2048, N=2000), "f32", 0, 0),
+    (dict(M=7, K=256, N=5000), "f32", 0, 4),         # 20-row shares: a 4-row last tile
+    (dict(M=4, K=384, N=20000), "bf16", 8, 0),       # 64-row shares, more than one per CU
+    (dict(M=16, K=1152, N=700), "f32", 0, 0),        # 3-row shares: 13 padding rows a tile
 ]
 
 

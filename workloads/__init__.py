@@ -169,9 +169,10 @@ def attention_flops(w: Workload) -> int:
 
 # name -> (base parameters).  Sizes may be overridden for reduced test cases.
 CONFIGS: Dict[str, dict] = {
-    # tiny step: B1 Hq8 Hkv2 D64 L128, RoPE 1e4 at pos L-1, no QK-norm
+    # tiny step: B1 Hq8 Hkv2 D64 L128, RoPE 1e4 at pos L-1, no QK-norm; one
+    # 128-row partition per KV head (the step then needs no merge)
     "1": dict(seed=1, B=1, Hq=8, Hkv=2, D=64, L=128, layout="last",
-              window=0, theta=1e4, norm=False, out_dtype="f32", part_tokens=64),
+              window=0, theta=1e4, norm=False, out_dtype="f32", part_tokens=128),
     # Qwen3-0.6B-shaped layer, L in {512, 2048}; new token at pos=L
     "2a": dict(seed=2, B=1, Hq=16, Hkv=8, D=128, L=512, layout="append",
                window=0, theta=1e6, norm=True, out_dtype="f32", part_tokens=128),
