@@ -28,18 +28,19 @@
 //   PV: O^T[16 cols x 16 rows] += V^T[16 x 32] * P^T[32 x 16] per 16-column
 //       block, the 32 keys of the tile as the k index in the order lane l's
 //       P operand already holds them: k = 8 k4 + e is key 4 k4 + e (e < 4)
-//       or 16 + 4 k4 + e - 4.  V is stored transposed in LDS with its keys
-//       in that order, so lane l's V operand is one 16-byte read.  P is
-//       rounded once to bf16 when the output is bf16 (an error of at most
-//       2^-9 sum p|V|, the order of the output's own rounding); for an fp32
-//       output P is carried as bf16 hi + lo (~16 mantissa bits) in two calls
-//       on the same V operand.
-// The tiles pass through two LDS stages: the next tile is stashed while the
-// current one is computed, with one barrier per tile.  Online softmax per
-// row with a lazy rescale: the reference maximum only moves when a tile's
-// maximum exceeds it by more than 2^8 (in exp2 units), so P stays below 256
-// and O is rarely rescaled.  Keys outside a row's range are masked only in
-// tiles that are not wholly inside every range of the wave's rows.
+//       or 16 + 4 k4 + e - 4.  V stays row-major in LDS; lane l's V operand
+//       comes from two transposed reads (ds_read_b64_tr_b16, four key rows
+//       each).  P is rounded once to bf16 when the output is bf16 (an error
+//       of at most 2^-9 sum p|V|, the order of the output's own rounding);
+//       for an fp32 output P is carried as bf16 hi + lo (~16 mantissa bits)
+//       in two calls on the same V operand.
+// K and V tiles go from the cache straight into LDS (buffer loads with the
+// LDS destination): K through two stages, fetched one tile ahead, V through
+// three, fetched two tiles ahead, with one barrier per tile.  Online softmax
+// per row with a lazy rescale: the reference maximum only moves when a
+// tile's maximum exceeds it by more than 2^8 (in exp2 units), so P stays
+// below 256 and O is rarely rescaled.  Keys outside a row's range are masked
+// only in tiles that are not wholly inside every range of the wave's rows.
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/gqa_decode.h"
@@ -69,14 +70,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, ui
 
 __device__ __forceinline__ int clampi(int64_t v, int lo, int hi) {
   return (int)(v < lo ? lo : v > hi ? hi : v);
-}
-
-// Position of key k of a tile in the transposed V rows: the order of the
-// PV k index within each 32-key half, 8 k4 + 4 kb + i for key 16 kb + 4 k4
-// + i of the half.
-__device__ __forceinline__ int vpos(int key) {
-  const int k = key & 31;
-  return (key & ~31) + 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
 }
 
 // Maximum that propagates NaN (IEEE 754-2019 maximum, v_maximum3_f32 on
@@ -118,18 +111,26 @@ attn_prefill_kernel(const PrefillArgs a) {
   constexpr bool PRO = QM >= 2;
   constexpr int KC = D / 32;            // QK slices
   constexpr int VB = D / 16;            // PV column blocks
-  constexpr int KROW = D * 2 + 16;      // K row pitch in LDS (conflict-free operand reads)
-  constexpr int VROW = kKeys * 2 + 16;  // pitch of a transposed V row (one column of V)
-  constexpr int CPR = D / 8;            // 16-byte chunks per cache row
-  constexpr int KFILL = kKeys * CPR / (kWaves * 64);   // K chunks per thread per tile
-  constexpr int VITEMS = (kKeys / 2) * CPR;            // (key pair, chunk) items per tile
-  constexpr int VFILL = (VITEMS + kWaves * 64 - 1) / (kWaves * 64);
-  constexpr int KBYTES = kKeys * KROW;
-  constexpr int STAGE = KBYTES + D * VROW;
-  static_assert(KFILL >= 1 && VITEMS % (kWaves * 64) == 0 || VITEMS < kWaves * 64,
-                "tile fill");
+  constexpr int RB = D * 2;             // bytes per cache row (unpadded in LDS)
+  constexpr int SW = D / 8;             // 16-byte chunks per row
+  constexpr int RPR = 256 / RB;         // rows per 256 bytes of LDS
+  constexpr int RPB = 1024 / RB;        // rows per 1 KiB block (one wave's direct load)
+  constexpr int KBYTES = kKeys * RB;    // one tile of K, and one of V
+  // LDS: two stages of K, then three of V (the V of a tile is fetched two
+  // tiles ahead, see the loop)
+  constexpr int VBASE = 2 * KBYTES;
+  constexpr int BPW = KBYTES / 1024 / kWaves;   // 1 KiB blocks per wave per tile, K and V each
+  static_assert(BPW >= 1 && KBYTES % (1024 * kWaves) == 0, "tile fill");
+  // The swizzle of a lane's row is the same in every block it fills.
+  static_assert((4 * kWaves) % SW == 0, "block-invariant swizzle");
+  // Whether a wave reads all of a tile's V operands into registers before
+  // it fetches the V of a later tile (see the loop).  An fp32 q (hi + lo)
+  // or P (hi + lo) leaves no room for the 16 staged operands.
+  constexpr bool kStageV = !QF32 && !PLO;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+  // 80 KiB: two workgroups per CU.  Nothing else may live in LDS (the
+  // split instances' arrival flag reuses the first word after the loop).
+  __shared__ __attribute__((aligned(16))) unsigned char lds[5 * KBYTES];
 
   const int Hq = a.Hq, Hkv = a.Hkv, S = a.S, T = a.T;
   const int G = Hq / Hkv;
@@ -387,103 +388,74 @@ attn_prefill_kernel(const PrefillArgs a) {
   const int tb = min(sp * per, ntiles);
   const int te = min(tb + per, ntiles);
 
-  // Tile fill.  K: thread t moves chunks t + 256 f (row-major, CPR chunks a
-  // row).  V: item t + 256 f (< VITEMS) is chunk it / (kKeys/2) of keys
-  // 2 (it % (kKeys/2)) and the next, which land side by side in the
-  // transposed rows.  Keys past the range are clamped into it (they are
-  // masked below, and a row the workgroup attends holds finite values).
-  constexpr int PAIRS = kKeys / 2;
-  const bool vthread = VITEMS >= kWaves * 64 || tid < VITEMS;
-  u32x4_t fk[KFILL], fv0[VFILL], fv1[VFILL];
+  // Tile fill: K and V rows go from the cache straight into LDS (buffer
+  // loads with the LDS destination, no register round trip).  One such load
+  // writes 1 KiB of LDS, lane i the 16 bytes at 16 i: RPB rows.  Rows are
+  // stored unpadded with their 16-byte chunks permuted -- chunk c of K row r
+  // at position c ^ ksw(r), of V row r at c ^ vsw(r) -- so that the operand
+  // reads below spread over all banks: a K read takes one chunk of 16
+  // consecutive rows, a transposed V read two adjacent chunks of 8
+  // consecutive rows per half-wave.  Lane i of wave w fills, in block
+  // w + kWaves f of the tile, row RPB (w + kWaves f) + i / SW, position
+  // i % SW, i.e. global chunk (i % SW) ^ swizzle; that swizzle does not
+  // depend on f.  Keys past the range are clamped into it (they are masked
+  // below, and a row the workgroup attends holds finite values).
+  auto ksw = [](int r) { return (r / RPR) & (SW - 1); };
+  auto vsw = [](int r) { return (2 * (r / RPR)) & (SW - 1); };
+  const int frow = wave * RPB + lane / SW;        // the lane's row in its first block
+  const uint32_t kfo = (uint32_t)(frow * RB + 16 * ((lane % SW) ^ ksw(frow)));
+  const uint32_t vfo = (uint32_t)(frow * RB + 16 * ((lane % SW) ^ vsw(frow)));
   auto clamp_key = [&](int key) { return key < kend ? key : kend - 1; };
-  // A tile wholly inside [kbeg, kend) needs no clamp: each load's offset is
-  // then the lane's fixed part plus the tile's (scalar) row offset.
-  uint32_t kofs[KFILL], vofs[VFILL];
-#pragma unroll
-  for (int f = 0; f < KFILL; ++f) {
-    const int ci = tid + kWaves * 64 * f;
-    kofs[f] = (uint32_t)(ci / CPR) * (uint32_t)(D * 2) + 16u * (ci % CPR);
-  }
-#pragma unroll
-  for (int f = 0; f < VFILL; ++f) {
-    const int it = tid + kWaves * 64 * f;
-    vofs[f] = (uint32_t)(2 * (it % PAIRS)) * (uint32_t)(D * 2) + 16u * (it / PAIRS);
-  }
-  auto fetch = [&](int tile) {
+  // One tile of K (V) into K (V) stage `stage`.
+  auto issue = [&](int tile, unsigned char* st, uint32_t lane_off,
+                   const __amdgpu_buffer_rsrc_t& rsrc) {
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
     const int base = kbeg + kKeys * tile;
     if (base + kKeys <= kend) {
-      const uint32_t so = (uint32_t)base * (uint32_t)(D * 2);
+      // wholly inside the range: the lane's part stays fixed, the tile and
+      // the block go in the scalar offset
 #pragma unroll
-      for (int f = 0; f < KFILL; ++f)
-        fk[f] = __builtin_bit_cast(u32x4_t,
-                                   __builtin_amdgcn_raw_buffer_load_b128(rk, kofs[f], so, 0));
-      if (vthread) {
+      for (int f = 0; f < BPW; ++f)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (lds_ptr_t)(st + 1024 * (wave + kWaves * f)), 16, lane_off,
+            (uint32_t)base * (uint32_t)RB + (uint32_t)(kWaves * f * 1024), 0, 0);
+    } else {
 #pragma unroll
-        for (int f = 0; f < VFILL; ++f) {
-          fv0[f] = __builtin_bit_cast(u32x4_t,
-                                      __builtin_amdgcn_raw_buffer_load_b128(rv, vofs[f], so, 0));
-          fv1[f] = __builtin_bit_cast(
-              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, vofs[f] + D * 2, so, 0));
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int f = 0; f < KFILL; ++f) {
-      const int ci = tid + kWaves * 64 * f;
-      const uint32_t off = (uint32_t)clamp_key(base + ci / CPR) * (uint32_t)(D * 2) +
-                           16u * (ci % CPR);
-      fk[f] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-    }
-    if (vthread) {
-#pragma unroll
-      for (int f = 0; f < VFILL; ++f) {
-        const int it = tid + kWaves * 64 * f;
-        const int vp = it % PAIRS, vm = it / PAIRS;
-        const uint32_t off0 =
-            (uint32_t)clamp_key(base + 2 * vp) * (uint32_t)(D * 2) + 16u * vm;
-        const uint32_t off1 =
-            (uint32_t)clamp_key(base + 2 * vp + 1) * (uint32_t)(D * 2) + 16u * vm;
-        fv0[f] = __builtin_bit_cast(u32x4_t,
-                                    __builtin_amdgcn_raw_buffer_load_b128(rv, off0, 0, 0));
-        fv1[f] = __builtin_bit_cast(u32x4_t,
-                                    __builtin_amdgcn_raw_buffer_load_b128(rv, off1, 0, 0));
+      for (int f = 0; f < BPW; ++f) {
+        const int blk = wave + kWaves * f;
+        const uint32_t vo = (uint32_t)clamp_key(base + blk * RPB + lane / SW) * (uint32_t)RB +
+                            (lane_off & (uint32_t)(RB - 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(st + 1024 * blk), 16, vo, 0,
+                                                 0, 0);
       }
     }
   };
-  auto stash = [&](int stage) {
-    unsigned char* st = lds + stage * STAGE;
-#pragma unroll
-    for (int f = 0; f < KFILL; ++f) {
-      const int ci = tid + kWaves * 64 * f;
-      *reinterpret_cast<u32x4_t*>(st + (ci / CPR) * KROW + 16 * (ci % CPR)) = fk[f];
-    }
-    if (vthread) {
-#pragma unroll
-      for (int f = 0; f < VFILL; ++f) {
-        const int it = tid + kWaves * 64 * f;
-        const int vp = it % PAIRS, vm = it / PAIRS;
-        // element e of the chunk is column 8 vm + e; keys 2 vp and 2 vp + 1
-        // pair up in one dword of that column's row
-        unsigned char* vt = st + KBYTES + 2 * vpos(2 * vp);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w = __builtin_amdgcn_perm(fv1[f][e >> 1], fv0[f][e >> 1],
-                                                   (e & 1) ? 0x07060302u : 0x05040100u);
-          *reinterpret_cast<uint32_t*>(vt + (8 * vm + e) * VROW) = w;
-        }
-      }
-    }
+  auto issue_k = [&](int tile, int stage) { issue(tile, lds + stage * KBYTES, kfo, rk); };
+  auto issue_v = [&](int tile, int stage) {
+    issue(tile, lds + VBASE + stage * KBYTES, vfo, rv);
   };
 
   if (te > tb) {
-    fetch(tb);
-    stash(0);
-    if (te > tb + 1) fetch(tb + 1);
+    issue_k(tb, 0);
+    issue_v(tb, 0);
+    if (te > tb + 1) issue_v(tb + 1, 1);
   }
+  wait_vmem();
   __syncthreads();
   for (int tile = tb; tile < te; ++tile) {
-    const unsigned char* cur = lds + ((tile - tb) & 1) * STAGE;
+    // Tile i = tile - tb reads K stage i % 2 and V stage i % 3.  The K of
+    // tile i + 1 is fetched now into the other K stage, which every wave
+    // finished reading before the barrier that ended the previous trip.
+    // The V of tile i + 2 is fetched once this wave has read the V
+    // operands of tile i: the compiler makes every transposed LDS read wait
+    // for all LDS-bound loads in flight (it cannot tell them apart), so a
+    // V fetch issued before the last of this tile's V reads would stall
+    // them.  Staged, all of them are read right after the softmax and the
+    // fetch goes out before the PV calls; unstaged, after them.
+    const int it = tile - tb;
+    const unsigned char* cur = lds + (it & 1) * KBYTES;
+    const unsigned char* curv = lds + VBASE + (it % 3) * KBYTES;
+    if (tile + 1 < te) issue_k(tile + 1, (it + 1) & 1);
     const int k0 = kbeg + kKeys * tile;
     const bool work = wave_live && k0 < need_hi && k0 + kKeys > need_lo;   // wave-uniform
     f32x4_t s[kKB][2];
@@ -495,8 +467,8 @@ attn_prefill_kernel(const PrefillArgs a) {
       auto kread = [&](int kb, u32x4_t* dst) {
 #pragma unroll
         for (int c = 0; c < KC; ++c)
-          dst[c] =
-              *reinterpret_cast<const u32x4_t*>(cur + (16 * kb + n) * KROW + 64 * c + 16 * k4);
+          dst[c] = *reinterpret_cast<const u32x4_t*>(
+              cur + (16 * kb + n) * RB + 16 * ((4 * c + k4) ^ ksw(16 * kb + n)));
       };
       // The two waves on a SIMD belong to different workgroups and each
       // alternates matrix-core blocks with VALU softmax work: the one in a
@@ -528,15 +500,30 @@ attn_prefill_kernel(const PrefillArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
     }
-    // Stash the next tile into the other stage (every wave finished reading
-    // that stage before the barrier that ended the previous trip), then
-    // fetch the one after: while the QK calls run, or -- with an fp32 q,
-    // whose hi and lo parts leave no registers for it -- after the PV calls.
-    constexpr bool kEarlyStash = !QF32;
-    if (kEarlyStash) {
-      if (tile + 1 < te) stash((tile + 1 - tb) & 1);
-      if (tile + 2 < te) fetch(tile + 2);
-    }
+    constexpr int NH = kKB / 2;
+    u32x4_t ph[NH][2], pl[NH][2];
+    // V operands: column block v, lane row n is column 16 v + n of V, and
+    // its eight k are keys 4 k4 + e and 16 + 4 k4 + e (e < 4) of the half,
+    // the order P holds them in.  Each half comes from one transposed read
+    // (ds_read_b64_tr_b16): in a group of 16 lanes, lane 4 e + q points at
+    // columns 16 v + 4 q .. + 3 of key row 4 k4 + e, and lane n of the group
+    // receives column 16 v + n of the four rows.
+    typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+    const int vq = lane & 3;
+    const int vrow = 4 * k4 + ((lane & 15) >> 2);   // vsw(vrow + 16 m) == vsw(vrow)
+    auto vread = [&](int x) {   // the operand of PV step x = (hh, v)
+      const int hh = x / VB, v = x % VB;
+      const int col = 16 * v + 4 * vq;
+      const unsigned char* p0 =
+          curv + (32 * hh + vrow) * RB + 16 * ((col / 8) ^ vsw(vrow)) + 2 * (col % 8);
+      const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
+      const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0 + 16 * RB));
+      const auto a2 = __builtin_bit_cast(uint2, lo4);
+      const auto b2 = __builtin_bit_cast(uint2, hi4);
+      return u32x4_t{a2.x, a2.y, b2.x, b2.y};
+    };
+    u32x4_t vop[kStageV ? NH * VB : 1];   // staged: the tile's V operands, step x at x
     if (work) {
       const bool full = k0 >= free_lo && k0 + kKeys <= free_hi;
       // Masks and the tile maximum of each row (raw scores; qscale > 0).
@@ -584,8 +571,6 @@ attn_prefill_kernel(const PrefillArgs a) {
       // half h: bf16 (hi) and, for an fp32 output, the bf16 remainder (lo).
       // Word w of half h holds k = 2w, 2w + 1: keys 32h + (4 k4 + 2w, + 1)
       // for w < 2, 32h + (16 + 4 k4 + 2w - 4, + 1) for w >= 2.
-      constexpr int NH = kKB / 2;
-      u32x4_t ph[NH][2], pl[NH][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float mref = mq[j];
@@ -613,24 +598,35 @@ attn_prefill_kernel(const PrefillArgs a) {
           }
       }
 
-      // PV: column block v, lane row n is column 16 v + n of V.  The V
-      // operand of step (hh, v) + 1 is read while step (hh, v) runs.
-      auto vread = [&](int it) {
-        const int hh = it / VB, v = it % VB;
-        return *reinterpret_cast<const u32x4_t*>(cur + KBYTES + (16 * v + n) * VROW + 64 * hh +
-                                                 16 * k4);
-      };
+      if constexpr (kStageV) {
+#pragma unroll
+        for (int x = 0; x < NH * VB; ++x) vop[x] = vread(x);
+      }
+    }
+    // The V of tile i + 2 into V stage (i + 2) % 3, which held tile i - 1:
+    // every wave finished reading it before the previous barrier.
+    if constexpr (kStageV)
+      if (tile + 2 < te) issue_v(tile + 2, (it + 2) % 3);
+    if (work) {
+      // PV: O^T[16 cols x 16 rows] += V^T[16 x 32] * P^T[32 x 16] per column
+      // block and 32-key half.  Unstaged, the operand of step x + 1 is read
+      // while step x runs.
       u32x4_t vbuf[2];
+      if constexpr (!kStageV) vbuf[0] = vread(0);
       __builtin_amdgcn_s_setprio(1);
-      vbuf[0] = vread(0);
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
         for (int v = 0; v < VB; ++v) {
-          const int it = hh * VB + v;
-          if (it + 1 < NH * VB) vbuf[(it + 1) & 1] = vread(it + 1);
-          __builtin_amdgcn_sched_barrier(0);
-          const u32x4_t va = vbuf[it & 1];
+          const int x = hh * VB + v;
+          u32x4_t va;
+          if constexpr (kStageV) {
+            va = vop[x];
+          } else {
+            if (x + 1 < NH * VB) vbuf[(x + 1) & 1] = vread(x + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            va = vbuf[x & 1];
+          }
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -641,15 +637,20 @@ attn_prefill_kernel(const PrefillArgs a) {
                   __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pl[hh][j]),
                   o[j][v], 0, 0, 0);
           }
-          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (!kStageV) __builtin_amdgcn_sched_barrier(0);
         }
       __builtin_amdgcn_s_setprio(0);
     }
-    if (!kEarlyStash) {
-      if (tile + 1 < te) stash((tile + 1 - tb) & 1);
-      if (tile + 2 < te) fetch(tile + 2);
-    }
-    __syncthreads();
+    if constexpr (!kStageV)
+      if (tile + 2 < te) issue_v(tile + 2, (it + 2) % 3);
+    // This wave's fetches of K i + 1 and V i + 1 have landed (only the
+    // V i + 2 fetch may still be in flight), and after the barrier every
+    // wave's have, and every wave is done with K stage i % 2.
+    if (tile + 2 < te)
+      wait_vmem_but<BPW>();
+    else
+      wait_vmem();
+    barrier_lds();
   }
 
   // Normalise and store.  Lane (n, k4) holds, for row n of block j, columns
@@ -708,7 +709,8 @@ attn_prefill_kernel(const PrefillArgs a) {
   // agent-scope acquire fence before it reads the partials back.
   wait_vmem();
   __syncthreads();
-  __shared__ int s_last;
+  // the tile stages are no longer read: their first word carries the flag
+  int* s_last = reinterpret_cast<int*>(lds);
   uint32_t* ticket = a.ws_cnt + team;
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
@@ -716,10 +718,10 @@ attn_prefill_kernel(const PrefillArgs a) {
     const bool last = old == (uint32_t)(splits - 1);
     // one wave invalidates before the barrier that the other waves' reads follow
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    s_last = last;
+    *s_last = last;
   }
   __syncthreads();
-  if (!s_last) return;
+  if (!*s_last) return;
   // Thread tid owns float4 groups tid + 256 i of the block's rows x D: row
   // (tid + 256 i) / (D/4).  One memory round trip per split: M, W and A are
   // the running maximum lse, weight sum and weighted sum.

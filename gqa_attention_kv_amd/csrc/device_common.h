@@ -114,4 +114,24 @@ __device__ __forceinline__ void sincos_pi_f64(double x, double* s, double* c) {
 // one CU, so it waits only for LDS traffic.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Waits until at most N of this wave's vector memory operations are still
+// outstanding (s_waitcnt vmcnt(N), N < 16): they complete in issue order,
+// so everything but the N most recent ones is done.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// Workgroup barrier after this wave's LDS reads have returned, leaving
+// vector memory alone.  __syncthreads() is a release/acquire fence plus the
+// barrier, and the fence also waits for every load still in flight into
+// LDS (buffer loads with the LDS destination count as vector memory), which
+// would drain a tile prefetch at every barrier.  A caller that needs some
+// of those loads complete waits for them itself beforehand.  The memory
+// clobber keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace gqa
