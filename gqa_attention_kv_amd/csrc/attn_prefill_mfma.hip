@@ -41,6 +41,8 @@
 // tile's maximum exceeds it by more than 2^8 (in exp2 units), so P stays
 // below 256 and O is rarely rescaled.  Keys outside a row's range are masked
 // only in tiles that are not wholly inside every range of the wave's rows.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "../../include/gqa_decode.h"
@@ -116,21 +118,22 @@ attn_prefill_kernel(const PrefillArgs a) {
   constexpr int RPR = 256 / RB;         // rows per 256 bytes of LDS
   constexpr int RPB = 1024 / RB;        // rows per 1 KiB block (one wave's direct load)
   constexpr int KBYTES = kKeys * RB;    // one tile of K, and one of V
-  // LDS: two stages of K, then three of V (the V of a tile is fetched two
-  // tiles ahead, see the loop)
-  constexpr int VBASE = 2 * KBYTES;
   constexpr int BPW = KBYTES / 1024 / kWaves;   // 1 KiB blocks per wave per tile, K and V each
   static_assert(BPW >= 1 && KBYTES % (1024 * kWaves) == 0, "tile fill");
   // The swizzle of a lane's row is the same in every block it fills.
   static_assert((4 * kWaves) % SW == 0, "block-invariant swizzle");
-  // Whether a wave reads all of a tile's V operands into registers before
-  // it fetches the V of a later tile (see the loop).  An fp32 q (hi + lo)
-  // or P (hi + lo) leaves no room for the 16 staged operands.
-  constexpr bool kStageV = !QF32 && !PLO;
+  // V operands read ahead in the PV loop (of its 2 D / 16 steps): fewer
+  // when q or P take two register sets
+  constexpr int VD = QF32 || PLO ? 3 : 6;
 
-  // 80 KiB: two workgroups per CU.  Nothing else may live in LDS (the
-  // split instances' arrival flag reuses the first word after the loop).
-  __shared__ __attribute__((aligned(16))) unsigned char lds[5 * KBYTES];
+  // Two stages of V (lds_a*) and two of K (lds_b*), 64 KiB for D = 128:
+  // two workgroups per CU.  Separate variables, so the compiler can tell a
+  // read of one stage from a fill of the other in flight (with one array it
+  // makes every transposing read wait for all fills); they are laid out in
+  // the order of their names.  The split instances' arrival flag reuses
+  // lds_b0 after the loop.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_a0[KBYTES], lds_a1[KBYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[KBYTES], lds_b1[KBYTES];
 
   const int Hq = a.Hq, Hkv = a.Hkv, S = a.S, T = a.T;
   const int G = Hq / Hkv;
@@ -402,14 +405,14 @@ attn_prefill_kernel(const PrefillArgs a) {
   // below, and a row the workgroup attends holds finite values).
   auto ksw = [](int r) { return (r / RPR) & (SW - 1); };
   auto vsw = [](int r) { return (2 * (r / RPR)) & (SW - 1); };
-  const int frow = wave * RPB + lane / SW;        // the lane's row in its first block
+    const int frow = wave * RPB + lane / SW;          // the lane's row in its first block
   const uint32_t kfo = (uint32_t)(frow * RB + 16 * ((lane % SW) ^ ksw(frow)));
   const uint32_t vfo = (uint32_t)(frow * RB + 16 * ((lane % SW) ^ vsw(frow)));
   auto clamp_key = [&](int key) { return key < kend ? key : kend - 1; };
-  // One tile of K (V) into K (V) stage `stage`.
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  // One tile of K (V) into the stage at `st`: BPW loads per wave.
   auto issue = [&](int tile, unsigned char* st, uint32_t lane_off,
-                   const __amdgpu_buffer_rsrc_t& rsrc) {
-    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+                   const __amdgpu_buffer_rsrc_t& rsrc) __attribute__((always_inline)) {
     const int base = kbeg + kKeys * tile;
     if (base + kKeys <= kend) {
       // wholly inside the range: the lane's part stays fixed, the tile and
@@ -430,227 +433,232 @@ attn_prefill_kernel(const PrefillArgs a) {
       }
     }
   };
-  auto issue_k = [&](int tile, int stage) { issue(tile, lds + stage * KBYTES, kfo, rk); };
-  auto issue_v = [&](int tile, int stage) {
-    issue(tile, lds + VBASE + stage * KBYTES, vfo, rv);
+  auto kstage = [&](auto S) __attribute__((always_inline)) -> unsigned char* {
+    if constexpr (decltype(S)::value == 0) return lds_b0;
+    else return lds_b1;
+  };
+  auto vstage = [&](auto S) __attribute__((always_inline)) -> unsigned char* {
+    if constexpr (decltype(S)::value == 0) return lds_a0;
+    else return lds_a1;
+  };
+  auto tile_work = [&](int tile) __attribute__((always_inline)) {   // wave-uniform: does the wave attend any key of the tile
+    const int k0 = kbeg + kKeys * tile;
+    return wave_live && k0 < need_hi && k0 + kKeys > need_lo;
   };
 
-  if (te > tb) {
-    issue_k(tb, 0);
-    issue_v(tb, 0);
-    if (te > tb + 1) issue_v(tb + 1, 1);
-  }
-  wait_vmem();
-  __syncthreads();
-  for (int tile = tb; tile < te; ++tile) {
-    // Tile i = tile - tb reads K stage i % 2 and V stage i % 3.  The K of
-    // tile i + 1 is fetched now into the other K stage, which every wave
-    // finished reading before the barrier that ended the previous trip.
-    // The V of tile i + 2 is fetched once this wave has read the V
-    // operands of tile i: the compiler makes every transposed LDS read wait
-    // for all LDS-bound loads in flight (it cannot tell them apart), so a
-    // V fetch issued before the last of this tile's V reads would stall
-    // them.  Staged, all of them are read right after the softmax and the
-    // fetch goes out before the PV calls; unstaged, after them.
-    const int it = tile - tb;
-    const unsigned char* cur = lds + (it & 1) * KBYTES;
-    const unsigned char* curv = lds + VBASE + (it % 3) * KBYTES;
-    if (tile + 1 < te) issue_k(tile + 1, (it + 1) & 1);
-    const int k0 = kbeg + kKeys * tile;
-    const bool work = wave_live && k0 < need_hi && k0 + kKeys > need_lo;   // wave-uniform
-    f32x4_t s[kKB][2];
-    if (work) {
-      // QK for every 16-key block and both row blocks.  The K operands of
-      // block kb + 1 are read from LDS while block kb's calls run (two
-      // register sets; the scheduling barriers keep the reads ahead).
-      u32x4_t kbuf[2][KC];
-      auto kread = [&](int kb, u32x4_t* dst) {
+  constexpr int NH = kKB / 2;
+  f32x4_t s[kKB][2];              // scores of the tile whose softmax comes next
+  u32x4_t ph[NH][2], pl[NH][2];   // P of the tile whose PV comes next
+
+  // QK for every 16-key block and both row blocks of the tile in K stage
+  // `cur`.  The K operands of block kb + 1 are read from LDS while block
+  // kb's calls run (two register sets; the scheduling barriers keep the
+  // reads ahead).
+  auto qk = [&](const unsigned char* cur) __attribute__((always_inline)) {
+    u32x4_t kbuf[2][KC];
+    auto kread = [&](int kb, u32x4_t* dst) {
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          dst[c] = *reinterpret_cast<const u32x4_t*>(
-              cur + (16 * kb + n) * RB + 16 * ((4 * c + k4) ^ ksw(16 * kb + n)));
-      };
-      // The two waves on a SIMD belong to different workgroups and each
-      // alternates matrix-core blocks with VALU softmax work: the one in a
-      // matrix-core block issues first, so the other's VALU work fills the
-      // gaps instead of competing for the same slots.
-      __builtin_amdgcn_s_setprio(1);
-      kread(0, kbuf[0]);
+      for (int c = 0; c < KC; ++c)
+        dst[c] = *reinterpret_cast<const u32x4_t*>(
+            cur + 16 * kb * RB +
+            ((uint32_t)(n * RB + 16 * ((4 * c + k4) ^ ksw(16 * kb + n))) &
+             (uint32_t)(16 * RB - 1)));   // the lane's part masked as the V reads' is
+    };
+    kread(0, kbuf[0]);
 #pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-        s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (kb + 1 < kKB) kread(kb + 1, kbuf[(kb + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int kb = 0; kb < kKB; ++kb) {
+      s[kb][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s[kb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (kb + 1 < kKB) kread(kb + 1, kbuf[(kb + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-          const u32x4_t ka = kbuf[kb & 1][c];
+      for (int c = 0; c < KC; ++c) {
+        const u32x4_t ka = kbuf[kb & 1][c];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < 2; ++j) {
+          s[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qh[j][c]),
+              s[kb][j], 0, 0, 0);
+          if constexpr (QF32)
             s[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, qh[j][c]),
+                __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, ql[j][c]),
                 s[kb][j], 0, 0, 0);
-            if constexpr (QF32)
-              s[kb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, ka), __builtin_bit_cast(bf16x8_t, ql[j][c]),
-                  s[kb][j], 0, 0, 0);
-          }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    constexpr int NH = kKB / 2;
-    u32x4_t ph[NH][2], pl[NH][2];
-    // V operands: column block v, lane row n is column 16 v + n of V, and
-    // its eight k are keys 4 k4 + e and 16 + 4 k4 + e (e < 4) of the half,
-    // the order P holds them in.  Each half comes from one transposed read
-    // (ds_read_b64_tr_b16): in a group of 16 lanes, lane 4 e + q points at
-    // columns 16 v + 4 q .. + 3 of key row 4 k4 + e, and lane n of the group
-    // receives column 16 v + n of the four rows.
+  };
+
+  // The online softmax of the tile starting at key k0: masks, row maxima,
+  // lazy rescale, P = exp2(s * qscale - m * qscale) as the B operands of the
+  // PV calls, one per 32-key half h: bf16 (hi) and, for an fp32 output, the
+  // bf16 remainder (lo).  Word w of half h holds k = 2w, 2w + 1: keys
+  // 32h + (4 k4 + 2w, + 1) for w < 2, 32h + (16 + 4 k4 + 2w - 4, + 1) for
+  // w >= 2.
+  auto softmax = [&](int k0) __attribute__((always_inline)) {
+    const bool full = k0 >= free_lo && k0 + kKeys <= free_hi;
+    float mnew[2];
+    bool need[2];
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 16 * kb + 4 * k4 + i;
+            if (key < rlo[j] || key >= rhi[j]) s[kb][j][i] = -INFINITY;
+          }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float t = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+        t = fmax_nan(t, fmax_nan(fmax_nan(s[kb][j][0], s[kb][j][1]),
+                                 fmax_nan(s[kb][j][2], s[kb][j][3])));
+      t = max_over_rows(t);
+      mnew[j] = fmax_nan(m[j], t);
+      // m = -inf with a finite maximum gives +inf (rescale); both -inf give
+      // NaN (no rescale: the row has seen no key yet).
+      need[j] = (mnew[j] - m[j]) * qscale > kRescaleLog2;
+    }
+    if (__any(need[0] || need[1])) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float alpha = need[j] ? __builtin_amdgcn_exp2f((m[j] - mnew[j]) * qscale) : 1.0f;
+        if (need[j]) {
+          m[j] = mnew[j];
+          mq[j] = m[j] * qscale;
+        }
+        l[j] *= alpha;
+#pragma unroll
+        for (int v = 0; v < VB; ++v) o[j][v] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float mref = mq[j];
+      float p[kKB][4];
+      float ps;
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j][i], qscale, -mref));
+          ps = kb == 0 && i == 0 ? p[0][0] : ps + p[kb][i];
+        }
+      l[j] += ps;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float pa = p[2 * hh + (w >> 1)][2 * (w & 1)];
+          const float pb = p[2 * hh + (w >> 1)][2 * (w & 1) + 1];
+          const uint32_t hw = pack_bf16(pa, pb);
+          ph[hh][j][w] = hw;
+          if constexpr (PLO)
+            pl[hh][j][w] = pack_bf16(pa - __uint_as_float(hw << 16),
+                                     pb - __uint_as_float(hw & 0xffff0000u));
+        }
+    }
+  };
+
+  // PV with the tile in V stage `curv`: O^T[16 cols x 16 rows] +=
+  // V^T[16 x 32] * P^T[32 x 16] per column block and 32-key half.  V
+  // operands: column block v, lane row n is column 16 v + n of V, and its
+  // eight k are keys 4 k4 + e and 16 + 4 k4 + e (e < 4) of the half, the
+  // order P holds them in.  Each half comes from one transposed read
+  // (ds_read_b64_tr_b16): in a group of 16 lanes, lane 4 e + q points at
+  // columns 16 v + 4 q .. + 3 of key row 4 k4 + e, and lane n of the group
+  // receives column 16 v + n of the four rows.
+  auto pv = [&](const unsigned char* curv) __attribute__((always_inline)) {
     typedef __attribute__((ext_vector_type(4))) short s16x4_t;
     typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
     const int vq = lane & 3;
     const int vrow = 4 * k4 + ((lane & 15) >> 2);   // vsw(vrow + 16 m) == vsw(vrow)
-    auto vread = [&](int x) {   // the operand of PV step x = (hh, v)
+    auto vread = [&](int x) {
       const int hh = x / VB, v = x % VB;
       const int col = 16 * v + 4 * vq;
-      const unsigned char* p0 =
-          curv + (32 * hh + vrow) * RB + 16 * ((col / 8) ^ vsw(vrow)) + 2 * (col % 8);
+      // The lane's part of the offset (rows below 16) masked to 16 rows, a
+      // no-op that lets the compiler see the read stays inside the stage
+      // (else it waits for the fills of the other stages in flight); the
+      // half and the second four-row group are constants.
+      const uint32_t o0 = (uint32_t)(vrow * RB + 16 * ((col / 8) ^ vsw(vrow)) + 2 * (col % 8)) &
+                          (uint32_t)(16 * RB - 1);
+      const unsigned char* p0 = curv + o0 + 32 * hh * RB;
       const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
       const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0 + 16 * RB));
       const auto a2 = __builtin_bit_cast(uint2, lo4);
       const auto b2 = __builtin_bit_cast(uint2, hi4);
       return u32x4_t{a2.x, a2.y, b2.x, b2.y};
     };
-    u32x4_t vop[kStageV ? NH * VB : 1];   // staged: the tile's V operands, step x at x
-    if (work) {
-      const bool full = k0 >= free_lo && k0 + kKeys <= free_hi;
-      // Masks and the tile maximum of each row (raw scores; qscale > 0).
-      float mnew[2];
-      bool need[2];
-      if (!full) {
+    // VD operands in flight: an LDS read takes longer than the two calls of
+    // a step
+    u32x4_t vbuf[VD];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int x = 0; x < VD - 1; ++x) vbuf[x] = vread(x);
 #pragma unroll
-          for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = k0 + 16 * kb + 4 * k4 + i;
-              if (key < rlo[j] || key >= rhi[j]) s[kb][j][i] = -INFINITY;
-            }
-      }
+    for (int x = 0; x < NH * VB; ++x) {
+      const int hh = x / VB, v = x % VB;
+      if (x + VD - 1 < NH * VB) vbuf[(x + VD - 1) % VD] = vread(x + VD - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4_t va = vbuf[x % VD];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        float t = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-          t = fmax_nan(t, fmax_nan(fmax_nan(s[kb][j][0], s[kb][j][1]),
-                                   fmax_nan(s[kb][j][2], s[kb][j][3])));
-        t = max_over_rows(t);
-        mnew[j] = fmax_nan(m[j], t);
-        // m = -inf with a finite maximum gives +inf (rescale); both -inf give
-        // NaN (no rescale: the row has seen no key yet).
-        need[j] = (mnew[j] - m[j]) * qscale > kRescaleLog2;
+        o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, ph[hh][j]), o[j][v],
+            0, 0, 0);
+        if constexpr (PLO)
+          o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pl[hh][j]), o[j][v],
+              0, 0, 0);
       }
-      if (__any(need[0] || need[1])) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float alpha = need[j] ? __builtin_amdgcn_exp2f((m[j] - mnew[j]) * qscale) : 1.0f;
-          if (need[j]) {
-            m[j] = mnew[j];
-            mq[j] = m[j] * qscale;
-          }
-          l[j] *= alpha;
-#pragma unroll
-          for (int v = 0; v < VB; ++v) o[j][v] *= alpha;
-        }
-      }
-
-      // P = exp2(s * qscale - m * qscale) as the B operands, one per 32-key
-      // half h: bf16 (hi) and, for an fp32 output, the bf16 remainder (lo).
-      // Word w of half h holds k = 2w, 2w + 1: keys 32h + (4 k4 + 2w, + 1)
-      // for w < 2, 32h + (16 + 4 k4 + 2w - 4, + 1) for w >= 2.
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float mref = mq[j];
-        float p[kKB][4];
-        float ps;
-#pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j][i], qscale, -mref));
-            ps = kb == 0 && i == 0 ? p[0][0] : ps + p[kb][i];
-          }
-        l[j] += ps;
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float pa = p[2 * hh + (w >> 1)][2 * (w & 1)];
-            const float pb = p[2 * hh + (w >> 1)][2 * (w & 1) + 1];
-            const uint32_t hw = pack_bf16(pa, pb);
-            ph[hh][j][w] = hw;
-            if constexpr (PLO)
-              pl[hh][j][w] = pack_bf16(pa - __uint_as_float(hw << 16),
-                                       pb - __uint_as_float(hw & 0xffff0000u));
-          }
-      }
-
-      if constexpr (kStageV) {
-#pragma unroll
-        for (int x = 0; x < NH * VB; ++x) vop[x] = vread(x);
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // The V of tile i + 2 into V stage (i + 2) % 3, which held tile i - 1:
-    // every wave finished reading it before the previous barrier.
-    if constexpr (kStageV)
-      if (tile + 2 < te) issue_v(tile + 2, (it + 2) % 3);
-    if (work) {
-      // PV: O^T[16 cols x 16 rows] += V^T[16 x 32] * P^T[32 x 16] per column
-      // block and 32-key half.  Unstaged, the operand of step x + 1 is read
-      // while step x runs.
-      u32x4_t vbuf[2];
-      if constexpr (!kStageV) vbuf[0] = vread(0);
+  };
+
+
+  // Tile i (counted from this split's first tile) sits in K and V stage
+  // i % 2.  At the top of trip i the K and V of tile i + 1 are fetched into
+  // the other stages, which every wave finished reading before the barrier
+  // that ended trip i - 1; the trip ends with each wave waiting for its own
+  // fills and a barrier, after which every wave sees them.  The loop is
+  // unrolled by two so that every LDS access names its stage variable.
+  const int nt = te - tb;
+  if (nt > 0) {
+    issue(tb, lds_b0, kfo, rk);
+    issue(tb, lds_a0, vfo, rv);
+  }
+  wait_vmem();
+  __syncthreads();
+  auto trip = [&](int it, auto ST) __attribute__((always_inline)) {
+    constexpr int st = decltype(ST)::value;
+    const auto other = std::integral_constant<int, 1 - st>{};
+    const int tile = tb + it;
+    if (it + 1 < nt) {
+      issue(tile + 1, kstage(other), kfo, rk);
+      issue(tile + 1, vstage(other), vfo, rv);
+    }
+    if (tile_work(tile)) {
+      // The two waves on a SIMD belong to different workgroups and each
+      // alternates matrix-core blocks with VALU softmax work: the one in a
+      // matrix-core block issues first, so the other's VALU work fills the
+      // gaps instead of competing for the same slots.
       __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-        for (int v = 0; v < VB; ++v) {
-          const int x = hh * VB + v;
-          u32x4_t va;
-          if constexpr (kStageV) {
-            va = vop[x];
-          } else {
-            if (x + 1 < NH * VB) vbuf[(x + 1) & 1] = vread(x + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            va = vbuf[x & 1];
-          }
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, ph[hh][j]),
-                o[j][v], 0, 0, 0);
-            if constexpr (PLO)
-              o[j][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pl[hh][j]),
-                  o[j][v], 0, 0, 0);
-          }
-          if constexpr (!kStageV) __builtin_amdgcn_sched_barrier(0);
-        }
+      qk(kstage(ST));
+      __builtin_amdgcn_s_setprio(0);
+      softmax(kbeg + kKeys * tile);
+      __builtin_amdgcn_s_setprio(1);
+      pv(vstage(ST));
       __builtin_amdgcn_s_setprio(0);
     }
-    if constexpr (!kStageV)
-      if (tile + 2 < te) issue_v(tile + 2, (it + 2) % 3);
-    // This wave's fetches of K i + 1 and V i + 1 have landed (only the
-    // V i + 2 fetch may still be in flight), and after the barrier every
-    // wave's have, and every wave is done with K stage i % 2.
-    if (tile + 2 < te)
-      wait_vmem_but<BPW>();
-    else
-      wait_vmem();
+    wait_vmem();
     barrier_lds();
+  };
+  for (int it = 0; it < nt; it += 2) {
+    trip(it, std::integral_constant<int, 0>{});
+    if (it + 1 < nt) trip(it + 1, std::integral_constant<int, 1>{});
   }
 
   // Normalise and store.  Lane (n, k4) holds, for row n of block j, columns
@@ -710,7 +718,7 @@ attn_prefill_kernel(const PrefillArgs a) {
   wait_vmem();
   __syncthreads();
   // the tile stages are no longer read: their first word carries the flag
-  int* s_last = reinterpret_cast<int*>(lds);
+  int* s_last = reinterpret_cast<int*>(lds_b0);
   uint32_t* ticket = a.ws_cnt + team;
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
