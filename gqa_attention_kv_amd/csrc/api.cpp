@@ -340,11 +340,12 @@ int gqa_attn_prefill_default_splits(int B, int S, int Hq, int Hkv) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1)
     return 1;
-  // Fewer row blocks than two per CU: two splits.  More splits measured
-  // slower on the fresh S = 1024 prefill (each split writes and the last
-  // reads back a 64 KB partial, as much as its share of the keys).
+  // Fewer row blocks than CUs: two splits.  With as many row blocks as CUs
+  // (the fresh S = 1024 prefill) one split measured faster than two, and
+  // three or four slower still: each split writes and the last reads back
+  // a 64 KB partial, as much as its share of the keys.
   const int64_t wgs = prefill_teams(B, S, Hq, Hkv);
-  return wgs < 2 * (int64_t)cus ? 2 : 1;
+  return wgs < (int64_t)cus ? 2 : 1;
 }
 
 int gqa_attn_prefill_split(const void* q, gqa_dtype_t q_dtype,

@@ -400,7 +400,7 @@ int gqa_attn_prefill(const void* q, gqa_dtype_t q_dtype,
  * GQA_ERR_NULL (splits > 1 without a workspace), GQA_ERR_WORKSPACE (too
  * small) and GQA_ERR_ALIGN (workspace not 256-byte aligned).
  * gqa_attn_prefill_default_splits suggests a split count for the current
- * device: 2 when the launch has fewer row blocks than two per CU, else 1;
+ * device: 2 when the launch has fewer row blocks than CUs, else 1;
  * it reads device attributes only and returns 1 when they cannot be read.
  */
 /*
