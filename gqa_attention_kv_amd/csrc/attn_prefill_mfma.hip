@@ -105,10 +105,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // bf16 / float32 that the kernel normalises and rotates itself (the q half
 // of the prologue).  SPLIT: the launch shares each row block's keys among
 // a.splits > 1 workgroups (the instances without it keep the plain loop and
-// epilogue).
-template <int D, int QM, bool PLO, bool SPLIT>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void
+// epilogue).  KG: key groups per workgroup -- with KG = 2 the workgroup has
+// two groups of kWaves waves on the same rows, group g taking the tiles
+// g, g + 2, ... of the range, combined through LDS at the end (for launches
+// too small to give every CU two workgroups).
+template <int D, int QM, bool PLO, bool SPLIT, int KG>
+__global__ __launch_bounds__(kWaves * KG * 64) __attribute__((amdgpu_waves_per_eu(2))) void
 attn_prefill_kernel(const PrefillArgs a) {
+  static_assert(KG == 1 || KG == 2, "one or two key groups");
+  constexpr int NTH = kWaves * KG * 64;   // threads
   constexpr bool QF32 = QM != 0;       // q carried as bf16 hi + lo
   constexpr bool PRO = QM >= 2;
   constexpr int KC = D / 32;            // QK slices
@@ -126,14 +131,19 @@ attn_prefill_kernel(const PrefillArgs a) {
   // when q or P take two register sets
   constexpr int VD = QF32 || PLO ? 3 : 6;
 
-  // Two stages of V (lds_a*) and two of K (lds_b*), 64 KiB for D = 128:
-  // two workgroups per CU.  Separate variables, so the compiler can tell a
-  // read of one stage from a fill of the other in flight (with one array it
-  // makes every transposing read wait for all fills); they are laid out in
-  // the order of their names.  The split instances' arrival flag reuses
-  // lds_b0 after the loop.
+  // Two stages of V (lds_a*) and two of K (lds_b*) per key group, 64 KiB
+  // per group for D = 128: two one-group workgroups per CU, or one
+  // two-group workgroup (the second group's stages are lds_c*, lds_d*).
+  // Separate variables, so the compiler can tell a read of one stage from a
+  // fill of another in flight (with one array it makes every transposing
+  // read wait for all fills); they are laid out in the order of their names.
+  // The split instances' arrival flag reuses lds_b0 after the loop, and the
+  // key groups' combine the first group's stages and lds_c0.
+  constexpr int KB2 = KG == 2 ? KBYTES : 16;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_a0[KBYTES], lds_a1[KBYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char lds_b0[KBYTES], lds_b1[KBYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_c0[KB2], lds_c1[KB2];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_d0[KB2], lds_d1[KB2];
 
   const int Hq = a.Hq, Hkv = a.Hkv, S = a.S, T = a.T;
   const int G = Hq / Hkv;
@@ -166,7 +176,9 @@ attn_prefill_kernel(const PrefillArgs a) {
   const int lane = tid & 63;
   // wave index in a scalar register, so tests on the wave's rows (which
   // tiles it works on, which need masks) are scalar branches
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv / kWaves;    // key group
+  const int wave = wv % kWaves;   // wave within the group: its rows and its share of the fills
   const int n = lane & 15, k4 = lane >> 4;
 
   const int len = a.lens[b];
@@ -204,6 +216,91 @@ attn_prefill_kernel(const PrefillArgs a) {
     free_lo = lo_of(n1);
     free_hi = n0;
   }
+
+  const int64_t slab = ((int64_t)b * Hkv + g) * T * D;
+  const uint32_t slab_bytes = (uint32_t)((int64_t)T * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = slab_rsrc(a.k_cache + slab, slab_bytes);
+  const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache + slab, slab_bytes);
+
+  const int ntiles = kend > kbeg ? (kend - kbeg + kKeys - 1) / kKeys : 0;
+  // This split's tiles [tb, te): the row block's tiles in `splits` nearly
+  // equal runs (all of them with one split).
+  const int per = (ntiles + splits - 1) / splits;
+  const int tb = min(sp * per, ntiles);
+  const int te = min(tb + per, ntiles);
+
+  // Tile fill: K and V rows go from the cache straight into LDS (buffer
+  // loads with the LDS destination, no register round trip).  One such load
+  // writes 1 KiB of LDS, lane i the 16 bytes at 16 i: RPB rows.  Rows are
+  // stored unpadded with their 16-byte chunks permuted -- chunk c of K row r
+  // at position c ^ ksw(r), of V row r at c ^ vsw(r) -- so that the operand
+  // reads below spread over all banks: a K read takes one chunk of 16
+  // consecutive rows, a transposed V read two adjacent chunks of 8
+  // consecutive rows per half-wave.  Lane i of wave w fills, in block
+  // w + kWaves f of the tile, row RPB (w + kWaves f) + i / SW, position
+  // i % SW, i.e. global chunk (i % SW) ^ swizzle; that swizzle does not
+  // depend on f.  Keys past the range are clamped into it (they are masked
+  // below, and a row the workgroup attends holds finite values).
+  auto ksw = [](int r) { return (r / RPR) & (SW - 1); };
+  auto vsw = [](int r) { return (2 * (r / RPR)) & (SW - 1); };
+  const int frow = wave * RPB + lane / SW;        // the lane's row in its first block
+  const uint32_t kfo = (uint32_t)(frow * RB + 16 * ((lane % SW) ^ ksw(frow)));
+  const uint32_t vfo = (uint32_t)(frow * RB + 16 * ((lane % SW) ^ vsw(frow)));
+  auto clamp_key = [&](int key) { return key < kend ? key : kend - 1; };
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  // One tile of K (V) into the stage at `st`: BPW loads per wave.
+  auto issue = [&](int tile, unsigned char* st, uint32_t lane_off,
+                   const __amdgpu_buffer_rsrc_t& rsrc) __attribute__((always_inline)) {
+    const int base = kbeg + kKeys * tile;
+    if (base + kKeys <= kend) {
+      // wholly inside the range: the lane's part stays fixed, the tile and
+      // the block go in the scalar offset
+#pragma unroll
+      for (int f = 0; f < BPW; ++f)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (lds_ptr_t)(st + 1024 * (wave + kWaves * f)), 16, lane_off,
+            (uint32_t)base * (uint32_t)RB + (uint32_t)(kWaves * f * 1024), 0, 0);
+    } else {
+#pragma unroll
+      for (int f = 0; f < BPW; ++f) {
+        const int blk = wave + kWaves * f;
+        const uint32_t vo = (uint32_t)clamp_key(base + blk * RPB + lane / SW) * (uint32_t)RB +
+                            (lane_off & (uint32_t)(RB - 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(st + 1024 * blk), 16, vo, 0,
+                                                 0, 0);
+      }
+    }
+  };
+  // stage S of key group GR
+  auto kstage = [&](auto GR, auto S) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int gr = decltype(GR)::value, st = decltype(S)::value;
+    if constexpr (gr == 0) return st == 0 ? lds_b0 : lds_b1;
+    else return st == 0 ? lds_d0 : lds_d1;
+  };
+  auto vstage = [&](auto GR, auto S) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int gr = decltype(GR)::value, st = decltype(S)::value;
+    if constexpr (gr == 0) return st == 0 ? lds_a0 : lds_a1;
+    else return st == 0 ? lds_c0 : lds_c1;
+  };
+  // The first tile of each key group goes out before the q prologue, so
+  // that its latency overlaps it: right away when q arrives ready, after the
+  // q loads when the kernel normalises and rotates q (loads complete in
+  // order, so the q arithmetic must not wait behind the tile).
+  // The fill is issued even for a group without tiles (its rows are clamped
+  // into the range, or read past the slab, which returns zeros): with the
+  // same number of loads on every path the compiler can wait for the q
+  // loads alone.
+  const int nt = te - tb;
+  auto first_fill = [&]() __attribute__((always_inline)) {
+    if (KG == 1 || grp == 0) {
+      issue(tb, lds_b0, kfo, rk);
+      issue(tb, lds_a0, vfo, rv);
+    } else {
+      issue(tb + 1, lds_d0, kfo, rk);
+      issue(tb + 1, lds_c0, vfo, rv);
+    }
+  };
+  if constexpr (!PRO) first_fill();
 
   // q operands (B of the QK calls): lane holds row n of block j, elements
   // 32c + 8 k4 .. + 8.
@@ -248,104 +345,143 @@ attn_prefill_kernel(const PrefillArgs a) {
     // turns in float64, sin and cos from v_sin_f32 / v_cos_f32, which take
     // turns.  NeoX pairs (i, i + D/2) sit in slices c and c + KC/2 of the
     // same lane; interleaved pairs (2i, 2i + 1) side by side in one slice.
-    float f[2][KC][8];
-    bool ok[2];
-    int tk[2];
+    // With two key groups the work is shared: group g computes row block g
+    // of its rows (slot 0 below) and the bf16 hi / lo operands are exchanged
+    // through LDS, so each SIMD computes every row once.
+    constexpr bool SQ = KG == 2;
+    constexpr int NJ = SQ ? 1 : 2;        // row blocks computed by this wave
+    auto jrow = [&](int jj) { return SQ ? grp : jj; };
+    float f[NJ][KC][8];
+    bool ok[NJ];
+    int tk[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = r0 + kRowsPerWave * wave + 16 * j + n;
-      ok[j] = row < SG;
-      tk[j] = ok[j] ? row / G : 0;
-      const int h = ok[j] ? row % G : 0;
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int row = r0 + kRowsPerWave * wave + 16 * jrow(jj) + n;
+      ok[jj] = row < SG;
+      tk[jj] = ok[jj] ? row / G : 0;
+      const int h = ok[jj] ? row % G : 0;
       const int64_t qoff =
-          (int64_t)b * a.q_bstride + ((int64_t)tk[j] * Hq + (int64_t)g * G + h) * D;
+          (int64_t)b * a.q_bstride + ((int64_t)tk[jj] * Hq + (int64_t)g * G + h) * D;
+      // Every load is issued unconditionally (a row past S*G reads token 0,
+      // head 0 of the group and is zeroed below), so they are all in flight
+      // together instead of one branch, and one wait, each.
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const int e = 32 * c + 8 * k4;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[j][c][i] = 0.0f;
-        if (!ok[j]) continue;
         if constexpr (QM == 3) {
           const float* p = reinterpret_cast<const float*>(a.q) + qoff + e;
           const float4 u = *reinterpret_cast<const float4*>(p);
           const float4 v = *reinterpret_cast<const float4*>(p + 4);
-          f[j][c][0] = u.x; f[j][c][1] = u.y; f[j][c][2] = u.z; f[j][c][3] = u.w;
-          f[j][c][4] = v.x; f[j][c][5] = v.y; f[j][c][6] = v.z; f[j][c][7] = v.w;
+          f[jj][c][0] = u.x; f[jj][c][1] = u.y; f[jj][c][2] = u.z; f[jj][c][3] = u.w;
+          f[jj][c][4] = v.x; f[jj][c][5] = v.y; f[jj][c][6] = v.z; f[jj][c][7] = v.w;
         } else {
           const u32x4_t w = *reinterpret_cast<const u32x4_t*>(
               reinterpret_cast<const uint16_t*>(a.q) + qoff + e);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            f[j][c][2 * i] = __uint_as_float(w[i] << 16);
-            f[j][c][2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+            f[jj][c][2 * i] = __uint_as_float(w[i] << 16);
+            f[jj][c][2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
           }
         }
       }
     }
+    // the norm weights and the rotary frequencies of the lane's pairs (NeoX:
+    // pair 32 c + 8 k4 + i of slice c < KC/2; interleaved: pair
+    // 16 c + 4 k4 + i/2 of slice c) are loaded with the q rows too
+    float wv[KC][8];
     if (a.wq != nullptr) {
-      float rs[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float ss = 0.0f;
-#pragma unroll
-        for (int c = 0; c < KC; ++c)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) ss = fmaf(f[j][c][i], f[j][c][i], ss);
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        rs[j] = ok[j] ? 1.0f / sqrtf(ss / (float)D + a.eps) : 0.0f;
-      }
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const float4 u = *reinterpret_cast<const float4*>(a.wq + 32 * c + 8 * k4);
         const float4 v = *reinterpret_cast<const float4*>(a.wq + 32 * c + 8 * k4 + 4);
-        const float wv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) f[j][c][i] = f[j][c][i] * rs[j] * wv[i];
+        wv[c][0] = u.x; wv[c][1] = u.y; wv[c][2] = u.z; wv[c][3] = u.w;
+        wv[c][4] = v.x; wv[c][5] = v.y; wv[c][6] = v.z; wv[c][7] = v.w;
       }
+    }
+    constexpr int NFR = D / 8;   // rotary pairs per lane
+    double fr[NFR];
+    if (a.rope) {
+      if (a.rope_interleaved) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) fr[4 * c + t] = a.inv_freq_rev[16 * c + 4 * k4 + t];
+      } else {
+#pragma unroll
+        for (int c = 0; c < KC / 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) fr[8 * c + i] = a.inv_freq_rev[32 * c + 8 * k4 + i];
+      }
+    }
+    first_fill();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[jj][c][i] = ok[jj] ? f[jj][c][i] : 0.0f;
+    if (a.wq != nullptr) {
+      float rs[NJ];
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ss = fmaf(f[jj][c][i], f[jj][c][i], ss);
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        rs[jj] = ok[jj] ? 1.0f / sqrtf(ss / (float)D + a.eps) : 0.0f;
+      }
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) f[jj][c][i] = f[jj][c][i] * rs[jj] * wv[c][i];
     }
     if (a.rope) {
       const float ms = a.rope_mscale;
       const int64_t p0 = a.pos[b];
-      // element (c, i) of row j and its partner (c2, i2) rotate by pair
-      // `pair` (indices stay compile-time: one loop per layout)
-      auto rotate = [&](int c, int i, int c2, int i2, int pair) {
-        const double fr_pair = a.inv_freq_rev[pair];
+      // element (c, i) of each row and its partner (c2, i2) rotate by the
+      // lane's pair `slot` (indices stay compile-time: one loop per layout)
+      auto rotate = [&](int c, int i, int c2, int i2, int slot) {
+        const double fr_pair = fr[slot];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const double rev = (double)(p0 + tk[j]) * fr_pair;
-          const float fr = (float)(rev - rint(rev));
-          const float cs = __builtin_amdgcn_cosf(fr) * ms, sn = __builtin_amdgcn_sinf(fr) * ms;
-          const float a1 = f[j][c][i], a2 = f[j][c2][i2];
-          f[j][c][i] = a1 * cs - a2 * sn;
-          f[j][c2][i2] = a2 * cs + a1 * sn;
+        for (int jj = 0; jj < NJ; ++jj) {
+          const double rev = (double)(p0 + tk[jj]) * fr_pair;
+          const float frac = (float)(rev - rint(rev));
+          const float cs = __builtin_amdgcn_cosf(frac) * ms, sn = __builtin_amdgcn_sinf(frac) * ms;
+          const float a1 = f[jj][c][i], a2 = f[jj][c2][i2];
+          f[jj][c][i] = a1 * cs - a2 * sn;
+          f[jj][c2][i2] = a2 * cs + a1 * sn;
         }
       };
       if (a.rope_interleaved) {
 #pragma unroll
         for (int c = 0; c < KC; ++c)
 #pragma unroll
-          for (int i = 0; i < 8; i += 2) rotate(c, i, c, i + 1, 16 * c + 4 * k4 + i / 2);
+          for (int i = 0; i < 8; i += 2) rotate(c, i, c, i + 1, 4 * c + i / 2);
       } else {
 #pragma unroll
         for (int c = 0; c < KC / 2; ++c)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) rotate(c, i, c + KC / 2, i, 32 * c + 8 * k4 + i);
+          for (int i = 0; i < 8; ++i) rotate(c, i, c + KC / 2, i, 8 * c + i);
       }
     }
+    u32x4_t hq[NJ][KC], lq[NJ][KC];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (a.q_out != nullptr && sp == 0 && ok[j]) {
-        const int row = r0 + kRowsPerWave * wave + 16 * j + n;
-        float* qo = a.q_out + (((int64_t)b * S + tk[j]) * Hq + (int64_t)g * G + row % G) * D;
+    for (int jj = 0; jj < NJ; ++jj) {
+      if (a.q_out != nullptr && sp == 0 && (SQ || grp == 0) && ok[jj]) {
+        const int row = r0 + kRowsPerWave * wave + 16 * jrow(jj) + n;
+        float* qo = a.q_out + (((int64_t)b * S + tk[jj]) * Hq + (int64_t)g * G + row % G) * D;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
           *reinterpret_cast<float4*>(qo + 32 * c + 8 * k4) =
-              float4{f[j][c][0], f[j][c][1], f[j][c][2], f[j][c][3]};
+              float4{f[jj][c][0], f[jj][c][1], f[jj][c][2], f[jj][c][3]};
           *reinterpret_cast<float4*>(qo + 32 * c + 8 * k4 + 4) =
-              float4{f[j][c][4], f[j][c][5], f[j][c][6], f[j][c][7]};
+              float4{f[jj][c][4], f[jj][c][5], f[jj][c][6], f[jj][c][7]};
         }
       }
 #pragma unroll
@@ -353,11 +489,49 @@ attn_prefill_kernel(const PrefillArgs a) {
         bf16x8_t hv, lv;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          hv[i] = (__bf16)f[j][c][i];
-          lv[i] = (__bf16)(f[j][c][i] - (float)hv[i]);
+          hv[i] = (__bf16)f[jj][c][i];
+          lv[i] = (__bf16)(f[jj][c][i] - (float)hv[i]);
         }
-        qh[j][c] = __builtin_bit_cast(u32x4_t, hv);
-        ql[j][c] = __builtin_bit_cast(u32x4_t, lv);
+        hq[jj][c] = __builtin_bit_cast(u32x4_t, hv);
+        lq[jj][c] = __builtin_bit_cast(u32x4_t, lv);
+      }
+    }
+    if constexpr (!SQ) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          qh[j][c] = hq[j][c];
+          ql[j][c] = lq[j][c];
+        }
+    } else {
+      // Exchange through the second stages, which no fill has touched yet
+      // (the first fills of the loop follow its opening barrier, and that
+      // barrier waits for these reads): row block j's operands of wave w
+      // sit at lane (16 B x 2 KC per lane) in the 8 KiB quarter w % 2 of
+      // lds_a1 / lds_b1 (j = 0) or lds_c1 / lds_d1 (j = 1), the variable
+      // chosen by w / 2.
+      constexpr int QB = 2 * KC * 16;   // bytes per lane
+      static_assert(2 * 64 * QB <= KB2, "exchange fits a stage");
+      auto area = [&](int j) -> unsigned char* {
+        unsigned char* v = j == 0 ? (wave < 2 ? lds_a1 : lds_b1) : (wave < 2 ? lds_c1 : lds_d1);
+        return v + (wave & 1) * 64 * QB + lane * QB;
+      };
+      unsigned char* mine = area(grp);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        *reinterpret_cast<u32x4_t*>(mine + 16 * c) = hq[0][c];
+        *reinterpret_cast<u32x4_t*>(mine + 16 * (KC + c)) = lq[0][c];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const unsigned char* src = area(j);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          qh[j][c] = *reinterpret_cast<const u32x4_t*>(src + 16 * c);
+          ql[j][c] = *reinterpret_cast<const u32x4_t*>(src + 16 * (KC + c));
+        }
       }
     }
   }
@@ -379,68 +553,6 @@ attn_prefill_kernel(const PrefillArgs a) {
   float l[2] = {0.f, 0.f};
   const float qscale = a.qscale;
 
-  const int64_t slab = ((int64_t)b * Hkv + g) * T * D;
-  const uint32_t slab_bytes = (uint32_t)((int64_t)T * D * 2);
-  const __amdgpu_buffer_rsrc_t rk = slab_rsrc(a.k_cache + slab, slab_bytes);
-  const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache + slab, slab_bytes);
-
-  const int ntiles = kend > kbeg ? (kend - kbeg + kKeys - 1) / kKeys : 0;
-  // This split's tiles [tb, te): the row block's tiles in `splits` nearly
-  // equal runs (all of them with one split).
-  const int per = (ntiles + splits - 1) / splits;
-  const int tb = min(sp * per, ntiles);
-  const int te = min(tb + per, ntiles);
-
-  // Tile fill: K and V rows go from the cache straight into LDS (buffer
-  // loads with the LDS destination, no register round trip).  One such load
-  // writes 1 KiB of LDS, lane i the 16 bytes at 16 i: RPB rows.  Rows are
-  // stored unpadded with their 16-byte chunks permuted -- chunk c of K row r
-  // at position c ^ ksw(r), of V row r at c ^ vsw(r) -- so that the operand
-  // reads below spread over all banks: a K read takes one chunk of 16
-  // consecutive rows, a transposed V read two adjacent chunks of 8
-  // consecutive rows per half-wave.  Lane i of wave w fills, in block
-  // w + kWaves f of the tile, row RPB (w + kWaves f) + i / SW, position
-  // i % SW, i.e. global chunk (i % SW) ^ swizzle; that swizzle does not
-  // depend on f.  Keys past the range are clamped into it (they are masked
-  // below, and a row the workgroup attends holds finite values).
-  auto ksw = [](int r) { return (r / RPR) & (SW - 1); };
-  auto vsw = [](int r) { return (2 * (r / RPR)) & (SW - 1); };
-    const int frow = wave * RPB + lane / SW;          // the lane's row in its first block
-  const uint32_t kfo = (uint32_t)(frow * RB + 16 * ((lane % SW) ^ ksw(frow)));
-  const uint32_t vfo = (uint32_t)(frow * RB + 16 * ((lane % SW) ^ vsw(frow)));
-  auto clamp_key = [&](int key) { return key < kend ? key : kend - 1; };
-  typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  // One tile of K (V) into the stage at `st`: BPW loads per wave.
-  auto issue = [&](int tile, unsigned char* st, uint32_t lane_off,
-                   const __amdgpu_buffer_rsrc_t& rsrc) __attribute__((always_inline)) {
-    const int base = kbeg + kKeys * tile;
-    if (base + kKeys <= kend) {
-      // wholly inside the range: the lane's part stays fixed, the tile and
-      // the block go in the scalar offset
-#pragma unroll
-      for (int f = 0; f < BPW; ++f)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (lds_ptr_t)(st + 1024 * (wave + kWaves * f)), 16, lane_off,
-            (uint32_t)base * (uint32_t)RB + (uint32_t)(kWaves * f * 1024), 0, 0);
-    } else {
-#pragma unroll
-      for (int f = 0; f < BPW; ++f) {
-        const int blk = wave + kWaves * f;
-        const uint32_t vo = (uint32_t)clamp_key(base + blk * RPB + lane / SW) * (uint32_t)RB +
-                            (lane_off & (uint32_t)(RB - 1));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(st + 1024 * blk), 16, vo, 0,
-                                                 0, 0);
-      }
-    }
-  };
-  auto kstage = [&](auto S) __attribute__((always_inline)) -> unsigned char* {
-    if constexpr (decltype(S)::value == 0) return lds_b0;
-    else return lds_b1;
-  };
-  auto vstage = [&](auto S) __attribute__((always_inline)) -> unsigned char* {
-    if constexpr (decltype(S)::value == 0) return lds_a0;
-    else return lds_a1;
-  };
   auto tile_work = [&](int tile) __attribute__((always_inline)) {   // wave-uniform: does the wave attend any key of the tile
     const int k0 = kbeg + kKeys * tile;
     return wave_live && k0 < need_hi && k0 + kKeys > need_lo;
@@ -625,40 +737,95 @@ attn_prefill_kernel(const PrefillArgs a) {
   // that ended trip i - 1; the trip ends with each wave waiting for its own
   // fills and a barrier, after which every wave sees them.  The loop is
   // unrolled by two so that every LDS access names its stage variable.
-  const int nt = te - tb;
-  if (nt > 0) {
-    issue(tb, lds_b0, kfo, rk);
-    issue(tb, lds_a0, vfo, rv);
-  }
-  wait_vmem();
-  __syncthreads();
-  auto trip = [&](int it, auto ST) __attribute__((always_inline)) {
-    constexpr int st = decltype(ST)::value;
-    const auto other = std::integral_constant<int, 1 - st>{};
-    const int tile = tb + it;
-    if (it + 1 < nt) {
-      issue(tile + 1, kstage(other), kfo, rk);
-      issue(tile + 1, vstage(other), vfo, rv);
-    }
-    if (tile_work(tile)) {
-      // The two waves on a SIMD belong to different workgroups and each
-      // alternates matrix-core blocks with VALU softmax work: the one in a
-      // matrix-core block issues first, so the other's VALU work fills the
-      // gaps instead of competing for the same slots.
-      __builtin_amdgcn_s_setprio(1);
-      qk(kstage(ST));
-      __builtin_amdgcn_s_setprio(0);
-      softmax(kbeg + kKeys * tile);
-      __builtin_amdgcn_s_setprio(1);
-      pv(vstage(ST));
-      __builtin_amdgcn_s_setprio(0);
-    }
+  // Key group GR's share of the range: tiles tb + GR + KG it.  Its tile it
+  // sits in the group's K and V stage it % 2 (tile 0 was fetched before the
+  // q prologue); at the top of trip it the K
+  // and V of its next tile are fetched into the other stages, which every
+  // wave finished reading before the barrier that ended trip it - 1; the
+  // trip ends with each wave waiting for its own fills and a barrier, after
+  // which every wave sees them.  The loop is unrolled by two so that every
+  // LDS access names its stage variable.  Both groups pass as many
+  // barriers: the one with a tile less passes an extra one.
+  auto run = [&](auto GR) __attribute__((always_inline)) {
+    constexpr int gr = decltype(GR)::value;
+    using ic0 = std::integral_constant<int, 0>;
+    using ic1 = std::integral_constant<int, 1>;
+    const int ng = nt > gr ? (nt - gr + KG - 1) / KG : 0;
+    // (the group's first tile was fetched before the q prologue)
     wait_vmem();
-    barrier_lds();
+    __syncthreads();
+    auto trip = [&](int it, auto ST) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value;
+      const auto other = std::integral_constant<int, 1 - st>{};
+      const int tile = tb + gr + KG * it;
+      if (it + 1 < ng) {
+        issue(tile + KG, kstage(GR, other), kfo, rk);
+        issue(tile + KG, vstage(GR, other), vfo, rv);
+      }
+      if (tile_work(tile)) {
+        // The two waves on a SIMD each alternate matrix-core blocks with
+        // VALU softmax work: the one in a matrix-core block issues first, so
+        // the other's VALU work fills the gaps instead of competing for the
+        // same slots.
+        __builtin_amdgcn_s_setprio(1);
+        qk(kstage(GR, ST));
+        __builtin_amdgcn_s_setprio(0);
+        softmax(kbeg + kKeys * tile);
+        __builtin_amdgcn_s_setprio(1);
+        pv(vstage(GR, ST));
+        __builtin_amdgcn_s_setprio(0);
+      }
+      wait_vmem();
+      barrier_lds();
+    };
+    for (int it = 0; it < ng; it += 2) {
+      trip(it, ic0{});
+      if (it + 1 < ng) trip(it + 1, ic1{});
+    }
+    if (KG == 2 && ng < (nt + KG - 1) / KG) barrier_lds();
   };
-  for (int it = 0; it < nt; it += 2) {
-    trip(it, std::integral_constant<int, 0>{});
-    if (it + 1 < nt) trip(it + 1, std::integral_constant<int, 1>{});
+  if constexpr (KG == 1) {
+    run(std::integral_constant<int, 0>{});
+  } else {
+    if (grp == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+    // Combine the groups' states, row by row, into the first group's
+    // registers: the second group's wave w leaves its o (16 KiB per wave),
+    // reference maxima and sums in LDS; the first group's wave w holds the
+    // same rows in the same lanes.  Every stage read has returned and no
+    // fill is in flight (each group's last trip fetches nothing).
+    float* om = reinterpret_cast<float*>(wave == 0 ? lds_a0 : wave == 1 ? lds_a1
+                                         : wave == 2 ? lds_b0 : lds_b1);
+    float* ml = reinterpret_cast<float*>(lds_c0) + 4 * 64 * wave;
+    if (grp == 1) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < VB; ++v)
+          *reinterpret_cast<f32x4_t*>(om + 4 * ((j * VB + v) * 64 + lane)) = o[j][v];
+      *reinterpret_cast<f32x4_t*>(ml + 4 * lane) = f32x4_t{m[0], m[1], l[0], l[1]};
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const f32x4_t o2 = *reinterpret_cast<const f32x4_t*>(ml + 4 * lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        // both references are maxima (or -inf) of raw scores; the merged
+        // one is the larger, and each side's weights scale by 2^((m - M) q)
+        const float m2 = o2[j], l2 = o2[2 + j];
+        const float M = fmax_nan(m[j], m2);
+        const bool any = M != -INFINITY;
+        const float a1 = any ? __builtin_amdgcn_exp2f((m[j] - M) * qscale) : 0.0f;
+        const float a2 = any ? __builtin_amdgcn_exp2f((m2 - M) * qscale) : 0.0f;
+        l[j] = l[j] * a1 + l2 * a2;
+#pragma unroll
+        for (int v = 0; v < VB; ++v) {
+          const f32x4_t ov = *reinterpret_cast<const f32x4_t*>(om + 4 * ((j * VB + v) * 64 + lane));
+          o[j][v] = o[j][v] * a1 + ov * a2;
+        }
+        m[j] = M;
+      }
+    }
   }
 
   // Normalise and store.  Lane (n, k4) holds, for row n of block j, columns
@@ -670,6 +837,7 @@ attn_prefill_kernel(const PrefillArgs a) {
   const __amdgpu_buffer_rsrc_t ro =
       SPLIT ? slab_rsrc(a.ws_o + team * splits * kRows * D, (uint32_t)(splits * kRows * D * 4))
             : slab_rsrc(nullptr, 0u);
+  // (with two key groups the first one holds the combined rows)
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float lt = l[j];
@@ -677,7 +845,7 @@ attn_prefill_kernel(const PrefillArgs a) {
     lt += __shfl_xor(lt, 32, 64);
     const int rr = kRowsPerWave * wave + 16 * j + n;    // row within the block
     const int row = r0 + rr;
-    if (row >= SG) continue;
+    if (row >= SG || grp != 0) continue;
     const int t = row / G, h = row % G;
     const int64_t orow = ((int64_t)b * S + t) * Hq + (int64_t)g * G + h;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
@@ -730,11 +898,11 @@ attn_prefill_kernel(const PrefillArgs a) {
   }
   __syncthreads();
   if (!*s_last) return;
-  // Thread tid owns float4 groups tid + 256 i of the block's rows x D: row
-  // (tid + 256 i) / (D/4).  One memory round trip per split: M, W and A are
+  // Thread tid owns float4 groups tid + NTH i of the block's rows x D: row
+  // (tid + NTH i) / (D/4).  One memory round trip per split: M, W and A are
   // the running maximum lse, weight sum and weighted sum.
   constexpr int QD = D / 4;
-  constexpr int GPT = kRows * QD / (kWaves * 64);
+  constexpr int GPT = kRows * QD / NTH;
   const int nvalid = SG - r0 < kRows ? SG - r0 : kRows;
   const float* lse_t = a.ws_lse + team * splits * kRows;
   float Mx[GPT], Wx[GPT];
@@ -750,7 +918,7 @@ attn_prefill_kernel(const PrefillArgs a) {
     float4 ok[GPT];
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
-      const int gi = tid + kWaves * 64 * i;
+      const int gi = tid + NTH * i;
       const int rr = gi / QD, d4 = gi % QD;
       lk[i] = -INFINITY;
       ok[i] = float4{0.f, 0.f, 0.f, 0.f};
@@ -778,7 +946,7 @@ attn_prefill_kernel(const PrefillArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < GPT; ++i) {
-    const int gi = tid + kWaves * 64 * i;
+    const int gi = tid + NTH * i;
     const int rr = gi / QD, d4 = gi % QD;
     if (rr >= nvalid) continue;
     const int row = r0 + rr;
@@ -799,15 +967,38 @@ attn_prefill_kernel(const PrefillArgs a) {
   if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Compute units of the current device (0 if the attribute cannot be read),
+// read once per device.
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// Unsplit launches with fewer workgroups than two per CU (one per CU at
+// most, by LDS) run two key groups per workgroup: eight waves on a CU
+// instead of four.
 template <int D, int QM, bool PLO>
 int launch_s(const PrefillArgs& a, hipStream_t s) {
-  const unsigned blocks = (unsigned)((int64_t)a.B * a.Hkv * a.row_blocks * a.splits);
-  if (a.splits > 1)
-    hipLaunchKernelGGL((attn_prefill_kernel<D, QM, PLO, true>), dim3(blocks),
+  const int64_t blocks = (int64_t)a.B * a.Hkv * a.row_blocks * a.splits;
+  if (a.splits > 1) {
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QM, PLO, true, 1>), dim3((unsigned)blocks),
                        dim3(kWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_prefill_kernel<D, QM, PLO, false>), dim3(blocks),
+  } else if (blocks < 2 * (int64_t)cu_count()) {
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QM, PLO, false, 2>), dim3((unsigned)blocks),
+                       dim3(2 * kWaves * 64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_prefill_kernel<D, QM, PLO, false, 1>), dim3((unsigned)blocks),
                        dim3(kWaves * 64), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_LAUNCH;
 }
 
