@@ -612,15 +612,26 @@ attn_prefill_kernel(const PrefillArgs a) {
     float mnew[2];
     bool need[2];
     if (!full) {
+      // Key k0 + 4 k4 + x (x = 16 kb + i) is in row j's range iff
+      // min(x - lo, hi - 1 - x) >= 0 with lo, hi taken relative to
+      // k0 + 4 k4; the sign of that minimum, spread over the word, selects
+      // -inf (v_bfi_b32).  Per-lane arithmetic: comparisons would each
+      // leave a lane mask in scalar registers, more of them than there are.
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {
+        const int lo = rlo[j] - (k0 + 4 * k4);
+        const int hm1 = rhi[j] - 1 - (k0 + 4 * k4);
 #pragma unroll
         for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 16 * kb + 4 * k4 + i;
-            if (key < rlo[j] || key >= rhi[j]) s[kb][j][i] = -INFINITY;
+            const int x = 16 * kb + i;
+            const int d = min(x - lo, hm1 - x);
+            const uint32_t out = (uint32_t)(d >> 31);   // all ones outside the range
+            s[kb][j][i] = __uint_as_float((__float_as_uint(s[kb][j][i]) & ~out) |
+                                          (0xff800000u & out));
           }
+      }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

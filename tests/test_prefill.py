@@ -133,6 +133,35 @@ def test_gpu_prefill(name, over, what):
         check_prologue_multi(w, got, ref, f"prefill {name} {over}")
 
 
+# Launches with at least two row-block workgroups per CU (512 on MI355X) run
+# one key group per workgroup; the smaller cases above run two (and the
+# full-size case below, one).  These cover the one-group instances for the
+# other q and output types and for D = 64.
+LARGE_GRID = [
+    ("6", dict(B=4, L=700, S=512), "prologue (raw bf16 q, QK-norm, RoPE)"),
+    ("7", dict(B=4, L=600, S=512, out_dtype="f32"), "bf16 q, fp32 out"),
+    ("1", dict(B=16, L=600, S=512), "D=64, prologue"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over,what", LARGE_GRID,
+                         ids=[f"grid{i}" for i in range(len(LARGE_GRID))])
+def test_gpu_prefill_large_grid(name, over, what):
+    _gpu()
+    from test_gpu_parity import check_attention
+    from test_multi_token import check_prologue_multi
+    w = W.make(name, **over)
+    blocks = w.B * w.Hkv * ((w.S * (w.Hq // w.Hkv) + 127) // 128)   # 128-row blocks
+    assert blocks >= 512
+    print(f"\n[case] prefill large grid cfg={name} {over} ({what})", flush=True)
+    ref = O.decode_step(w)
+    got = _step(w)
+    check_attention(got, ref, w.out_dtype, f"prefill large grid {name} {over}")
+    if w.pos is not None:
+        check_prologue_multi(w, got, ref, f"prefill large grid {name} {over}")
+
+
 # bf16 q (given directly) and a bf16 output at D = 128, the chunked-prefill
 # configuration: every group size, windows, bidirectional, ragged blocks
 BF16_PATH = [
