@@ -63,7 +63,7 @@ constexpr int kRows = kWaves * kRowsPerWave;      // query rows per workgroup
 constexpr int kKeys = 64;
 constexpr int kKB = kKeys / 16;                   // 16-key blocks per tile
 static_assert(kKeys == 32 || kKeys == 64, "tile of 32 or 64 keys");
-constexpr float kRescaleLog2 = 8.0f;              // lazy-rescale threshold
+constexpr float kSumLimit = 256.0f;               // lazy rescale: a lane's weight sum per tile
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -609,8 +609,6 @@ attn_prefill_kernel(const PrefillArgs a) {
   // w >= 2.
   auto softmax = [&](int k0) __attribute__((always_inline)) {
     const bool full = k0 >= free_lo && k0 + kKeys <= free_hi;
-    float mnew[2];
-    bool need[2];
     if (!full) {
       // Key k0 + 4 k4 + x (x = 16 kb + i) is in row j's range iff
       // min(x - lo, hi - 1 - x) >= 0 with lo, hi taken relative to
@@ -633,58 +631,68 @@ attn_prefill_kernel(const PrefillArgs a) {
           }
       }
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float t = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-        t = fmax_nan(t, fmax_nan(fmax_nan(s[kb][j][0], s[kb][j][1]),
-                                 fmax_nan(s[kb][j][2], s[kb][j][3])));
-      t = max_over_rows(t);
-      mnew[j] = fmax_nan(m[j], t);
-      // m = -inf with a finite maximum gives +inf (rescale); both -inf give
-      // NaN (no rescale: the row has seen no key yet).
-      need[j] = (mnew[j] - m[j]) * qscale > kRescaleLog2;
-    }
-    if (__any(need[0] || need[1])) {
+    // P against the current references and each lane's sum of them.
+    float ps[2];
+    auto weights = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float alpha = need[j] ? __builtin_amdgcn_exp2f((m[j] - mnew[j]) * qscale) : 1.0f;
-        if (need[j]) {
-          m[j] = mnew[j];
+        const float mref = mq[j];
+        float p[kKB][4];
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j][i], qscale, -mref));
+            ps[j] = kb == 0 && i == 0 ? p[0][0] : ps[j] + p[kb][i];
+          }
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float pa = p[2 * hh + (w >> 1)][2 * (w & 1)];
+            const float pb = p[2 * hh + (w >> 1)][2 * (w & 1) + 1];
+            const uint32_t hw = pack_bf16(pa, pb);
+            ph[hh][j][w] = hw;
+            if constexpr (PLO)
+              pl[hh][j][w] = pack_bf16(pa - __uint_as_float(hw << 16),
+                                       pb - __uint_as_float(hw & 0xffff0000u));
+          }
+      }
+    };
+    weights();
+    // The reference maximum moves only when a row has none yet (-inf: no
+    // finite score seen) or a lane's weights of the tile sum past 2^8 (so
+    // every accepted weight is at most 2^8).  Only then is the tile's exact
+    // row maximum formed, the state rescaled and the weights recomputed;
+    // the common tile takes no maximum at all.
+    const bool need0 = m[0] == -INFINITY || ps[0] > kSumLimit;
+    const bool need1 = m[1] == -INFINITY || ps[1] > kSumLimit;
+    if (__any(need0 || need1)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float t = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+          t = fmax_nan(t, fmax_nan(fmax_nan(s[kb][j][0], s[kb][j][1]),
+                                   fmax_nan(s[kb][j][2], s[kb][j][3])));
+        t = max_over_rows(t);
+        const float mnew = fmax_nan(m[j], t);
+        // false for a NaN maximum (the NaN reaches the output through the
+        // weights) and while the row has seen only -inf
+        const bool move = mnew > m[j];
+        const float alpha = move ? __builtin_amdgcn_exp2f((m[j] - mnew) * qscale) : 1.0f;
+        if (move) {
+          m[j] = mnew;
           mq[j] = m[j] * qscale;
         }
         l[j] *= alpha;
 #pragma unroll
         for (int v = 0; v < VB; ++v) o[j][v] *= alpha;
       }
+      weights();
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float mref = mq[j];
-      float p[kKB][4];
-      float ps;
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j][i], qscale, -mref));
-          ps = kb == 0 && i == 0 ? p[0][0] : ps + p[kb][i];
-        }
-      l[j] += ps;
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float pa = p[2 * hh + (w >> 1)][2 * (w & 1)];
-          const float pb = p[2 * hh + (w >> 1)][2 * (w & 1) + 1];
-          const uint32_t hw = pack_bf16(pa, pb);
-          ph[hh][j][w] = hw;
-          if constexpr (PLO)
-            pl[hh][j][w] = pack_bf16(pa - __uint_as_float(hw << 16),
-                                     pb - __uint_as_float(hw & 0xffff0000u));
-        }
-    }
+    l[0] += ps[0];
+    l[1] += ps[1];
   };
 
   // PV with the tile in V stage `curv`: O^T[16 cols x 16 rows] +=
