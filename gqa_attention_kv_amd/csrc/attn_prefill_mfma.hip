@@ -30,17 +30,19 @@
 //       P operand already holds them: k = 8 k4 + e is key 4 k4 + e (e < 4)
 //       or 16 + 4 k4 + e - 4.  V stays row-major in LDS; lane l's V operand
 //       comes from two transposed reads (ds_read_b64_tr_b16, four key rows
-//       each).  P is rounded once to bf16 when the output is bf16 (an error
-//       of at most 2^-9 sum p|V|, the order of the output's own rounding);
-//       for an fp32 output P is carried as bf16 hi + lo (~16 mantissa bits)
-//       in two calls on the same V operand.
+//       each).  P is rounded once to bf16 when the output is bf16 (a
+//       relative error of at most 2^-8 per weight, so at most 2^-8 of
+//       sum p|V| / sum p in the output, the order of the output's own
+//       rounding); for an fp32 output P is carried as bf16 hi + lo (~16
+//       mantissa bits) in two calls on the same V operand.
 // K and V tiles go from the cache straight into LDS (buffer loads with the
-// LDS destination): K through two stages, fetched one tile ahead, V through
-// three, fetched two tiles ahead, with one barrier per tile.  Online softmax
-// per row with a lazy rescale: the reference maximum only moves when a
-// tile's maximum exceeds it by more than 2^8 (in exp2 units), so P stays
-// below 256 and O is rarely rescaled.  Keys outside a row's range are masked
-// only in tiles that are not wholly inside every range of the wave's rows.
+// LDS destination) through two stages each, the next tile fetched while the
+// current one is computed, with one barrier per tile.  Online softmax per
+// row with a lazy rescale: the weights are formed against the current
+// reference maximum, which moves only when a row has none yet or a lane's
+// weights of the tile sum past 2^8, so P stays at most 256 and O is rarely
+// rescaled.  Keys outside a row's range are masked only in tiles that are
+// not wholly inside every range of the wave's rows.
 #include <type_traits>
 
 #include "device_common.h"

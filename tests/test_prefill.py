@@ -7,6 +7,7 @@ sequences and chunks at the end of a longer cache, fp32 q from the prologue
 and bf16 q given directly, ragged row blocks, every group size, D = 64,
 windows, ragged lengths, rows with no key, NaN outside the attended rows --
 and the full-size chunked-prefill config on sampled tokens."""
+import dataclasses
 import math
 
 import numpy as np
@@ -217,6 +218,63 @@ def test_gpu_prefill_poisoned_rows(causal):
     ref = O.decode_step(w)
     got = _step(w, poison=True)
     check_attention(got, ref, w.out_dtype, "prefill poisoned")
+
+
+# Scores that climb along the keys: each K row gets c_t u added, u one unit
+# direction per (sequence, KV head) and c_t rising to `top`, so for a head
+# with q.u > 0 every tile's weights pass 2^8 against the running maximum
+# and the reference moves tile after tile (and for q.u < 0 falls behind
+# it).  (config, overrides, splits, top)
+CLIMB = [
+    ("7", dict(B=2, L=1200, S=128), 1, 800.0),
+    ("7", dict(B=2, L=900, S=96, out_dtype="f32"), 1, 800.0),
+    ("7", dict(B=2, L=1200, S=128), 3, 800.0),
+    ("6", dict(B=2, L=700, S=64, out_dtype="f32"), 1, 800.0),
+    ("1", dict(B=2, L=600, S=100, layout="noprologue", out_dtype="bf16"), 1, 400.0),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over,splits,top", CLIMB, ids=[f"c{i}" for i in range(len(CLIMB))])
+def test_gpu_prefill_climbing_scores(name, over, splits, top):
+    _gpu()
+    from gqa_attention_kv_amd import runner
+    from test_gpu_parity import check_attention
+    w = W.make(name, **over)
+    rng = np.random.default_rng(17)
+    T = w.k_cache.shape[2]
+    base = (w.k_cache.astype(np.uint32) << 16).view(np.float32)
+    u = rng.standard_normal((w.B, w.Hkv, 1, w.D)).astype(np.float32)
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    c = (top * np.arange(T, dtype=np.float32) / T)[None, None, :, None]
+    w.k_cache[:] = W.fp32_to_bf16_bits(base + c * u)
+    print(f"\n[case] prefill climbing scores cfg={name} {over} splits={splits} top={top}",
+          flush=True)
+    ref = O.decode_step(w)
+    step = runner.DeviceStep(w, mode="prefill", splits=splits)
+    step.run()
+    got = step.results()
+    what = f"prefill climbing {name} {over} splits={splits}"
+    if w.out_dtype == "f32":
+        check_attention(got, ref, w.out_dtype, what)
+        return
+    # bf16 output: the weights are rounded once to bf16 and so is the output,
+    # each a relative error of at most 2^-8; with one key dominating a row
+    # |out| approaches |V| and the fixed bf16 bar no longer bounds that.  The
+    # bound per element: 2^-8 (sum p|V| / sum p) + 2^-8 |out| + 1e-3, the
+    # first term from the oracle run on |V|.  (No K/V row is appended here.)
+    assert w.pos is None
+    wa = dataclasses.replace(w, v_cache=w.v_cache & np.uint16(0x7FFF))
+    vabs = O.decode_step(wa)["out"]
+    bound = 2.0 ** -8 * vabs + 2.0 ** -8 * np.abs(ref["out"]) + 1e-3
+    err = np.abs(got["out"] - ref["out"])
+    assert np.all(np.isfinite(got["out"])), f"{what}: non-finite output"
+    assert np.all(err <= bound), f"{what}: max excess {float(np.max(err - bound))}"
+    rl, gl = ref["lse"], got["lse"]
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(gl), fin), f"{what}: lse finiteness differs"
+    from test_gpu_parity import LSE_TOL
+    assert float(np.max(np.abs(gl[fin] - rl[fin]))) <= LSE_TOL, f"{what}: lse"
 
 
 @pytest.mark.gpu
