@@ -705,20 +705,35 @@ attn_prefill_kernel(const PrefillArgs a) {
   // (ds_read_b64_tr_b16): in a group of 16 lanes, lane 4 e + q points at
   // columns 16 v + 4 q .. + 3 of key row 4 k4 + e, and lane n of the group
   // receives column 16 v + n of the four rows.
+  // The lane's part of the V read offset for column block v (rows below
+  // 16), masked to 16 rows: a no-op that lets the compiler see that a read
+  // stays inside its stage (else it waits for the fills of the other stages
+  // in flight).  Without the q prologue it is formed once, the empty asm
+  // keeping it whole: left to itself the compiler rebuilt it from two parts
+  // with an add before every read (the prologue instances, short of
+  // registers, keep that).
+  const int vq = lane & 3;
+  const int vrow = 4 * k4 + ((lane & 15) >> 2);   // vsw(vrow + 16 m) == vsw(vrow)
+  auto voff_of = [&](int v) -> uint32_t {
+    const int col = 16 * v + 4 * vq;
+    return (uint32_t)(vrow * RB + 16 * ((col / 8) ^ vsw(vrow)) + 2 * (col % 8));
+  };
+  uint32_t voff[VB];
+  if constexpr (!PRO) {
+#pragma unroll
+    for (int v = 0; v < VB; ++v) {
+      uint32_t t = voff_of(v);
+      asm volatile("" : "+v"(t));
+      voff[v] = t & (uint32_t)(16 * RB - 1);
+    }
+  }
   auto pv = [&](const unsigned char* curv) __attribute__((always_inline)) {
     typedef __attribute__((ext_vector_type(4))) short s16x4_t;
     typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-    const int vq = lane & 3;
-    const int vrow = 4 * k4 + ((lane & 15) >> 2);   // vsw(vrow + 16 m) == vsw(vrow)
     auto vread = [&](int x) {
       const int hh = x / VB, v = x % VB;
-      const int col = 16 * v + 4 * vq;
-      // The lane's part of the offset (rows below 16) masked to 16 rows, a
-      // no-op that lets the compiler see the read stays inside the stage
-      // (else it waits for the fills of the other stages in flight); the
-      // half and the second four-row group are constants.
-      const uint32_t o0 = (uint32_t)(vrow * RB + 16 * ((col / 8) ^ vsw(vrow)) + 2 * (col % 8)) &
-                          (uint32_t)(16 * RB - 1);
+      const uint32_t o0 = PRO ? voff_of(v) & (uint32_t)(16 * RB - 1) : voff[v];
+      // the half and the second four-row group are constants
       const unsigned char* p0 = curv + o0 + 32 * hh * RB;
       const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
       const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p0 + 16 * RB));
