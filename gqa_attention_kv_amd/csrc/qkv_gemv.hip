@@ -47,6 +47,10 @@ constexpr int kMaxTiles = 4;                     // tiles per workgroup share
 constexpr int kAhead = 1;                        // items in flight beyond the one computed
 constexpr int kStepCols = 128;                   // columns per step (256 bytes of a row)
 constexpr int kRowU4 = kStepCols * 2 / 16 + 1;   // slab row pitch in 16-byte units (272 B)
+// The weights are read exactly once per launch: their loads carry the
+// non-temporal policy (nt), so they do not displace what the L2 and the
+// Infinity Cache should keep.
+constexpr int kStreamPolicy = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(kWaves * 64) void qkv_gemv_kernel(const GemvArgs a,
     for (int i = 0; i < 4; ++i)
       wt[slot][i] = __builtin_bit_cast(
           u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                       rw, roff[t][i] == wbytes ? wbytes : roff[t][i] + col, 0, 0));
+                       rw, roff[t][i] == wbytes ? wbytes : roff[t][i] + col, 0, kStreamPolicy));
   };
   auto fetch_x = [&](int slot, int j) {
     const int c0 = step_of(j) * kStepCols;
