@@ -212,7 +212,7 @@ constexpr float kRescaleLog2 = 8.0f;
 // head h % G, so rel(h) = (h / G) Hq + h % G, and columns h >= nc are padding.
 template <int D, int CT, int NW, bool MT>
 __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head0, int G,
-                                               int nc) {
+                                               int nc, int count) {
   constexpr int NTH = NW * 64;
   constexpr int NG = CT * D / 4;                // float4 output groups
   constexpr int GPT = NG > NTH ? NG / NTH : 1;  // groups per thread
@@ -239,7 +239,7 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
 #pragma unroll
     for (int e = 0; e < 4; ++e) Ax[j][e] = 0.0f;
   }
-  for (int k0 = s; k0 < num_parts; k0 += KS * MB) {
+  for (int k0 = s; k0 < count; k0 += KS * MB) {
     float lk[GPT][MB];
     f32x4_t ov[GPT][MB];
 #pragma unroll
@@ -255,7 +255,7 @@ __device__ __forceinline__ void merge_partials(const KernelArgs& a, int64_t head
         const int kk = k0 + k * KS;
         lk[j][k] = -INFINITY;
         ov[j][k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (kk < num_parts && col) {
+        if (kk < count && col) {
           lk[j][k] = __hip_atomic_load(Lh + kk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const uint32_t off = (uint32_t)(((rh * num_parts + kk) * D + 4 * d4) * 4);
           ov[j][k] = __builtin_amdgcn_raw_buffer_load_b128(Ors, off, 0, kCoherent);
@@ -1089,27 +1089,37 @@ attn_decode_mfma_kernel(const KernelArgs a) {
       MODE == Mode::Step
           ? make_rsrc(a.ws_o + head0 * num_parts * D, (uint32_t)((size_t)span * num_parts * D * 4))
           : make_rsrc(nullptr, 0u);
-  for (int idx = threadIdx.x; idx < ppw * CT * Q4; idx += NW * 64) {
-    const int pp = ppw == 1 ? 0 : idx / (CT * Q4);   // partition of the pair
+  // A Step workgroup with two partitions combines them here and writes one
+  // partial, at index pgrp: the merge reads half as many (for the 64-
+  // partition long-context step, 64 KB per KV head instead of 128 KB, the
+  // read one CU makes at the end of the launch).  Split writes one partial
+  // per partition, its output contract.
+  constexpr bool kPairOne = MODE == Mode::Step && ppw == 2;
+  constexpr int npw = kPairOne ? 1 : ppw;   // partials written per workgroup
+  for (int idx = threadIdx.x; idx < npw * CT * Q4; idx += NW * 64) {
+    const int pp = npw == 1 ? 0 : idx / (CT * Q4);   // partition of the pair
     const int h = (idx / Q4) % CT;    // column
     const int d = 4 * (idx % Q4);
-    const int pout = pgrp * ppw + pp;
+    const int pout = kPairOne ? pgrp : pgrp * ppw + pp;
     if (h >= NC) {                    // columns only grow with idx within a partition
-      if (ppw == 1) break;
+      if (npw == 1) break;
       continue;
     }
-    if (ppw > 1 && pout >= num_parts) continue;
+    if (!kPairOne && ppw > 1 && pout >= num_parts) continue;
+    // the waves of this partial: its partition's, or both partitions' (a
+    // pair's missing second partition ran no rows: m = -inf, l = 0)
+    auto mine = [&](int w) { return kPairOne || w / wpp == pp; };
     const int64_t oh = orow(h);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w)
-      if (w / wpp == pp) M = fmaxf(M, sm_m[w][h]);
+      if (mine(w)) M = fmaxf(M, sm_m[w][h]);
     const float Ms = (M == -INFINITY) ? 0.0f : M;
     float L = 0.0f;
     float4 A = float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      if (w / wpp != pp) continue;
+      if (!mine(w)) continue;
       const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - Ms);
       const float4 ow = *reinterpret_cast<const float4*>(&sm_o[w][h][d]);
       L += sm_l[w][h] * f;
@@ -1180,7 +1190,7 @@ attn_decode_mfma_kernel(const KernelArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    merge_partials<D, CT, NW, MT>(a, head0, G, NC);
+    merge_partials<D, CT, NW, MT>(a, head0, G, NC, kPairOne ? npg : num_parts);
     if (threadIdx.x == 0)
       __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
