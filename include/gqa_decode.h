@@ -232,8 +232,9 @@ int gqa_attn_decode_merge(const void* workspace, size_t workspace_bytes,
  * RoPE + KV-cache writes; fusedtok 1.0.1 README: attention_decode with the
  * flash-decoding split): the effect of gqa_qkv_prologue followed by
  * gqa_attn_decode_splitk and gqa_attn_decode_merge, with q_out optional.
- * Each (partition, KV head, sequence) workgroup rotates the new query
- * itself and writes its partition's partial (o, lse); the last workgroup of
+ * Each workgroup -- one partition of a (sequence, KV head), or two
+ * consecutive ones for long contexts -- rotates the new query itself and
+ * writes one partial (o, lse) for the rows it attends; the last workgroup of
  * each (sequence, KV head) to finish merges the partials in a fixed order,
  * so reruns are bit-identical.  The workgroup whose partition attends row
  * pos[b] computes the appended K/V row and uses it in place of reading that
