@@ -387,7 +387,20 @@ attn_decode_mfma_kernel(const KernelArgs a) {
   const int nbg = a.B * a.Hkv;
   const int npg = MODE == Mode::Final ? 1 : (a.num_parts + ppw - 1) / ppw;
   int pgrp, bg;
-  if (npg >= 8) {
+  if (MT && npg >= 8) {
+    // Several tokens: the last partition of every team, often a stub (the
+    // new tokens' rows past the last whole partition), after all the
+    // others, so the whole partitions take the first round of resident
+    // workgroups (measured on 4 draft tokens over 8192 rows: 59.0 -> 57.0 us)
+    const int head = nbg * (npg - 1);
+    if ((int)blockIdx.x < head) {
+      bg = (int)blockIdx.x / (npg - 1);
+      pgrp = (int)blockIdx.x - bg * (npg - 1);
+    } else {
+      bg = (int)blockIdx.x - head;
+      pgrp = npg - 1;
+    }
+  } else if (npg >= 8) {
     bg = (int)blockIdx.x / npg;
     pgrp = (int)blockIdx.x - bg * npg;
   } else {
